@@ -1,0 +1,205 @@
+"""Benchmark: causal RoPE attention forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one forward (attn_fwd) and one backward (attn_bwd_dq then
+attn_bwd_dkdv, which is exactly what attn_bwd enqueues) over one batch of
+synthetic input already resident in HBM; the RoPE tables are built before the
+timed region (they depend only on T, D and the base, like weights). Throughput
+uses the causal FLOP convention: forward 2*B*H*T^2*D, backward 2.5x forward.
+
+Prints ONE JSON line. Besides the headline figures it carries
+  roofline      for the kernel with the longest average duration, timed with
+                HIP events on the stream the kernels run on;
+  cpu_baseline  the float64 oracle timed on this host's cores on a bounded
+                sample of the same workload (and a parity check of the GPU
+                outputs on that sample).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s, bf16 B8 H12 T1024 D64; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16/fp16 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def causal_flops(B, H, T, D):
+    unit = float(B) * H * T * T * D          # one causal product: 2 * (T^2/2) * D per head
+    return {"fwd": 2 * unit, "bwd": 5 * unit,
+            # products each kernel evaluates on the causal half (its own algorithmic work)
+            "fwd_kernel": 2 * unit, "dq_kernel": 3 * unit, "dkdv_kernel": 4 * unit}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=96,
+                    help="heads of the workload the CPU oracle runs on")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention op is independent per "
+              "(batch, head) and this build has no multi-GPU path; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import causal_attention_attn_amd as attn
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    attn.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    B, H, T, D = w.shape
+    dt = attn.ATTN_BF16 if w.dtype == "bf16" else attn.ATTN_F32
+    print(f"# workload {name} B{B} H{H} T{T} D{D} {w.dtype}", file=sys.stderr, flush=True)
+    x = workloads.make(w, seed=0)
+    g = {n: t.to(dev) for n, t in x.items()}
+    q, k, v, do = g["q"], g["k"], g["v"], g["do"]
+    cs, sn = attn.rope_tables(T, D, w.base, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wsb = attn.attn_bwd_workspace_bytes(B, H, T, D, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def fwd():
+        attn.attn_fwd(q, k, v, cs, sn, o, lse, B, H, T, D, dt, sh)
+
+    def bwd_dq():
+        attn.attn_bwd_dq(q, k, v, o, do, lse, cs, sn, dq, ws, wsb, B, H, T, D, dt, sh)
+
+    def bwd_dkdv():
+        attn.attn_bwd_dkdv(q, k, v, do, lse, cs, sn, dk, dv, ws, wsb, B, H, T, D, dt, sh)
+
+    for _ in range(args.warmup):
+        fwd(); bwd_dq(); bwd_dkdv()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream); fwd()
+        e[1].record(stream); bwd_dq()
+        e[2].record(stream); bwd_dkdv()
+        e[3].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / K
+    per = {n: np.array([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)])
+           for j, n in enumerate(("fwd_kernel", "dq_kernel", "dkdv_kernel"))}
+    print(f"# timed {K} steps in {wall:.3f} s wall", file=sys.stderr, flush=True)
+
+    fl = causal_flops(B, H, T, D)
+    total = fl["fwd"] + fl["bwd"]
+    value = total / (ms_step * 1e-3) / 1e12
+    kernels = {}
+    for n, arr in per.items():
+        ms = float(np.mean(arr))
+        kernels[n] = {"avg_us": round(ms * 1e3, 2), "p10_us": round(float(np.percentile(arr, 10)) * 1e3, 2),
+                      "p90_us": round(float(np.percentile(arr, 90)) * 1e3, 2),
+                      "tflops": round(fl[n] / (ms * 1e-3) / 1e12, 1)}
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
+    ach = fl[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline(w, x, dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv), args.cpu_heads)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "H": H, "T": T, "D": D, "causal": True,
+                   "rope_base": w.base, "gflop_per_step": round(total / 1e9, 3)},
+        "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, x, gpu_out, heads):
+    """Time the float64 oracle (as it stands) on the first `heads` heads of the
+    same inputs and compare the GPU outputs on those heads."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - informational only
+        blas_threads = None
+    B, H, T, D = w.shape
+    heads = max(1, min(heads, B * H))
+    sel = [(i // H, i % H) for i in range(heads)]
+    f = {n: np.stack([workloads.as_float64(t)[b, h] for b, h in sel])[None]
+         for n, t in x.items()}
+    t0 = time.perf_counter()
+    ro, rl = oracle.attention_forward(f["q"], f["k"], f["v"], base=w.base)
+    t1 = time.perf_counter()
+    rg = oracle.attention_backward(f["q"], f["k"], f["v"], f["do"], base=w.base)
+    t2 = time.perf_counter()
+    fl = causal_flops(1, heads, T, D)
+    secs = t2 - t0
+    cpu = {"value": round((fl["fwd"] + fl["bwd"]) / secs / 1e12, 6), "unit": "TFLOP/s",
+           "cores": blas_threads, "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+           "sample": f"{heads} of {B * H} heads (all T={T} rows), fwd {t1 - t0:.2f} s + "
+                     f"bwd {t2 - t1:.2f} s, numpy float64 full T x T matrices, causal FLOP count"}
+    worst = {}
+    ref = dict(o=ro, dq=rg[0], dk=rg[1], dv=rg[2])
+    for n, r in ref.items():
+        gg = np.stack([workloads.as_float64(gpu_out[n])[b, h] for b, h in sel])[None]
+        d = gg - r
+        worst[n] = {"max_abs": float(np.max(np.abs(d))),
+                    "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(r))}
+    return cpu, {"heads": heads, **worst}
+
+
+if __name__ == "__main__":
+    main()

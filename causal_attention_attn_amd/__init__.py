@@ -1,0 +1,23 @@
+"""MI355X (gfx950) causal self-attention with rotary position embedding.
+
+The computation runs in libattn.so (hand-written HIP kernels behind a C ABI,
+include/attn.h); this package is its Python binding. torch provides device
+memory and streams only.
+"""
+
+from ._lib import (  # noqa: F401
+    ATTN_BF16,
+    ATTN_F32,
+    LIB_PATH,
+    AttnError,
+    attn_bwd,
+    attn_bwd_dkdv,
+    attn_bwd_dq,
+    attn_bwd_workspace_bytes,
+    attn_fwd,
+    attn_last_hip_error,
+    attn_rope_tables,
+    attn_status_string,
+    load,
+)
+from .api import backward, forward, rope_tables  # noqa: F401

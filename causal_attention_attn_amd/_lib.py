@@ -1,0 +1,136 @@
+"""ctypes binding of libattn.so: the C ABI of include/attn.h under the same names.
+
+Argument marshalling only. Tensor arguments may be torch tensors (their
+data_ptr() is passed) or plain integer device addresses; `stream` may be a
+torch.cuda.Stream, an integer hipStream_t handle, or None for torch's current
+stream on the current device. A non-zero status raises AttnError. There is no
+fallback: if the library is missing, every call raises.
+"""
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_BF16 = 0
+ATTN_F32 = 1
+
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
+    4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_ALIAS",
+    8: "ATTN_ERR_VALUE",
+}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIGS = {
+    "attn_rope_tables": (_I, [_P, _P, _I, _I, ctypes.c_double, _P]),
+    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                      _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                         _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                           _I, _I, _I, _I, _I, _P]),
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+    "attn_last_hip_error": (_I, []),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        detail = ""
+        if status == 6:
+            detail = f" (hipError_t {load().attn_last_hip_error()})"
+        name = STATUS.get(status, str(status))
+        super().__init__(f"{fn} failed: {name}: "
+                         f"{load().attn_status_string(status).decode()}{detail}")
+
+
+def load(path=None):
+    """Load libattn.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m causal_attention_attn_amd.build`"
+                           " (the GPU path has no fallback)")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _call(name, *args):
+    st = getattr(load(), name)(*args)
+    if st != 0:
+        raise AttnError(name, st)
+
+
+def attn_rope_tables(cos_tab, sin_tab, T, D, base=10000.0, stream=None):
+    _call("attn_rope_tables", _ptr(cos_tab), _ptr(sin_tab), T, D, float(base), _stream(stream))
+
+
+def attn_fwd(q, k, v, cos_tab, sin_tab, o, lse, B, H, T, D, dtype, stream=None):
+    _call("attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(cos_tab), _ptr(sin_tab), _ptr(o),
+          _ptr(lse), B, H, T, D, dtype, _stream(stream))
+
+
+def attn_bwd_workspace_bytes(B, H, T, D, dtype):
+    return int(load().attn_bwd_workspace_bytes(B, H, T, D, dtype))
+
+
+def attn_bwd(q, k, v, o, dO, lse, cos_tab, sin_tab, dq, dk, dv, workspace, workspace_bytes,
+             B, H, T, D, dtype, stream=None):
+    _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(cos_tab),
+          _ptr(sin_tab), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), int(workspace_bytes),
+          B, H, T, D, dtype, _stream(stream))
+
+
+def attn_bwd_dq(q, k, v, o, dO, lse, cos_tab, sin_tab, dq, workspace, workspace_bytes,
+                B, H, T, D, dtype, stream=None):
+    _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+          _ptr(cos_tab), _ptr(sin_tab), _ptr(dq), _ptr(workspace), int(workspace_bytes),
+          B, H, T, D, dtype, _stream(stream))
+
+
+def attn_bwd_dkdv(q, k, v, dO, lse, cos_tab, sin_tab, dk, dv, workspace, workspace_bytes,
+                  B, H, T, D, dtype, stream=None):
+    _call("attn_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(cos_tab),
+          _ptr(sin_tab), _ptr(dk), _ptr(dv), _ptr(workspace), int(workspace_bytes),
+          B, H, T, D, dtype, _stream(stream))
+
+
+def attn_status_string(status):
+    return load().attn_status_string(status).decode()
+
+
+def attn_last_hip_error():
+    return int(load().attn_last_hip_error())

@@ -1,0 +1,67 @@
+"""Tensor-level helpers over the C ABI: they allocate outputs with torch on the
+inputs' device and call the library on torch's current stream. Every step of
+the computation runs in the library's HIP kernels."""
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.ATTN_BF16, torch.float32: _lib.ATTN_F32}
+_tables = {}
+
+
+def _dtype_code(t):
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+    return _DTYPES[t.dtype]
+
+
+def _shape(*ts):
+    x = ts[0]
+    if x.dim() != 4:
+        raise ValueError("expected [B, H, T, D] tensors")
+    for t in ts:
+        if t.shape != x.shape or t.dtype != x.dtype or t.device != x.device:
+            raise ValueError("tensors must share shape, dtype and device")
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, T, D]")
+    return tuple(x.shape)
+
+
+def rope_tables(T, D, base=10000.0, device=None):
+    """fp32 cos/sin tables [T, D/2] built by the library's table kernel; cached
+    per (device, T, D, base)."""
+    dev = torch.device(device if device is not None else "cuda")
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    key = (dev, T, D, float(base))
+    if key not in _tables:
+        cs = torch.empty((T, D // 2), dtype=torch.float32, device=dev)
+        sn = torch.empty_like(cs)
+        _lib.attn_rope_tables(cs, sn, T, D, base)
+        _tables[key] = (cs, sn)
+    return _tables[key]
+
+
+def forward(q, k, v, base=10000.0):
+    """Causal RoPE attention forward; returns (o, lse)."""
+    B, H, T, D = _shape(q, k, v)
+    cs, sn = rope_tables(T, D, base, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    _lib.attn_fwd(q, k, v, cs, sn, o, lse, B, H, T, D, _dtype_code(q))
+    return o, lse
+
+
+def backward(q, k, v, o, do, lse, base=10000.0):
+    """Gradients of sum(o * do) w.r.t. the pre-RoPE q, k and v; returns (dq, dk, dv)."""
+    B, H, T, D = _shape(q, k, v, o, do)
+    cs, sn = rope_tables(T, D, base, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = _lib.attn_bwd_workspace_bytes(B, H, T, D, _dtype_code(q))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _lib.attn_bwd(q, k, v, o, do, lse, cs, sn, dq, dk, dv, ws, nbytes, B, H, T, D,
+                  _dtype_code(q))
+    return dq, dk, dv

@@ -1,0 +1,187 @@
+// C ABI of libattn.so (declared in include/attn.h): argument validation, status
+// codes and dispatch to the gfx950 kernels. Nothing here allocates, frees or
+// synchronises; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "attn.h"
+#include "launchers.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_shape(int B, int H, int T, int D, int dtype) {
+    if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+    if (D != 64 && D != 128) return ATTN_ERR_SHAPE;
+    if (B < 1 || H < 1 || T < 1) return ATTN_ERR_SHAPE;
+    const long long elems = (long long)B * H * T * D;
+    if (elems >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (p == nullptr) return ATTN_ERR_NULL;
+    for (const void* p : ps)
+        if (misaligned(p)) return ATTN_ERR_ALIGN;
+    return ATTN_OK;
+}
+
+bool any_alias(std::initializer_list<const void*> outs, std::initializer_list<const void*> ins) {
+    for (const void* a : outs) {
+        for (const void* b : ins)
+            if (a == b) return true;
+    }
+    for (const void* a : outs) {
+        int n = 0;
+        for (const void* b : outs) n += (a == b);
+        if (n > 1) return true;
+    }
+    return false;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return ATTN_OK;
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_HIP;
+}
+
+size_t workspace_need(int B, int H, int T) {
+    const size_t bytes = (size_t)4 * B * H * T;
+    return (bytes + 255) & ~(size_t)255;
+}
+
+int check_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+              const float* cs, const float* sn, const void* ws, size_t ws_bytes, int B, int H,
+              int T, int D, int dtype) {
+    int st = check_shape(B, H, T, D, dtype);
+    if (st) return st;
+    st = check_ptrs({q, k, v, dO, lse, cs, sn});
+    if (st) return st;
+    if (ws == nullptr || ws_bytes < workspace_need(B, H, T)) return ATTN_ERR_WORKSPACE;
+    if (misaligned(ws)) return ATTN_ERR_ALIGN;
+    return ATTN_OK;
+}
+
+attn::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
+                       const void* dO, const float* lse, const float* cs, const float* sn,
+                       void* dq, void* dk, void* dv, const void* ws, int B, int H, int T, int D,
+                       void* stream) {
+    attn::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO;
+    a.lse = lse; a.cs = cs; a.sn = sn;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.delta = static_cast<float*>(const_cast<void*>(ws));
+    a.B = B; a.H = H; a.T = T; a.D = D;
+    a.stream = static_cast<hipStream_t>(stream);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_rope_tables(float* cos_tab, float* sin_tab, int T, int D, double base, void* stream) {
+    if (cos_tab == nullptr || sin_tab == nullptr) return ATTN_ERR_NULL;
+    if (T < 1 || D < 2 || D > 1024 || (D & 1)) return ATTN_ERR_SHAPE;
+    if ((long long)T * (D / 2) >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    if (!(base > 1.0) || base != base) return ATTN_ERR_VALUE;
+    if (cos_tab == sin_tab) return ATTN_ERR_ALIAS;
+    return hip_status(attn::launch_rope_tables(cos_tab, sin_tab, T, D, base,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, const float* cos_tab,
+             const float* sin_tab, void* o, float* lse, int B, int H, int T, int D, int dtype,
+             void* stream) {
+    int st = check_shape(B, H, T, D, dtype);
+    if (st) return st;
+    st = check_ptrs({q, k, v, cos_tab, sin_tab, o, lse});
+    if (st) return st;
+    if (any_alias({o, lse}, {q, k, v, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
+    attn::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.cs = cos_tab; a.sn = sin_tab; a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.T = T; a.D = D;
+    a.stream = static_cast<hipStream_t>(stream);
+    return hip_status(dtype == ATTN_BF16 ? attn::launch_fwd_bf16(a) : attn::launch_fwd_f32(a));
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype) {
+    if (check_shape(B, H, T, D, dtype) != ATTN_OK) return 0;
+    return workspace_need(B, H, T);
+}
+
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, const float* cos_tab, const float* sin_tab, void* dq,
+                void* workspace, size_t workspace_bytes, int B, int H, int T, int D, int dtype,
+                void* stream) {
+    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, workspace, workspace_bytes, B, H, T,
+                       D, dtype);
+    if (st) return st;
+    st = check_ptrs({o, dq});
+    if (st) return st;
+    if (any_alias({dq, workspace}, {q, k, v, o, dO, lse, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
+    const attn::BwdArgs a = bwd_args(q, k, v, o, dO, lse, cos_tab, sin_tab, dq, nullptr,
+                                     nullptr, workspace, B, H, T, D, stream);
+    return hip_status(dtype == ATTN_BF16 ? attn::launch_bwd_dq_bf16(a)
+                                         : attn::launch_bwd_dq_f32(a));
+}
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                  const float* lse, const float* cos_tab, const float* sin_tab, void* dk,
+                  void* dv, const void* workspace, size_t workspace_bytes, int B, int H, int T,
+                  int D, int dtype, void* stream) {
+    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, workspace, workspace_bytes, B, H, T,
+                       D, dtype);
+    if (st) return st;
+    st = check_ptrs({dk, dv});
+    if (st) return st;
+    if (any_alias({dk, dv}, {q, k, v, dO, lse, cos_tab, sin_tab, workspace}))
+        return ATTN_ERR_ALIAS;
+    const attn::BwdArgs a = bwd_args(q, k, v, nullptr, dO, lse, cos_tab, sin_tab, nullptr, dk,
+                                     dv, workspace, B, H, T, D, stream);
+    return hip_status(dtype == ATTN_BF16 ? attn::launch_bwd_dkdv_bf16(a)
+                                         : attn::launch_bwd_dkdv_f32(a));
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, const float* cos_tab, const float* sin_tab, void* dq, void* dk,
+             void* dv, void* workspace, size_t workspace_bytes, int B, int H, int T, int D,
+             int dtype, void* stream) {
+    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, workspace, workspace_bytes, B, H, T,
+                       D, dtype);
+    if (st) return st;
+    st = check_ptrs({o, dq, dk, dv});
+    if (st) return st;
+    if (any_alias({dq, dk, dv, workspace}, {q, k, v, o, dO, lse, cos_tab, sin_tab}))
+        return ATTN_ERR_ALIAS;
+    st = attn_bwd_dq(q, k, v, o, dO, lse, cos_tab, sin_tab, dq, workspace, workspace_bytes, B, H,
+                     T, D, dtype, stream);
+    if (st) return st;
+    return attn_bwd_dkdv(q, k, v, dO, lse, cos_tab, sin_tab, dk, dv, workspace, workspace_bytes,
+                         B, H, T, D, dtype, stream);
+}
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "null pointer";
+        case ATTN_ERR_SHAPE: return "unsupported shape";
+        case ATTN_ERR_DTYPE: return "unknown dtype";
+        case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+        case ATTN_ERR_HIP: return "HIP launch failed";
+        case ATTN_ERR_ALIAS: return "output aliases an input";
+        case ATTN_ERR_VALUE: return "invalid scalar argument";
+        default: return "unknown status";
+    }
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

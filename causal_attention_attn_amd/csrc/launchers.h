@@ -1,0 +1,38 @@
+// Host-side launchers of the attention kernels. Arguments are validated by the
+// C ABI layer before any of these is called; launchers only pick the template
+// instance, size the grid and enqueue on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace attn {
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    const float *cs, *sn;
+    void* o;
+    float* lse;
+    int B, H, T, D;
+    hipStream_t stream;
+};
+
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dO;
+    const float *lse, *cs, *sn;
+    void *dq, *dk, *dv;
+    float* delta;  // [B, H, T] fp32 workspace
+    int B, H, T, D;
+    hipStream_t stream;
+};
+
+hipError_t launch_rope_tables(float* cs, float* sn, int T, int D, double base, hipStream_t s);
+
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a);
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a);
+
+hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_bwd_dq_f32(const BwdArgs& a);
+hipError_t launch_bwd_dkdv_f32(const BwdArgs& a);
+
+}  // namespace attn

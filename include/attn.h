@@ -1,0 +1,149 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) causal RoPE attention library, libattn.so.
+ *
+ * The operation (forward and backward) is causal self-attention with rotary
+ * position embedding applied to the query and key projections, as the pages
+ * describe it: a prediction may depend only on earlier positions, and RoPE is
+ * applied to the projections to encode relative positions ("Tiny Hackable CUDA",
+ * section 3, causal attention paragraph); the engine uses a hand-written
+ * FlashAttention with RoPE, and its analytic gradients (RoPE included) are
+ * checked against centred differences in double precision ("Show HN: NanoEuler",
+ * paragraph 2). Head shapes follow the GPT-2-small specification of 12 heads and
+ * width 768 (NanoEuler article on techinfos.ro, "Arhitectură și tehnologii
+ * folosite"), so D = 64; D = 128 is also supported.
+ *
+ * Definitions used by every entry point (readings where the pages are silent):
+ *   theta_i   = base^(-2i/D), i = 0 .. D/2-1, D = head dimension
+ *   R_t x     rotates each adjacent pair (x[2i], x[2i+1]) by the angle t*theta_i:
+ *             (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos); positions start at 0
+ *   S[t,u]    = (1/sqrt(D)) <R_t q_t, R_u k_u>, kept for u <= t, -inf for u > t
+ *   P         = row softmax of S;  o_t = sum_u P[t,u] v_u   (v is not rotated)
+ *   lse_t     = natural log of sum_{u<=t} exp(S[t,u])
+ *   backward  = gradients of L = sum(o * dO) with respect to the un-rotated
+ *               q, k and v (the RoPE backward is part of the operation).
+ *
+ * Conventions common to all calls:
+ *   - Every tensor pointer is a DEVICE pointer, 16-byte aligned; tensors are
+ *     contiguous row-major [B, H, T, D] with D innermost; lse and the backward
+ *     workspace hold [B, H, T] fp32; cos/sin tables are [T, D/2] fp32.
+ *   - dtype is ATTN_BF16 (bf16 storage, fp32 accumulation) or ATTN_F32 (fp32
+ *     everywhere); it applies to q, k, v, o, dO, dq, dk and dv.
+ *   - D in {64, 128}; T >= 1; B*H >= 1; B*H*T*D < 2^31. The scale is fixed at
+ *     1/sqrt(D). There is no dropout, bias, padding mask or grouped-query sharing.
+ *   - The caller owns all memory. The library never allocates, frees or
+ *     synchronises; work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) and the call returns before the GPU finishes.
+ *   - Outputs must not alias inputs; outputs are overwritten, not accumulated.
+ *   - Every failure is reported by the return value. Arguments are validated
+ *     before anything is launched; nothing aborts and no exception crosses the
+ *     ABI. ATTN_ERR_HIP means a launch failed; attn_last_hip_error() then gives
+ *     the hipError_t value (per calling thread).
+ */
+#ifndef CAUSAL_ROPE_ATTN_H
+#define CAUSAL_ROPE_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_dtype { ATTN_BF16 = 0, ATTN_F32 = 1 };
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,       /* a required pointer is NULL                         */
+    ATTN_ERR_SHAPE = 2,      /* B, H, T or D outside the supported range           */
+    ATTN_ERR_DTYPE = 3,      /* unknown dtype                                      */
+    ATTN_ERR_ALIGN = 4,      /* a tensor pointer is not 16-byte aligned            */
+    ATTN_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required         */
+    ATTN_ERR_HIP = 6,        /* a HIP launch failed (see attn_last_hip_error)      */
+    ATTN_ERR_ALIAS = 7,      /* an output pointer equals an input pointer          */
+    ATTN_ERR_VALUE = 8       /* a scalar argument (e.g. the RoPE base) is invalid   */
+};
+
+/*
+ * attn_rope_tables - fill the RoPE tables cos_tab[t*(D/2) + i] = cos(t*theta_i)
+ * and sin_tab[t*(D/2) + i] = sin(t*theta_i) for t < T, i < D/2.
+ * The angle t*theta_i and its cosine/sine are evaluated in double precision on
+ * the GPU and rounded once to fp32. Position encoding per "Tiny Hackable CUDA",
+ * section 3 (RoPE on the projections, relative positions); base must be > 1
+ * (10000 for the model the pages describe). D must be even, 2 <= D <= 1024.
+ * Tables depend only on (T, D, base): build once, reuse for every call.
+ */
+int attn_rope_tables(float* cos_tab, float* sin_tab, int T, int D, double base,
+                     void* stream);
+
+/*
+ * attn_fwd - forward pass. Reads the pre-RoPE q, k and v, rotates q and k on
+ * load, and writes o = softmax(S) v and lse (natural log-sum-exp of each row's
+ * scaled, masked scores; saved for the backward). FlashAttention-style: the
+ * T x T score matrix is never stored ("Show HN: NanoEuler", paragraph 2).
+ *   q, k, v   [B,H,T,D] dtype, inputs
+ *   cos_tab, sin_tab  [T,D/2] fp32 from attn_rope_tables (or equal values)
+ *   o         [B,H,T,D] dtype, output
+ *   lse       [B,H,T] fp32, output
+ */
+int attn_fwd(const void* q, const void* k, const void* v,
+             const float* cos_tab, const float* sin_tab,
+             void* o, float* lse,
+             int B, int H, int T, int D, int dtype, void* stream);
+
+/*
+ * attn_bwd_workspace_bytes - device workspace attn_bwd needs: the per-row
+ * delta_t = sum_d dO[t,d] o[t,d] in fp32, 4*B*H*T bytes rounded up to 256.
+ * Returns 0 for arguments attn_bwd would reject.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype);
+
+/*
+ * attn_bwd - backward pass: the analytic gradients of L = sum(o * dO) with
+ * respect to the pre-RoPE q, k and v ("Show HN: NanoEuler", paragraph 2: every
+ * analytic gradient, RoPE's included, is checked against centred differences).
+ * Recompute-based: P is rebuilt from q, k and lse; nothing of size T x T is
+ * stored. Runs attn_bwd_dq then attn_bwd_dkdv on `stream`.
+ *   q, k, v, o, dO  [B,H,T,D] dtype, inputs (o and lse from attn_fwd)
+ *   lse             [B,H,T] fp32, input
+ *   dq, dk, dv      [B,H,T,D] dtype, outputs (overwritten)
+ *   workspace       device buffer of at least attn_bwd_workspace_bytes()
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const void* dO, const float* lse,
+             const float* cos_tab, const float* sin_tab,
+             void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes,
+             int B, int H, int T, int D, int dtype, void* stream);
+
+/*
+ * attn_bwd_dq - first stage of attn_bwd: writes delta_t = sum_d dO[t,d] o[t,d]
+ * into the workspace and dq (gradient w.r.t. the pre-RoPE q) into dq.
+ * Same arguments and rules as attn_bwd, minus dk and dv.
+ */
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                const void* dO, const float* lse,
+                const float* cos_tab, const float* sin_tab,
+                void* dq, void* workspace, size_t workspace_bytes,
+                int B, int H, int T, int D, int dtype, void* stream);
+
+/*
+ * attn_bwd_dkdv - second stage of attn_bwd: writes dk (w.r.t. the pre-RoPE k)
+ * and dv. Reads delta from the workspace, so attn_bwd_dq must have been
+ * enqueued before it on the same stream (or completed) with the same inputs.
+ */
+int attn_bwd_dkdv(const void* q, const void* k, const void* v,
+                  const void* dO, const float* lse,
+                  const float* cos_tab, const float* sin_tab,
+                  void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                  int B, int H, int T, int D, int dtype, void* stream);
+
+/* attn_status_string - static, human-readable name of a status code. */
+const char* attn_status_string(int status);
+
+/* attn_last_hip_error - hipError_t of the calling thread's last ATTN_ERR_HIP (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAUSAL_ROPE_ATTN_H */

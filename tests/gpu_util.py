@@ -1,0 +1,69 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI binding
+and compare with the float64 oracle under the stated tolerances."""
+
+import numpy as np
+import torch
+
+import causal_attention_attn_amd as attn
+import oracle
+import workloads
+
+# bf16 storage: max-abs <= 2e-2 and relative L2 <= 1e-2 per output tensor;
+# fp32: max-abs <= 1e-4.
+TOL = {"bf16": dict(max_abs=2e-2, rel_l2=1e-2), "f32": dict(max_abs=1e-4, rel_l2=1e-5)}
+
+
+def gpu_run(x, base=10000.0):
+    """x: dict of CPU tensors q, k, v, do. Returns dict of CPU tensors o, lse, dq, dk, dv."""
+    dev = torch.device("cuda", 0)
+    g = {n: t.to(dev) for n, t in x.items()}
+    o, lse = attn.forward(g["q"], g["k"], g["v"], base=base)
+    dq, dk, dv = attn.backward(g["q"], g["k"], g["v"], o, g["do"], lse, base=base)
+    torch.cuda.synchronize()
+    return {n: t.cpu() for n, t in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv).items()}
+
+
+def oracle_run(x, base=10000.0, heads=None):
+    """float64 oracle on the exact values of x, optionally on a list of (b, h) heads only."""
+    f = {n: workloads.as_float64(t) for n, t in x.items()}
+    if heads is not None:
+        f = {n: np.stack([a[b, h] for b, h in heads])[None] for n, a in f.items()}
+    o, lse = oracle.attention_forward(f["q"], f["k"], f["v"], base=base)
+    dq, dk, dv = oracle.attention_backward(f["q"], f["k"], f["v"], f["do"], base=base)
+    return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+
+
+def select_heads(out, heads):
+    return {n: np.stack([workloads.as_float64(t)[b, h] for b, h in heads])[None]
+            for n, t in out.items()}
+
+
+def errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    d = got - ref
+    return float(np.max(np.abs(d))) if d.size else 0.0, \
+        float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
+
+
+def assert_close(got, ref, dtype, label=""):
+    """Checks o, dq, dk, dv (lse is reported but gated loosely)."""
+    tol = TOL[dtype]
+    report = []
+    for n in ("o", "dq", "dk", "dv"):
+        g = got[n] if isinstance(got[n], np.ndarray) else workloads.as_float64(got[n])
+        mx, rel = errors(g, ref[n])
+        report.append(f"{n}: max-abs {mx:.2e} rel-l2 {rel:.2e}")
+        assert np.all(np.isfinite(g)), f"{label} {n} has non-finite values"
+        assert mx <= tol["max_abs"], f"{label} {n} max-abs {mx:.3e} > {tol['max_abs']}"
+        # an identically zero reference (e.g. dq, dk at T = 1) has no relative error
+        if dtype == "bf16" and np.any(ref[n] != 0):
+            assert rel <= tol["rel_l2"], f"{label} {n} rel-l2 {rel:.3e} > {tol['rel_l2']}"
+    g = got["lse"] if isinstance(got["lse"], np.ndarray) else workloads.as_float64(got["lse"])
+    mx, _ = errors(g, ref["lse"])
+    report.append(f"lse: max-abs {mx:.2e}")
+    # lse is diagnostic (not one of the gated outputs): the fp16 score operands
+    # carry a relative error ~2^-11, so its bound grows with the logit magnitude
+    big = float(np.max(np.abs(ref["lse"]))) if ref["lse"].size else 0.0
+    lse_tol = 1e-2 + 1e-3 * big if dtype == "bf16" else 1e-5
+    assert mx <= lse_tol, f"{label} lse max-abs {mx:.3e} > {lse_tol:.3e}"
+    print(label, "; ".join(report), flush=True)

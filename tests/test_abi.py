@@ -1,0 +1,123 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_attention_attn_amd as attn
+from causal_attention_attn_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "attn.h")
+
+# a fake, 16-byte aligned, non-null address; every call below fails validation
+# before any launch, so it is never dereferenced
+FAKE = 0x100000
+MIS = FAKE + 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return attn.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\*]+\s+\**\s*(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_rope_tables",
+              "attn_bwd_workspace_bytes", "attn_status_string", "attn_last_hip_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+    assert set(declared_functions()) == set(_lib._SIGS)
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        assert attn.attn_status_string(code) != "unknown status"
+    assert attn.attn_status_string(99) == "unknown status"
+    assert attn.attn_last_hip_error() == 0
+
+
+def test_workspace_size(lib):
+    assert attn.attn_bwd_workspace_bytes(8, 12, 1024, 64, 0) == 4 * 8 * 12 * 1024
+    assert attn.attn_bwd_workspace_bytes(1, 1, 3, 64, 0) == 256
+    assert attn.attn_bwd_workspace_bytes(1, 1, 3, 96, 0) == 0
+    assert attn.attn_bwd_workspace_bytes(1, 1, 0, 64, 0) == 0
+    assert attn.attn_bwd_workspace_bytes(1, 1, 3, 64, 7) == 0
+
+
+def status_of(fn, *args):
+    with pytest.raises(attn.AttnError) as e:
+        fn(*args)
+    return e.value.status
+
+
+def fwd_args(**over):
+    a = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, cos_tab=FAKE + 48, sin_tab=FAKE + 64,
+             o=FAKE + 80, lse=FAKE + 96, B=1, H=1, T=8, D=64, dtype=0, stream=0)
+    a.update(over)
+    return a
+
+
+def test_fwd_rejects_bad_arguments(lib):
+    f = lambda **o: status_of(lambda: attn.attn_fwd(**fwd_args(**o)))
+    assert f(q=0) == 1
+    assert f(lse=0) == 1
+    assert f(D=96) == 2
+    assert f(D=32) == 2
+    assert f(T=0) == 2
+    assert f(B=0) == 2
+    assert f(B=1 << 16, H=1 << 10, T=1 << 10) == 2      # 2^42 elements
+    assert f(dtype=2) == 3
+    assert f(k=MIS) == 4
+    assert f(o=FAKE) == 7                                 # o aliases q
+    assert f(lse=FAKE + 32) == 7                          # lse aliases v
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    base = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, o=FAKE + 48, dO=FAKE + 64, lse=FAKE + 80,
+                cos_tab=FAKE + 96, sin_tab=FAKE + 112, dq=FAKE + 128, dk=FAKE + 144,
+                dv=FAKE + 160, workspace=FAKE + 176, workspace_bytes=256, B=1, H=1, T=8,
+                D=64, dtype=0, stream=0)
+    f = lambda **o: status_of(lambda: attn.attn_bwd(**{**base, **o}))
+    assert f(dO=0) == 1
+    assert f(D=100) == 2
+    assert f(dtype=-1) == 3
+    assert f(dq=MIS) == 4
+    assert f(workspace=0) == 5
+    assert f(workspace_bytes=255) == 5
+    assert f(dk=FAKE) == 7
+    assert f(dv=FAKE + 144) == 7                          # dv aliases dk
+    assert f(workspace=FAKE + 80) == 7                    # workspace aliases lse
+
+
+def test_rope_tables_reject_bad_arguments(lib):
+    f = lambda **o: status_of(lambda: attn.attn_rope_tables(
+        **{**dict(cos_tab=FAKE, sin_tab=FAKE + 16, T=4, D=64, base=10000.0, stream=0), **o}))
+    assert f(cos_tab=0) == 1
+    assert f(D=63) == 2
+    assert f(T=0) == 2
+    assert f(base=1.0) == 8
+    assert f(base=float("nan")) == 8
+    assert f(sin_tab=FAKE) == 7
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load(str(tmp_path / "libattn.so"))

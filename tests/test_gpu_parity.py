@@ -1,0 +1,146 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on the
+same seeded inputs, plus exact special cases and invariants."""
+
+import numpy as np
+import pytest
+
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests.gpu_util import assert_close, gpu_run, oracle_run, select_heads
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import causal_attention_attn_amd as attn
+    attn.load()
+
+
+def test_tiny_f32_workload():
+    w = workloads.WORKLOADS[workloads.TINY]
+    x = workloads.make(w)
+    assert_close(gpu_run(x), oracle_run(x), "f32", w.name)
+
+
+# shapes that cross tile boundaries and leave ragged tails (tiles are 32/64/128 rows)
+SMALL = [(1, 1, 1), (1, 1, 3), (1, 2, 63), (1, 1, 64), (2, 1, 65), (1, 3, 127), (1, 1, 128),
+         (1, 2, 200), (1, 1, 257), (2, 2, 333)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B,H,T", SMALL)
+def test_bf16_small_shapes(B, H, T, D):
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    x = workloads.make(w, seed=T + D, shape=(B, H, T, D))
+    assert_close(gpu_run(x), oracle_run(x), "bf16", f"bf16 B{B} H{H} T{T} D{D}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 2, 65), (1, 1, 200), (2, 1, 129)])
+def test_f32_small_shapes(B, H, T, D):
+    w = workloads.WORKLOADS[workloads.TINY]
+    x = workloads.make(w, seed=T + D, shape=(B, H, T, D))
+    assert_close(gpu_run(x), oracle_run(x), "f32", f"f32 B{B} H{H} T{T} D{D}")
+
+
+def test_peaky_logits_small():
+    w = workloads.WORKLOADS["peaky_bf16_b16h12t2048d64"]
+    x = workloads.make(w, shape=(1, 2, 300, 64))
+    assert_close(gpu_run(x), oracle_run(x), "bf16", "peaky small")
+
+
+FULL = [
+    ("gpt2s_bf16_b8h12t1024d64", [(0, 0), (3, 7), (7, 11)]),
+    ("longctx_bf16_b2h12t4096d64", [(0, 0), (1, 11)]),
+    ("peaky_bf16_b16h12t2048d64", [(0, 0), (15, 11)]),
+    ("wide_bf16_b1h6t8192d128", [(0, 5)]),
+]
+
+
+@pytest.mark.parametrize("name,heads", FULL)
+def test_full_size_workloads_on_sampled_heads(name, heads):
+    """Full-size launch (the benchmark's configuration); the oracle checks whole
+    heads, which are independent of each other."""
+    w = workloads.WORKLOADS[name]
+    x = workloads.make(w)
+    got = gpu_run(x)
+    assert_close(select_heads(got, heads), oracle_run(x, heads=heads), "bf16", name)
+
+
+def test_row_zero_is_v_zero_bitwise():
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    for D in (64, 128):
+        x = workloads.make(w, seed=5, shape=(2, 3, 150, D))
+        got = gpu_run(x)
+        assert torch.equal(got["o"][:, :, 0], x["v"][:, :, 0])
+        # exactly 0 in exact arithmetic; on the GPU dP (MFMA) and delta (VALU)
+        # sum the same products in different orders, leaving fp32 rounding noise
+        assert float(got["dq"][:, :, 0].abs().max()) < 1e-5
+
+
+def test_zero_queries_uniform_attention():
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    for D in (64, 128):
+        x = workloads.make(w, seed=6, shape=(1, 2, 190, D))
+        x["q"] = torch.zeros_like(x["q"])
+        got = gpu_run(x)
+        v = workloads.as_float64(x["v"])
+        n = np.arange(1, 191, dtype=np.float64)
+        np.testing.assert_allclose(workloads.as_float64(got["o"]),
+                                   np.cumsum(v, axis=2) / n[:, None], atol=2e-2)
+        np.testing.assert_allclose(workloads.as_float64(got["lse"]),
+                                   np.broadcast_to(np.log(n), (1, 2, 190)), atol=1e-5)
+        assert float(np.max(np.abs(workloads.as_float64(got["dk"])))) < 1e-3
+
+
+def test_causal_invariance_bitwise():
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    for dtype_w, D in ((w, 64), (w, 128), (workloads.WORKLOADS[workloads.TINY], 64)):
+        x = workloads.make(dtype_w, seed=7, shape=(1, 2, 260, D))
+        base = gpu_run(x)
+        for t in (0, 31, 64, 129, 258):
+            y = {n: v.clone() for n, v in x.items()}
+            noise = workloads.make(dtype_w, seed=100 + t, shape=(1, 2, 260, D))
+            for n in y:
+                y[n][:, :, t + 1:] = noise[n][:, :, t + 1:]
+            got = gpu_run(y)
+            for n in ("o", "lse", "dq"):
+                assert torch.equal(got[n][:, :, :t + 1], base[n][:, :, :t + 1]), (D, t, n)
+
+
+def test_deterministic():
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    x = workloads.make(w, seed=8, shape=(2, 3, 700, 64))
+    a, b = gpu_run(x), gpu_run(x)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_rope_table_kernel():
+    import causal_attention_attn_amd as attn
+    for T, D in ((1, 64), (1024, 64), (8192, 128)):
+        cs, sn = attn.rope_tables(T, D, 10000.0, "cuda:0")
+        t = np.arange(T, dtype=np.float64)[:, None]
+        ang = t * 10000.0 ** (-np.arange(0, D, 2, dtype=np.float64) / D)
+        np.testing.assert_allclose(cs.cpu().double().numpy(), np.cos(ang), rtol=0, atol=1e-7)
+        np.testing.assert_allclose(sn.cpu().double().numpy(), np.sin(ang), rtol=0, atol=1e-7)
+
+
+def test_abi_errors_on_gpu():
+    import causal_attention_attn_amd as attn
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="cuda")
+    cs, sn = attn.rope_tables(8, 64, 10000.0, "cuda:0")
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 1, 8), dtype=torch.float32, device="cuda")
+    with pytest.raises(attn.AttnError):
+        attn.attn_fwd(q, q, q, cs, sn, o, lse, 1, 1, 8, 96, attn.ATTN_BF16)
+    with pytest.raises(attn.AttnError):
+        attn.attn_fwd(q, q, q, cs, sn, q, lse, 1, 1, 8, 64, attn.ATTN_BF16)
+    attn.attn_fwd(q, q, q, cs, sn, o, lse, 1, 1, 8, 64, attn.ATTN_BF16)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0)
