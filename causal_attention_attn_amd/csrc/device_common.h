@@ -12,6 +12,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 namespace attn {
@@ -38,9 +39,8 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Round two floats to a 16-bit type (nearest-even) and pack them, first in the low half.
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    const T a = (T)lo, b = (T)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    typedef T T2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, T2));
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) { return pack2<bf16>(lo, hi); }
 
@@ -52,122 +52,163 @@ template <typename T> struct Vec8;
 template <> struct Vec8<bf16> { typedef bf16x8 type; };
 template <> struct Vec8<f16> { typedef f16x8 type; };
 
-// Eight consecutive features of row t of a [T, D] bf16 head starting at d0 (a
-// multiple of 8), rotated by R_t with the fp32 cos/sin tables [T, D/2]:
-// pair p becomes (x0 c - x1 s, x0 s + x1 c). Rows t >= T give zeros.
+// Row (0..31) of the 32x32 MFMA result held in item i of lane half h.
+__device__ __forceinline__ int item_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+// Column order of transposed LDS tiles. Items 8j..8j+7 of a lane half h of a
+// 32x32 result (rows 16j + 8g + 4h + i, g = 0..1, i = 0..3) are the B operand of
+// a following MFMA that contracts over those rows. Storing row u of the
+// contraction at column col_perm(u) (bits 2 and 3 swapped) puts those eight rows
+// at columns 16j + 8h .. 16j + 8h + 7, so the matching A operand is one 16-byte
+// LDS read.
+__device__ __forceinline__ int col_perm(int u) {
+    return (u & ~12) | ((u & 4) << 1) | ((u & 8) >> 1);
+}
+
+}  // namespace attn
+
+namespace attn {
+
+// Max (or sum) of x over the two lanes l and l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float max_across_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Raw buffer resource over `bytes` bytes at p: loads at byte offsets >= bytes
+// return zeros, which is how the kernels read past the end of a sequence.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+__device__ __forceinline__ f32x4 buf_load_f4(rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Buffers of one [T, D] bf16 head and of the [T, D/2] fp32 RoPE tables.
 template <int D>
-__device__ __forceinline__ void rope8(const bf16* __restrict__ x, int t, int d0,
-                                      const float* __restrict__ cs,
-                                      const float* __restrict__ sn, int T, float* r) {
-    if (t >= T) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r[i] = 0.f;
-        return;
-    }
-    const u32x4 w = *reinterpret_cast<const u32x4*>(x + (size_t)t * D + d0);
-    const f32x4 c = *reinterpret_cast<const f32x4*>(cs + (size_t)t * (D / 2) + d0 / 2);
-    const f32x4 s = *reinterpret_cast<const f32x4*>(sn + (size_t)t * (D / 2) + d0 / 2);
+struct HeadBufs {
+    rsrc_t x, c, s;
+    __device__ __forceinline__ HeadBufs(const bf16* head, const float* cs, const float* sn,
+                                        int T)
+        : x(make_rsrc(head, (uint32_t)T * D * 2)),
+          c(make_rsrc(cs, (uint32_t)T * (D / 2) * 4)),
+          s(make_rsrc(sn, (uint32_t)T * (D / 2) * 4)) {}
+};
+
+// Eight features d0 .. d0+7 of row t (zeros past the end), rotated by R_t in
+// fp32 and rounded once to the 16-bit type T: pair p -> (x0 c - x1 s, x0 s + x1 c).
+template <int D, typename T>
+__device__ __forceinline__ typename Vec8<T>::type rope_operand(const HeadBufs<D>& hb, int t,
+                                                               int d0) {
+    const u32x4 w = buf_load16(hb.x, (uint32_t)(t * D + d0) * 2);
+    const f32x4 c = buf_load_f4(hb.c, (uint32_t)(t * (D / 2) + d0 / 2) * 4);
+    const f32x4 s = buf_load_f4(hb.s, (uint32_t)(t * (D / 2) + d0 / 2) * 4);
+    u32x4 r;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const float x0 = bf16_lo(w[p]), x1 = bf16_hi(w[p]);
-        r[2 * p] = x0 * c[p] - x1 * s[p];
-        r[2 * p + 1] = x0 * s[p] + x1 * c[p];
+        r[p] = pack2<T>(x0 * c[p] - x1 * s[p], x0 * s[p] + x1 * c[p]);
     }
+    return as_vec8<typename Vec8<T>::type>(r);
 }
 
-// rope8, rounded once to the 16-bit type T and packed as an MFMA operand.
-template <int D, typename T>
-__device__ __forceinline__ typename Vec8<T>::type load_rope8(const bf16* __restrict__ x, int t,
-                                                             int d0, const float* __restrict__ cs,
-                                                             const float* __restrict__ sn, int T_) {
-    float r[8];
-    rope8<D>(x, t, d0, cs, sn, T_, r);
-    u32x4 w;
+// Register-staged copy of rows [r0, r0 + ROWS) of a head, loaded by NT threads
+// in units of two rows x 8 features (consecutive lanes take consecutive 16-byte
+// pieces of a row, so eight lanes read one 128-byte row). load() issues the global reads (and, with
+// ROT, those of the matching cos/sin entries) so they can complete while the
+// caller computes; store() then rotates by RoPE in fp32 (if ROT), rounds once
+// and writes a row-major copy rm[ROWS][D + 8] of type RM and/or a transposed
+// copy tr[D][ROWS + 8] of type TR (void = not written) whose columns follow
+// col_perm. Rows at or beyond T read as zeros.
+template <int D, int ROWS, int NT, bool ROT>
+struct RowStage {
+    static constexpr int UNITS = (ROWS / 2) * (D / 8);
+    static constexpr int U = UNITS / NT;
+    static_assert(UNITS % NT == 0, "tile units must divide evenly among threads");
+    u32x4 a[U], b[U];
+    f32x4 ca[U], sa[U], cb[U], sb[U];
+
+    __device__ __forceinline__ void load(const HeadBufs<D>& hb, int r0, int tid) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) w[p] = pack2<T>(r[2 * p], r[2 * p + 1]);
-    return as_vec8<typename Vec8<T>::type>(w);
-}
+        for (int j = 0; j < U; ++j) {
+            const int u = j * NT + tid;
+            const int dc = u % (D / 8), kp = u / (D / 8);
+            const int ra = r0 + 2 * kp;
+            a[j] = buf_load16(hb.x, (uint32_t)(ra * D + 8 * dc) * 2);
+            b[j] = buf_load16(hb.x, (uint32_t)((ra + 1) * D + 8 * dc) * 2);
+            if constexpr (ROT) {
+                ca[j] = buf_load_f4(hb.c, (uint32_t)(ra * (D / 2) + 4 * dc) * 4);
+                sa[j] = buf_load_f4(hb.s, (uint32_t)(ra * (D / 2) + 4 * dc) * 4);
+                cb[j] = buf_load_f4(hb.c, (uint32_t)((ra + 1) * (D / 2) + 4 * dc) * 4);
+                sb[j] = buf_load_f4(hb.s, (uint32_t)((ra + 1) * (D / 2) + 4 * dc) * 4);
+            }
+        }
+    }
 
-// Eight consecutive bf16 at (t, d0) of a [T, D] head without rotation; zero if t >= T.
-template <int D>
-__device__ __forceinline__ u32x4 load_row8(const bf16* __restrict__ x, int t, int d0, int T) {
-    if (t >= T) return u32x4{0u, 0u, 0u, 0u};
-    return *reinterpret_cast<const u32x4*>(x + (size_t)t * D + d0);
-}
-
-// Row permutation inside a 32-row MFMA block. When the A operand's row rho is
-// taken from tile row key_perm(rho), item i of lane half h of the 32x32 result
-// belongs to tile row 16*(i/8) + 8h + (i%8). Items 8j..8j+7 of a lane then form,
-// after rounding to 16 bits, the B operand of a following MFMA whose contraction
-// runs over those 32 rows in natural order (chunk j, lane half h <-> rows
-// 16j + 8h .. 16j + 8h + 7).
-__device__ __forceinline__ int key_perm(int rho) {
-    const int g = rho >> 3, hh = (rho >> 2) & 1, i = rho & 3;
-    return 16 * (g >> 1) + 8 * hh + 4 * (g & 1) + i;
-}
-
-// Tile row (0..31) of result item i held by lane half h, for blocks computed
-// with key_perm rows.
-__device__ __forceinline__ int item_row(int i, int h) { return 16 * (i >> 3) + 8 * h + (i & 7); }
-
-// Stage rows [r0, r0 + ROWS) of a [T, D] bf16 head into LDS as a row-major copy
-// rm[ROWS][D + 8] of type RM and/or a transposed copy tr[D][ROWS + 8] of type TR
-// (RM/TR = void: not written). With ROT the rows are rotated by RoPE in fp32 and
-// rounded once to each copy's type; without ROT the bf16 values are copied as
-// they are (RM and TR must then be bf16). Rows at or beyond T become zeros.
-// Work unit: two rows times 8 features; NT threads share the units.
-template <int D, int ROWS, int NT, bool ROT, typename RM, typename TR>
-__device__ __forceinline__ void stage_rows(const bf16* __restrict__ x, int r0, int T,
-                                           const float* __restrict__ cs,
-                                           const float* __restrict__ sn, void* rm_, void* tr_,
-                                           int tid) {
-    constexpr bool HAS_RM = !__is_same(RM, void), HAS_TR = !__is_same(TR, void);
-    constexpr int RS = D + 8, TS = ROWS + 8;
-    constexpr int UNITS = (ROWS / 2) * (D / 8);
-    uint16_t* rm = static_cast<uint16_t*>(rm_);
-    uint16_t* tr = static_cast<uint16_t*>(tr_);
+    template <typename RM, typename TR>
+    __device__ __forceinline__ void store(void* rm_, void* tr_, int tid) const {
+        constexpr bool HAS_RM = !__is_same(RM, void), HAS_TR = !__is_same(TR, void);
+        constexpr int RS = D + 8, TS = ROWS + 8;
+        uint16_t* rm = static_cast<uint16_t*>(rm_);
+        uint16_t* tr = static_cast<uint16_t*>(tr_);
 #pragma unroll
-    for (int u0 = 0; u0 < UNITS; u0 += NT) {
-        const int u = u0 + tid;
-        if (UNITS % NT != 0 && u >= UNITS) break;
-        const int kp = u % (ROWS / 2), dc = u / (ROWS / 2);
-        const int ra = r0 + 2 * kp;
-        u32x4 a_rm, b_rm;
-        uint32_t t_w[8];
-        if constexpr (ROT) {
-            float a[8], b[8];
-            rope8<D>(x, ra, 8 * dc, cs, sn, T, a);
-            rope8<D>(x, ra + 1, 8 * dc, cs, sn, T, b);
-            if constexpr (HAS_RM) {
+        for (int j = 0; j < U; ++j) {
+            const int u = j * NT + tid;
+            const int dc = u % (D / 8), kp = u / (D / 8);
+            u32x4 a_rm, b_rm;
+            uint32_t t_w[8];
+            if constexpr (ROT) {
+                float fa[8], fb[8];
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    a_rm[p] = pack2<RM>(a[2 * p], a[2 * p + 1]);
-                    b_rm[p] = pack2<RM>(b[2 * p], b[2 * p + 1]);
+                    const float a0 = bf16_lo(a[j][p]), a1 = bf16_hi(a[j][p]);
+                    const float b0 = bf16_lo(b[j][p]), b1 = bf16_hi(b[j][p]);
+                    fa[2 * p] = a0 * ca[j][p] - a1 * sa[j][p];
+                    fa[2 * p + 1] = a0 * sa[j][p] + a1 * ca[j][p];
+                    fb[2 * p] = b0 * cb[j][p] - b1 * sb[j][p];
+                    fb[2 * p + 1] = b0 * sb[j][p] + b1 * cb[j][p];
+                }
+                if constexpr (HAS_RM) {
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        a_rm[p] = pack2<RM>(fa[2 * p], fa[2 * p + 1]);
+                        b_rm[p] = pack2<RM>(fb[2 * p], fb[2 * p + 1]);
+                    }
+                }
+                if constexpr (HAS_TR) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t_w[e] = pack2<TR>(fa[e], fb[e]);
+                }
+            } else {
+                a_rm = a[j];
+                b_rm = b[j];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    t_w[2 * e] = (a[j][e] & 0xffffu) | (b[j][e] << 16);
+                    t_w[2 * e + 1] = (a[j][e] >> 16) | (b[j][e] & 0xffff0000u);
                 }
             }
+            if constexpr (HAS_RM) {
+                *reinterpret_cast<u32x4*>(rm + (2 * kp) * RS + 8 * dc) = a_rm;
+                *reinterpret_cast<u32x4*>(rm + (2 * kp + 1) * RS + 8 * dc) = b_rm;
+            }
             if constexpr (HAS_TR) {
+                const int col = col_perm(2 * kp);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) t_w[e] = pack2<TR>(a[e], b[e]);
+                for (int e = 0; e < 8; ++e)
+                    *reinterpret_cast<uint32_t*>(tr + (8 * dc + e) * TS + col) = t_w[e];
             }
-        } else {
-            a_rm = load_row8<D>(x, ra, 8 * dc, T);
-            b_rm = load_row8<D>(x, ra + 1, 8 * dc, T);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                t_w[2 * e] = (a_rm[e] & 0xffffu) | (b_rm[e] << 16);
-                t_w[2 * e + 1] = (a_rm[e] >> 16) | (b_rm[e] & 0xffff0000u);
-            }
-        }
-        if constexpr (HAS_RM) {
-            *reinterpret_cast<u32x4*>(rm + (2 * kp) * RS + 8 * dc) = a_rm;
-            *reinterpret_cast<u32x4*>(rm + (2 * kp + 1) * RS + 8 * dc) = b_rm;
-        }
-        if constexpr (HAS_TR) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<uint32_t*>(tr + (8 * dc + e) * TS + 2 * kp) = t_w[e];
         }
     }
-}
+};
 
 }  // namespace attn

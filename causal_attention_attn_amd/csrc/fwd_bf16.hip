@@ -19,8 +19,11 @@
 //     (v_mfma_f32_32x32x16_bf16). fp16 bounds |rotated q|, |rotated k| by 65504;
 //   * S^T puts one query per lane column, so each lane owns one query's running
 //     max/sum and only one cross-lane exchange (lane ^ 32) is needed per tile;
-//   * the K rows are fed in the key_perm order, which makes the rounded
-//     probabilities directly the B operand of O^T += V^T P^T;
+//   * V is stored transposed with its key columns in col_perm order, so the
+//     rounded probabilities of S^T are directly the B operand of
+//     O^T += V^T P^T and each A operand is one 16-byte LDS read;
+//   * tiles wholly below the block's first query take a branch-free path; only
+//     the last one or two tiles check for skipped and masked 32-key blocks;
 //   * workgroups are issued heaviest q-block first; consecutive block ids walk
 //     the heads so that the q-blocks of one head share an XCD's L2 whenever
 //     the head count is a multiple of the XCD count.
@@ -41,108 +44,147 @@ struct FwdTile {
     static constexpr int NSB = BN / 32;
 };
 
+// Running state of one lane's query: O^T accumulator (this lane's half of the
+// head dimension), reference maximum m (log2 units) and partial row sum l.
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+struct FwdState {
+    f32x16 o[D / 32];
+    float m, l;
+};
+
+// One 64-key tile for one wave. DIAG: the tile may reach this wave's diagonal,
+// so 32-key sub-blocks above it are skipped and the diagonal one is masked.
+template <int D, bool DIAG>
+__device__ __forceinline__ void fwd_tile(FwdState<D>& st, const f16x8* qf, const f16* ks,
+                                         const bf16* vt, int k0, int wq0, int c32, int hf,
+                                         float sc) {
+    using C = FwdTile<D>;
+    constexpr float kRescale = 8.f;
+    f32x16 s[C::NSB];
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+        if (DIAG && k0 + 32 * sb > wq0) break;
+        const f16* krow = ks + (32 * sb + c32) * C::KS + 8 * hf;
+        f32x16 acc = mfma32(*reinterpret_cast<const f16x8*>(krow), qf[0], f32x16{});
+#pragma unroll
+        for (int c = 1; c < C::DK; ++c)
+            acc = mfma32(*reinterpret_cast<const f16x8*>(krow + 16 * c), qf[c], acc);
+        s[sb] = acc;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+        if (DIAG && k0 + 32 * sb > wq0) break;
+        if (DIAG && k0 + 32 * sb == wq0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (item_row(i, hf) > c32) s[sb][i] = -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[sb][i], s[sb][i + 1]));
+    }
+    mx = max_across_halves(mx) * sc;
+    // the reference maximum only moves when the tile maximum exceeds it by more
+    // than kRescale (log2 units), so the O/l rescale is rare; unnormalised
+    // probabilities stay below 2^kRescale
+    if (mx > st.m + kRescale) {
+        const float alpha = exp2_fast(st.m - mx);
+        st.m = mx;
+        st.l *= alpha;
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b) st.o[b] *= alpha;
+    }
+    const float mneg = -st.m;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+        if (DIAG && k0 + 32 * sb > wq0) break;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = exp2_fast(fmaf(s[sb][8 * j + 2 * e], sc, mneg));
+                const float p1 = exp2_fast(fmaf(s[sb][8 * j + 2 * e + 1], sc, mneg));
+                st.l += p0 + p1;
+                w[e] = pack_bf16x2(p0, p1);
+            }
+            pb[j] = as_bf16x8(w);
+        }
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b) {
+            const bf16* vrow = vt + (32 * b + c32) * C::VS + 32 * sb + 8 * hf;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                st.o[b] = mfma32(*reinterpret_cast<const bf16x8*>(vrow + 16 * j), pb[j], st.o[b]);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ cs, const float* __restrict__ sn, bf16* __restrict__ o,
     float* __restrict__ lse, int BH, int T, int nqb, float sc) {
     using C = FwdTile<D>;
-    __shared__ __attribute__((aligned(16))) f16 Ks[C::BN * C::KS];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[D * C::VS];
+    // two buffers of (rotated K row-major, V transposed); one barrier per tile
+    __shared__ __attribute__((aligned(16))) f16 Ks[2][C::BN * C::KS];
+    __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * C::VS];
 
     const int bid = blockIdx.x;
     const int bh = bid % BH;
     const int qb = nqb - 1 - bid / BH;
     const int q0 = qb * C::BM;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c32 = lane & 31, hf = lane >> 5;
     const size_t hoff = (size_t)bh * T * D;
-    const bf16* qh = q + hoff;
-    const bf16* kh = k + hoff;
-    const bf16* vh = v + hoff;
+    const HeadBufs<D> qb_(q + hoff, cs, sn, T), kb_(k + hoff, cs, sn, T), vb_(v + hoff, cs, sn, T);
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
 
-    f16x8 qf[C::DK];
-#pragma unroll
-    for (int c = 0; c < C::DK; ++c) qf[c] = load_rope8<D, f16>(qh, tq, 16 * c + 8 * hf, cs, sn, T);
-
-    f32x16 oacc[C::DB];
-#pragma unroll
-    for (int b = 0; b < C::DB; ++b) oacc[b] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
-
     const int kend = min(T, q0 + C::BM);
     const int ntiles = (kend + C::BN - 1) / C::BN;
-    const int kp = key_perm(c32);
+    const int nfull = min(ntiles, q0 / C::BN);  // tiles wholly below every query of the block
+    RowStage<D, C::BN, C::NT, true> kst;
+    RowStage<D, C::BN, C::NT, false> vst;
+    kst.load(kb_, 0, tid);
+    vst.load(vb_, 0, tid);
+
+    f16x8 qf[C::DK];
+#pragma unroll
+    for (int c = 0; c < C::DK; ++c) qf[c] = rope_operand<D, f16>(qb_, tq, 16 * c + 8 * hf);
+
+    FwdState<D> st;
+#pragma unroll
+    for (int b = 0; b < C::DB; ++b) st.o[b] = f32x16{};
+    st.m = -INFINITY;
+    st.l = 0.f;
+
+    kst.template store<f16, void>(Ks[0], nullptr, tid);
+    vst.template store<void, bf16>(nullptr, Vt[0], tid);
+    __syncthreads();
 
     for (int n = 0; n < ntiles; ++n) {
         const int k0 = n * C::BN;
-        __syncthreads();
-        stage_rows<D, C::BN, C::NT, true, f16, void>(kh, k0, T, cs, sn, Ks, nullptr, tid);
-        stage_rows<D, C::BN, C::NT, false, void, bf16>(vh, k0, T, cs, sn, nullptr, Vt, tid);
-        __syncthreads();
-
-        if (k0 > wq0) continue;  // whole tile above this wave's diagonal
-
-        f32x16 s[C::NSB];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int sb = 0; sb < C::NSB; ++sb) {
-            const int kb = k0 + 32 * sb;
-            if (kb > wq0) break;
-            f32x16 acc = f32x16{};
-            const f16* krow = Ks + (32 * sb + kp) * C::KS + 8 * hf;
-#pragma unroll
-            for (int c = 0; c < C::DK; ++c)
-                acc = mfma32(*reinterpret_cast<const f16x8*>(krow + 16 * c), qf[c], acc);
-            if (kb == wq0) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (item_row(i, hf) > c32) acc[i] = -INFINITY;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[i]);
-            s[sb] = acc;
+        const int cur = n & 1;
+        const bool more = n + 1 < ntiles;
+        if (more) {
+            kst.load(kb_, k0 + C::BN, tid);
+            vst.load(vb_, k0 + C::BN, tid);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m_run, mx * sc);
-        const float alpha = exp2_fast(m_run - mnew);
-        m_run = mnew;
-        l_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < C::DB; ++b) oacc[b] *= alpha;
-
-        float lsum = 0.f;
-#pragma unroll
-        for (int sb = 0; sb < C::NSB; ++sb) {
-            const int kb = k0 + 32 * sb;
-            if (kb > wq0) break;
-            bf16x8 pb[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                u32x4 w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p0 = exp2_fast(fmaf(s[sb][8 * j + 2 * e], sc, -mnew));
-                    const float p1 = exp2_fast(fmaf(s[sb][8 * j + 2 * e + 1], sc, -mnew));
-                    lsum += p0 + p1;
-                    w[e] = pack_bf16x2(p0, p1);
-                }
-                pb[j] = as_bf16x8(w);
-            }
-#pragma unroll
-            for (int b = 0; b < C::DB; ++b) {
-                const bf16* vrow = Vt + (32 * b + c32) * C::VS + 32 * sb + 8 * hf;
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    oacc[b] = mfma32(*reinterpret_cast<const bf16x8*>(vrow + 16 * j), pb[j], oacc[b]);
-            }
+        if (n < nfull)
+            fwd_tile<D, false>(st, qf, Ks[cur], Vt[cur], k0, wq0, c32, hf, sc);
+        else if (k0 <= wq0)
+            fwd_tile<D, true>(st, qf, Ks[cur], Vt[cur], k0, wq0, c32, hf, sc);
+        if (more) {
+            kst.template store<f16, void>(Ks[cur ^ 1], nullptr, tid);
+            vst.template store<void, bf16>(nullptr, Vt[cur ^ 1], tid);
         }
-        l_run += lsum;
+        __syncthreads();
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = sum_across_halves(st.l);
     if (tq < T) {
         const float inv = 1.f / l_tot;
         bf16* orow = o + hoff + (size_t)tq * D;
@@ -151,12 +193,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 u32x2 w;
-                w[0] = pack_bf16x2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
-                w[1] = pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
+                w[0] = pack_bf16x2(st.o[b][4 * g] * inv, st.o[b][4 * g + 1] * inv);
+                w[1] = pack_bf16x2(st.o[b][4 * g + 2] * inv, st.o[b][4 * g + 3] * inv);
                 *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * g + 4 * hf) = w;
             }
         }
-        if (hf == 0) lse[(size_t)bh * T + tq] = (m_run + log2f(l_tot)) * kLn2;
+        if (hf == 0) lse[(size_t)bh * T + tq] = (st.m + log2f(l_tot)) * kLn2;
     }
 }
 
