@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = one forward (attn_fwd) and one backward (attn_bwd_dq then
+One step = one forward (attn_rotate_qk then attn_fwd_rotated, which is
+exactly what attn_fwd enqueues) and one backward (attn_bwd_dq then
 attn_bwd_dkdv, which is exactly what attn_bwd enqueues) over one batch of
 synthetic input already resident in HBM; the RoPE tables are built before the
 timed region (they depend only on T, D and the base, like weights). Throughput
@@ -34,7 +35,8 @@ def causal_flops(B, H, T, D):
     unit = float(B) * H * T * T * D          # one causal product: 2 * (T^2/2) * D per head
     return {"fwd": 2 * unit, "bwd": 5 * unit,
             # products each kernel evaluates on the causal half (its own algorithmic work)
-            "fwd_kernel": 2 * unit, "dq_kernel": 3 * unit, "dkdv_kernel": 4 * unit}
+            "rotate_kernel": 0.0, "fwd_kernel": 2 * unit, "dq_kernel": 3 * unit,
+            "dkdv_kernel": 4 * unit}
 
 
 def main():
@@ -81,40 +83,50 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     wsb = attn.attn_bwd_workspace_bytes(B, H, T, D, dt)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    nsv = attn.attn_saved_bytes(B, H, T, D, dt)
+    saved = torch.empty(max(nsv, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
+    if dt != attn.ATTN_BF16:
+        print("bench.py times the bf16 path", file=sys.stderr)
+        sys.exit(2)
+
+    def rotate():
+        attn.attn_rotate_qk(q, k, cs, sn, saved, nsv, B, H, T, D, dt, sh)
 
     def fwd():
-        attn.attn_fwd(q, k, v, cs, sn, o, lse, B, H, T, D, dt, sh)
+        attn.attn_fwd_rotated(saved, nsv, v, o, lse, B, H, T, D, dt, sh)
 
     def bwd_dq():
-        attn.attn_bwd_dq(q, k, v, o, do, lse, cs, sn, dq, ws, wsb, B, H, T, D, dt, sh)
+        attn.attn_bwd_dq(q, k, v, o, do, lse, cs, sn, saved, nsv, dq, ws, wsb, B, H, T, D, dt, sh)
 
     def bwd_dkdv():
-        attn.attn_bwd_dkdv(q, k, v, do, lse, cs, sn, dk, dv, ws, wsb, B, H, T, D, dt, sh)
+        attn.attn_bwd_dkdv(q, k, v, do, lse, cs, sn, saved, nsv, dk, dv, ws, wsb, B, H, T, D, dt,
+                           sh)
 
     for _ in range(args.warmup):
-        fwd(); bwd_dq(); bwd_dkdv()
+        rotate(); fwd(); bwd_dq(); bwd_dkdv()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
         e = ev[i]
-        e[0].record(stream); fwd()
-        e[1].record(stream); bwd_dq()
-        e[2].record(stream); bwd_dkdv()
-        e[3].record(stream)
+        e[0].record(stream); rotate()
+        e[1].record(stream); fwd()
+        e[2].record(stream); bwd_dq()
+        e[3].record(stream); bwd_dkdv()
+        e[4].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / K
     per = {n: np.array([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)])
-           for j, n in enumerate(("fwd_kernel", "dq_kernel", "dkdv_kernel"))}
+           for j, n in enumerate(("rotate_kernel", "fwd_kernel", "dq_kernel", "dkdv_kernel"))}
     print(f"# timed {K} steps in {wall:.3f} s wall", file=sys.stderr, flush=True)
 
     fl = causal_flops(B, H, T, D)
@@ -126,6 +138,9 @@ def main():
         kernels[n] = {"avg_us": round(ms * 1e3, 2), "p10_us": round(float(np.percentile(arr, 10)) * 1e3, 2),
                       "p90_us": round(float(np.percentile(arr, 90)) * 1e3, 2),
                       "tflops": round(fl[n] / (ms * 1e-3) / 1e12, 1)}
+    # the rotation pass is memory-bound: q and k read (bf16), rotated q and k written (fp16)
+    rot_bytes = 2 * (2 + 2) * B * H * T * D
+    kernels["rotate_kernel"]["gbs"] = round(rot_bytes / (kernels["rotate_kernel"]["avg_us"] * 1e-6) / 1e9, 1)
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
     ach = fl[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),

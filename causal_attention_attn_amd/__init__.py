@@ -15,8 +15,11 @@ from ._lib import (  # noqa: F401
     attn_bwd_dq,
     attn_bwd_workspace_bytes,
     attn_fwd,
+    attn_fwd_rotated,
     attn_last_hip_error,
     attn_rope_tables,
+    attn_rotate_qk,
+    attn_saved_bytes,
     attn_status_string,
     load,
 )

@@ -19,20 +19,24 @@ ATTN_F32 = 1
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
     4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_ALIAS",
-    8: "ATTN_ERR_VALUE",
+    8: "ATTN_ERR_VALUE", 9: "ATTN_ERR_SAVED",
 }
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
+_Z = ctypes.c_size_t
 _SIGS = {
     "attn_rope_tables": (_I, [_P, _P, _I, _I, ctypes.c_double, _P]),
-    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
-    "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
-    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+    "attn_saved_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "attn_rotate_qk": (_I, [_P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
+    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
+    "attn_fwd_rotated": (_I, [_P, _Z, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _P, _Z,
                       _I, _I, _I, _I, _I, _P]),
-    "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+    "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _Z,
                          _I, _I, _I, _I, _I, _P]),
-    "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+    "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _Z,
                            _I, _I, _I, _I, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
@@ -98,34 +102,49 @@ def attn_rope_tables(cos_tab, sin_tab, T, D, base=10000.0, stream=None):
     _call("attn_rope_tables", _ptr(cos_tab), _ptr(sin_tab), T, D, float(base), _stream(stream))
 
 
-def attn_fwd(q, k, v, cos_tab, sin_tab, o, lse, B, H, T, D, dtype, stream=None):
+def attn_saved_bytes(B, H, T, D, dtype):
+    return int(load().attn_saved_bytes(B, H, T, D, dtype))
+
+
+def attn_rotate_qk(q, k, cos_tab, sin_tab, saved, saved_bytes, B, H, T, D, dtype, stream=None):
+    _call("attn_rotate_qk", _ptr(q), _ptr(k), _ptr(cos_tab), _ptr(sin_tab), _ptr(saved),
+          int(saved_bytes), B, H, T, D, dtype, _stream(stream))
+
+
+def attn_fwd(q, k, v, cos_tab, sin_tab, o, lse, saved, saved_bytes, B, H, T, D, dtype,
+             stream=None):
     _call("attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(cos_tab), _ptr(sin_tab), _ptr(o),
-          _ptr(lse), B, H, T, D, dtype, _stream(stream))
+          _ptr(lse), _ptr(saved), int(saved_bytes), B, H, T, D, dtype, _stream(stream))
+
+
+def attn_fwd_rotated(saved, saved_bytes, v, o, lse, B, H, T, D, dtype, stream=None):
+    _call("attn_fwd_rotated", _ptr(saved), int(saved_bytes), _ptr(v), _ptr(o), _ptr(lse),
+          B, H, T, D, dtype, _stream(stream))
 
 
 def attn_bwd_workspace_bytes(B, H, T, D, dtype):
     return int(load().attn_bwd_workspace_bytes(B, H, T, D, dtype))
 
 
-def attn_bwd(q, k, v, o, dO, lse, cos_tab, sin_tab, dq, dk, dv, workspace, workspace_bytes,
-             B, H, T, D, dtype, stream=None):
+def attn_bwd(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, dk, dv,
+             workspace, workspace_bytes, B, H, T, D, dtype, stream=None):
     _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(cos_tab),
-          _ptr(sin_tab), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), int(workspace_bytes),
-          B, H, T, D, dtype, _stream(stream))
+          _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dq), _ptr(dk), _ptr(dv),
+          _ptr(workspace), int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
 
 
-def attn_bwd_dq(q, k, v, o, dO, lse, cos_tab, sin_tab, dq, workspace, workspace_bytes,
-                B, H, T, D, dtype, stream=None):
+def attn_bwd_dq(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, workspace,
+                workspace_bytes, B, H, T, D, dtype, stream=None):
     _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
-          _ptr(cos_tab), _ptr(sin_tab), _ptr(dq), _ptr(workspace), int(workspace_bytes),
-          B, H, T, D, dtype, _stream(stream))
+          _ptr(cos_tab), _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dq),
+          _ptr(workspace), int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
 
 
-def attn_bwd_dkdv(q, k, v, dO, lse, cos_tab, sin_tab, dk, dv, workspace, workspace_bytes,
-                  B, H, T, D, dtype, stream=None):
+def attn_bwd_dkdv(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dk, dv, workspace,
+                  workspace_bytes, B, H, T, D, dtype, stream=None):
     _call("attn_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(cos_tab),
-          _ptr(sin_tab), _ptr(dk), _ptr(dv), _ptr(workspace), int(workspace_bytes),
-          B, H, T, D, dtype, _stream(stream))
+          _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dk), _ptr(dv), _ptr(workspace),
+          int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
 
 
 def attn_status_string(status):

@@ -46,22 +46,30 @@ def rope_tables(T, D, base=10000.0, device=None):
 
 
 def forward(q, k, v, base=10000.0):
-    """Causal RoPE attention forward; returns (o, lse)."""
+    """Causal RoPE attention forward; returns (o, lse, saved). `saved` holds the
+    rotated q and k (bf16 inputs; an empty tensor for fp32) and must be passed
+    to backward()."""
     B, H, T, D = _shape(q, k, v)
+    dt = _dtype_code(q)
     cs, sn = rope_tables(T, D, base, q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    _lib.attn_fwd(q, k, v, cs, sn, o, lse, B, H, T, D, _dtype_code(q))
-    return o, lse
+    nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
+    saved = torch.empty(max(nsaved, 1), dtype=torch.uint8, device=q.device)
+    _lib.attn_fwd(q, k, v, cs, sn, o, lse, saved if nsaved else None, nsaved, B, H, T, D, dt)
+    return o, lse, saved
 
 
-def backward(q, k, v, o, do, lse, base=10000.0):
-    """Gradients of sum(o * do) w.r.t. the pre-RoPE q, k and v; returns (dq, dk, dv)."""
+def backward(q, k, v, o, do, lse, saved, base=10000.0):
+    """Gradients of sum(o * do) w.r.t. the pre-RoPE q, k and v; returns (dq, dk, dv).
+    `saved` is the third value forward() returned for these inputs."""
     B, H, T, D = _shape(q, k, v, o, do)
+    dt = _dtype_code(q)
     cs, sn = rope_tables(T, D, base, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    nbytes = _lib.attn_bwd_workspace_bytes(B, H, T, D, _dtype_code(q))
+    nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
+    nbytes = _lib.attn_bwd_workspace_bytes(B, H, T, D, dt)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    _lib.attn_bwd(q, k, v, o, do, lse, cs, sn, dq, dk, dv, ws, nbytes, B, H, T, D,
-                  _dtype_code(q))
+    _lib.attn_bwd(q, k, v, o, do, lse, cs, sn, saved if nsaved else None, nsaved, dq, dk, dv,
+                  ws, nbytes, B, H, T, D, dt)
     return dq, dk, dv

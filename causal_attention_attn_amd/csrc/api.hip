@@ -51,32 +51,48 @@ int hip_status(hipError_t e) {
     return ATTN_ERR_HIP;
 }
 
-size_t workspace_need(int B, int H, int T) {
-    const size_t bytes = (size_t)4 * B * H * T;
-    return (bytes + 255) & ~(size_t)255;
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t saved_need(int B, int H, int T, int D, int dtype) {
+    return dtype == ATTN_BF16 ? round256((size_t)4 * B * H * T * D) : 0;
+}
+
+size_t workspace_need(int B, int H, int T, int dtype) {
+    return round256((size_t)(dtype == ATTN_BF16 ? 8 : 4) * B * H * T);
+}
+
+// the rotated q/k buffer an entry point reads: required for bf16, unused for fp32
+int check_saved(const void* saved, size_t saved_bytes, int B, int H, int T, int D, int dtype) {
+    if (dtype != ATTN_BF16) return ATTN_OK;
+    if (saved == nullptr) return ATTN_ERR_NULL;
+    if (misaligned(saved)) return ATTN_ERR_ALIGN;
+    if (saved_bytes < saved_need(B, H, T, D, dtype)) return ATTN_ERR_SAVED;
+    return ATTN_OK;
 }
 
 int check_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-              const float* cs, const float* sn, const void* ws, size_t ws_bytes, int B, int H,
-              int T, int D, int dtype) {
+              const float* cs, const float* sn, const void* saved, size_t saved_bytes,
+              const void* ws, size_t ws_bytes, int B, int H, int T, int D, int dtype) {
     int st = check_shape(B, H, T, D, dtype);
     if (st) return st;
     st = check_ptrs({q, k, v, dO, lse, cs, sn});
     if (st) return st;
-    if (ws == nullptr || ws_bytes < workspace_need(B, H, T)) return ATTN_ERR_WORKSPACE;
+    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+    if (st) return st;
+    if (ws == nullptr || ws_bytes < workspace_need(B, H, T, dtype)) return ATTN_ERR_WORKSPACE;
     if (misaligned(ws)) return ATTN_ERR_ALIGN;
     return ATTN_OK;
 }
 
 attn::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
                        const void* dO, const float* lse, const float* cs, const float* sn,
-                       void* dq, void* dk, void* dv, const void* ws, int B, int H, int T, int D,
-                       void* stream) {
+                       const void* saved, void* dq, void* dk, void* dv, const void* ws, int B,
+                       int H, int T, int D, void* stream) {
     attn::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO;
-    a.lse = lse; a.cs = cs; a.sn = sn;
+    a.lse = lse; a.cs = cs; a.sn = sn; a.rot = saved;
     a.dq = dq; a.dk = dk; a.dv = dv;
-    a.delta = static_cast<float*>(const_cast<void*>(ws));
+    a.ws = static_cast<float*>(const_cast<void*>(ws));
     a.B = B; a.H = H; a.T = T; a.D = D;
     a.stream = static_cast<hipStream_t>(stream);
     return a;
@@ -96,75 +112,123 @@ int attn_rope_tables(float* cos_tab, float* sin_tab, int T, int D, double base, 
                                                static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_saved_bytes(int B, int H, int T, int D, int dtype) {
+    if (check_shape(B, H, T, D, dtype) != ATTN_OK) return 0;
+    return saved_need(B, H, T, D, dtype);
+}
+
+int attn_rotate_qk(const void* q, const void* k, const float* cos_tab, const float* sin_tab,
+                   void* saved, size_t saved_bytes, int B, int H, int T, int D, int dtype,
+                   void* stream) {
+    int st = check_shape(B, H, T, D, dtype);
+    if (st) return st;
+    if (dtype != ATTN_BF16) return ATTN_OK;  // the fp32 path rotates on load
+    st = check_ptrs({q, k, cos_tab, sin_tab});
+    if (st) return st;
+    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+    if (st) return st;
+    if (any_alias({saved}, {q, k, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
+    return hip_status(attn::launch_rotate_qk(q, k, cos_tab, sin_tab, saved, B, H, T, D,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void* o, float* lse,
+                     int B, int H, int T, int D, int dtype, void* stream) {
+    int st = check_shape(B, H, T, D, dtype);
+    if (st) return st;
+    if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    st = check_ptrs({v, o, lse});
+    if (st) return st;
+    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+    if (st) return st;
+    if (any_alias({o, lse}, {v, saved})) return ATTN_ERR_ALIAS;
+    attn::FwdArgs a = {};
+    a.v = v; a.rot = saved; a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.T = T; a.D = D;
+    a.stream = static_cast<hipStream_t>(stream);
+    return hip_status(attn::launch_fwd_bf16(a));
+}
+
 int attn_fwd(const void* q, const void* k, const void* v, const float* cos_tab,
-             const float* sin_tab, void* o, float* lse, int B, int H, int T, int D, int dtype,
-             void* stream) {
+             const float* sin_tab, void* o, float* lse, void* saved, size_t saved_bytes, int B,
+             int H, int T, int D, int dtype, void* stream) {
     int st = check_shape(B, H, T, D, dtype);
     if (st) return st;
     st = check_ptrs({q, k, v, cos_tab, sin_tab, o, lse});
     if (st) return st;
-    if (any_alias({o, lse}, {q, k, v, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
-    attn::FwdArgs a;
+    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+    if (st) return st;
+    if (any_alias({o, lse}, {q, k, v, cos_tab, sin_tab, saved})) return ATTN_ERR_ALIAS;
+    if (dtype == ATTN_BF16) {
+        if (any_alias({saved}, {q, k, v, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
+        st = attn_rotate_qk(q, k, cos_tab, sin_tab, saved, saved_bytes, B, H, T, D, dtype,
+                            stream);
+        if (st) return st;
+        return attn_fwd_rotated(saved, saved_bytes, v, o, lse, B, H, T, D, dtype, stream);
+    }
+    attn::FwdArgs a = {};
     a.q = q; a.k = k; a.v = v; a.cs = cos_tab; a.sn = sin_tab; a.o = o; a.lse = lse;
     a.B = B; a.H = H; a.T = T; a.D = D;
     a.stream = static_cast<hipStream_t>(stream);
-    return hip_status(dtype == ATTN_BF16 ? attn::launch_fwd_bf16(a) : attn::launch_fwd_f32(a));
+    return hip_status(attn::launch_fwd_f32(a));
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype) {
     if (check_shape(B, H, T, D, dtype) != ATTN_OK) return 0;
-    return workspace_need(B, H, T);
+    return workspace_need(B, H, T, dtype);
 }
 
 int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                const float* lse, const float* cos_tab, const float* sin_tab, void* dq,
-                void* workspace, size_t workspace_bytes, int B, int H, int T, int D, int dtype,
-                void* stream) {
-    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, workspace, workspace_bytes, B, H, T,
-                       D, dtype);
+                const float* lse, const float* cos_tab, const float* sin_tab, const void* saved,
+                size_t saved_bytes, void* dq, void* workspace, size_t workspace_bytes, int B,
+                int H, int T, int D, int dtype, void* stream) {
+    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, workspace,
+                       workspace_bytes, B, H, T, D, dtype);
     if (st) return st;
     st = check_ptrs({o, dq});
     if (st) return st;
-    if (any_alias({dq, workspace}, {q, k, v, o, dO, lse, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
-    const attn::BwdArgs a = bwd_args(q, k, v, o, dO, lse, cos_tab, sin_tab, dq, nullptr,
+    if (any_alias({dq, workspace}, {q, k, v, o, dO, lse, cos_tab, sin_tab, saved}))
+        return ATTN_ERR_ALIAS;
+    const attn::BwdArgs a = bwd_args(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, dq, nullptr,
                                      nullptr, workspace, B, H, T, D, stream);
     return hip_status(dtype == ATTN_BF16 ? attn::launch_bwd_dq_bf16(a)
                                          : attn::launch_bwd_dq_f32(a));
 }
 
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
-                  const float* lse, const float* cos_tab, const float* sin_tab, void* dk,
-                  void* dv, const void* workspace, size_t workspace_bytes, int B, int H, int T,
-                  int D, int dtype, void* stream) {
-    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, workspace, workspace_bytes, B, H, T,
-                       D, dtype);
+                  const float* lse, const float* cos_tab, const float* sin_tab,
+                  const void* saved, size_t saved_bytes, void* dk, void* dv,
+                  const void* workspace, size_t workspace_bytes, int B, int H, int T, int D,
+                  int dtype, void* stream) {
+    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, workspace,
+                       workspace_bytes, B, H, T, D, dtype);
     if (st) return st;
     st = check_ptrs({dk, dv});
     if (st) return st;
-    if (any_alias({dk, dv}, {q, k, v, dO, lse, cos_tab, sin_tab, workspace}))
+    if (any_alias({dk, dv}, {q, k, v, dO, lse, cos_tab, sin_tab, saved, workspace}))
         return ATTN_ERR_ALIAS;
-    const attn::BwdArgs a = bwd_args(q, k, v, nullptr, dO, lse, cos_tab, sin_tab, nullptr, dk,
-                                     dv, workspace, B, H, T, D, stream);
+    const attn::BwdArgs a = bwd_args(q, k, v, nullptr, dO, lse, cos_tab, sin_tab, saved, nullptr,
+                                     dk, dv, workspace, B, H, T, D, stream);
     return hip_status(dtype == ATTN_BF16 ? attn::launch_bwd_dkdv_bf16(a)
                                          : attn::launch_bwd_dkdv_f32(a));
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-             const float* lse, const float* cos_tab, const float* sin_tab, void* dq, void* dk,
-             void* dv, void* workspace, size_t workspace_bytes, int B, int H, int T, int D,
-             int dtype, void* stream) {
-    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, workspace, workspace_bytes, B, H, T,
-                       D, dtype);
+             const float* lse, const float* cos_tab, const float* sin_tab, const void* saved,
+             size_t saved_bytes, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int H, int T, int D, int dtype, void* stream) {
+    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, workspace,
+                       workspace_bytes, B, H, T, D, dtype);
     if (st) return st;
     st = check_ptrs({o, dq, dk, dv});
     if (st) return st;
-    if (any_alias({dq, dk, dv, workspace}, {q, k, v, o, dO, lse, cos_tab, sin_tab}))
+    if (any_alias({dq, dk, dv, workspace}, {q, k, v, o, dO, lse, cos_tab, sin_tab, saved}))
         return ATTN_ERR_ALIAS;
-    st = attn_bwd_dq(q, k, v, o, dO, lse, cos_tab, sin_tab, dq, workspace, workspace_bytes, B, H,
-                     T, D, dtype, stream);
+    st = attn_bwd_dq(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, workspace,
+                     workspace_bytes, B, H, T, D, dtype, stream);
     if (st) return st;
-    return attn_bwd_dkdv(q, k, v, dO, lse, cos_tab, sin_tab, dk, dv, workspace, workspace_bytes,
-                         B, H, T, D, dtype, stream);
+    return attn_bwd_dkdv(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dk, dv,
+                         workspace, workspace_bytes, B, H, T, D, dtype, stream);
 }
 
 const char* attn_status_string(int status) {
@@ -172,12 +236,13 @@ const char* attn_status_string(int status) {
         case ATTN_OK: return "ok";
         case ATTN_ERR_NULL: return "null pointer";
         case ATTN_ERR_SHAPE: return "unsupported shape";
-        case ATTN_ERR_DTYPE: return "unknown dtype";
+        case ATTN_ERR_DTYPE: return "unsupported dtype";
         case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
         case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
         case ATTN_ERR_HIP: return "HIP launch failed";
         case ATTN_ERR_ALIAS: return "output aliases an input";
         case ATTN_ERR_VALUE: return "invalid scalar argument";
+        case ATTN_ERR_SAVED: return "saved rotated q/k buffer too small";
         default: return "unknown status";
     }
 }

@@ -320,7 +320,7 @@ static hipError_t launch_dq32(const BwdArgs& a) {
     hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v,
                        (const float*)a.o, (const float*)a.dO, a.lse, a.cs, a.sn, (float*)a.dq,
-                       a.delta, BH, a.T, nqb, scale * kLog2e, scale);
+                       a.ws, BH, a.T, nqb, scale * kLog2e, scale);
     return hipGetLastError();
 }
 
@@ -332,7 +332,7 @@ static hipError_t launch_dkdv32(const BwdArgs& a) {
     const float scale = 1.f / sqrtf((float)D);
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<D>, dim3(nkb * BH), dim3(C::NT), 0, a.stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                       (const float*)a.dO, a.lse, a.delta, a.cs, a.sn, (float*)a.dk,
+                       (const float*)a.dO, a.lse, a.ws, a.cs, a.sn, (float*)a.dk,
                        (float*)a.dv, BH, a.T, nkb, scale * kLog2e, scale);
     return hipGetLastError();
 }

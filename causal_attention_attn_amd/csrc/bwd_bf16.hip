@@ -2,25 +2,28 @@
 //
 // The pages' engine computes every gradient by hand, RoPE's included, and checks
 // them against centred differences ("Show HN: NanoEuler", paragraph 2). Here the
-// backward recomputes the probabilities from q, k and the saved log-sum-exp
-// instead of storing the T x T matrix, in two deterministic kernels (no atomics):
+// backward recomputes the probabilities from the rotated q, k and the saved
+// log-sum-exp instead of storing the T x T matrix, in two deterministic kernels
+// (no atomics):
 //
 //   dq kernel   (one workgroup = 128 queries of a head; loops over key tiles
 //                up to the diagonal): delta_t = sum_d dO[t,d] o[t,d] in its
-//                prologue (written to the workspace), then
+//                prologue, written with lse_t*log2(e) to the workspace, then
 //                P = exp(S - lse), dP = dO V^T, dS = P (dP - delta),
 //                dQ^r += s dS K^r, and finally dq = R_t^T dQ^r.
 //   dkdv kernel (one workgroup = 128 keys of a head; loops over query tiles
 //                from the diagonal down): with the same P and dS,
 //                dV += P^T dO, dK^r += s dS^T Q^r, and finally dk = R_u^T dK^r.
 //
-// Every product is a 32x32x16 MFMA contraction with fp32 accumulation: the
-// score recompute uses fp16 operands (rotated q and k, as in the forward), the
-// others bf16 (dO, V, P, dS and bf16 copies of rotated q and k). In the dq kernel a
-// lane column is a query (S^T, dP^T, dQ^T), in the dkdv kernel a lane column is
-// a key (S, dP, dV^T, dK^T). Transposed LDS tiles store their columns in
-// col_perm order, so rounded P and dS are directly the B operand of the next
-// contraction and every A operand is one 16-byte LDS read.
+// Every product is a 32x32x16 MFMA contraction with fp32 accumulation. The
+// rotated q and k and dS are fp16 (the score recompute needs the 11-bit
+// significand, see the forward; dS then shares the fp16 MFMA with them, which
+// bounds |dS| by 65504); dO, V and P are bf16. In the dq kernel a lane column
+// is a query (S^T, dP^T, dQ^T), in the dkdv kernel a key (S, dP, dV^T, dK^T).
+// Tiles stream from global memory straight into an NS-stage LDS ring
+// (buffer_load ... lds); row-major tiles give the row operands with 16-byte
+// reads and the transposed operands through ds_read_b64_tr_b16, so rounded P
+// and dS registers are directly the B operand of the next contraction.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -29,84 +32,74 @@ namespace attn {
 template <int D>
 struct BwdTile {
     static constexpr int NT = 256;
+    static constexpr int NW = 4;
     static constexpr int DK = D / 16;
     static constexpr int DB = D / 32;
-    static constexpr int RS = D + 8;   // LDS row stride, row-major tiles
-    // dq kernel
-    static constexpr int QM = 128;     // queries per workgroup
-    static constexpr int KN = 64;      // keys per LDS tile
-    static constexpr int KTS = KN + 8; // LDS row stride, transposed key tile
-    // dkdv kernel
-    static constexpr int KM = 128;     // keys per workgroup
-    static constexpr int QN = 64;      // queries per LDS tile
-    static constexpr int QTS = QN + 8; // LDS row stride, transposed query tiles
-    // D = 64: two LDS buffers, the next tile's global loads issued before the
-    // current tile's math. D = 128: one buffer and no register prefetch (the
-    // staging registers would push the kernels past 256 VGPRs and two buffers
-    // would leave room for one workgroup per CU).
-    static constexpr int NBUF = D == 64 ? 2 : 1;
+    static constexpr int QM = 128;     // dq kernel: queries per workgroup
+    static constexpr int KN = 64;      // dq kernel: keys per LDS tile
+    static constexpr int KM = 128;     // dkdv kernel: keys per workgroup
+    static constexpr int QN = 64;      // dkdv kernel: queries per LDS tile
+    static constexpr int TILE = 64 * D * 2;            // bytes of one 64-row tile
+    static constexpr int NS = D == 64 ? 3 : 2;         // LDS ring stages
+    static constexpr int LPT = 2 * TILE / 1024 / NW;   // tile load instructions per wave
 };
 
 // One 64-key tile of the dq kernel for one wave (32 queries). DIAG: the tile may
 // reach this wave's diagonal (32-key blocks above it skipped, the diagonal one masked).
 template <int D, bool DIAG>
 __device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const bf16x8* df,
-                                        const f16* ks, const bf16* vs, const bf16* kt, int k0,
-                                        int wq0, int c32, int hf, float sc, float nlt,
-                                        float dl) {
+                                        const char* ks, const char* vs, int k0, int wq0,
+                                        int lane, float sc, float lt, float dl) {
     using C = BwdTile<D>;
+    const int c32 = lane & 31, hf = lane >> 5;
 #pragma unroll
     for (int sb = 0; sb < C::KN / 32; ++sb) {
         const int kb = k0 + 32 * sb;
         if (DIAG && kb > wq0) break;
-        const f16* krow = ks + (32 * sb + c32) * C::RS + 8 * hf;
-        const bf16* vrow = vs + (32 * sb + c32) * C::RS + 8 * hf;
-        f32x16 s = mfma32(*reinterpret_cast<const f16x8*>(krow), qf[0], f32x16{});
-        f32x16 dp = mfma32(*reinterpret_cast<const bf16x8*>(vrow), df[0], f32x16{});
+        const int row = 32 * sb + c32;
+        f32x16 s = mfma32(lds_row8<D, f16x8>(ks, row, 8 * hf), qf[0], f32x16{});
+        f32x16 dp = mfma32(lds_row8<D, bf16x8>(vs, row, 8 * hf), df[0], f32x16{});
 #pragma unroll
         for (int c = 1; c < C::DK; ++c) {
-            s = mfma32(*reinterpret_cast<const f16x8*>(krow + 16 * c), qf[c], s);
-            dp = mfma32(*reinterpret_cast<const bf16x8*>(vrow + 16 * c), df[c], dp);
+            s = mfma32(lds_row8<D, f16x8>(ks, row, 16 * c + 8 * hf), qf[c], s);
+            dp = mfma32(lds_row8<D, bf16x8>(vs, row, 16 * c + 8 * hf), df[c], dp);
         }
         if (DIAG && kb == wq0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 if (item_row(i, hf) > c32) s[i] = -INFINITY;
         }
-        bf16x8 dsb[2];
+        f16x8 dsb[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             u32x4 w;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 8 * j + 2 * e;
-                const float p0 = exp2_fast(fmaf(s[i], sc, nlt));
-                const float p1 = exp2_fast(fmaf(s[i + 1], sc, nlt));
-                w[e] = pack_bf16x2(p0 * (dp[i] - dl), p1 * (dp[i + 1] - dl));
+                const float p0 = exp2_fast(fmaf(s[i], sc, -lt));
+                const float p1 = exp2_fast(fmaf(s[i + 1], sc, -lt));
+                w[e] = pack2<f16>(p0 * (dp[i] - dl), p1 * (dp[i + 1] - dl));
             }
-            dsb[j] = as_bf16x8(w);
+            dsb[j] = as_vec8<f16x8>(w);
         }
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
-            const bf16* trow = kt + (32 * b + c32) * C::KTS + 32 * sb + 8 * hf;
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                acc[b] = mfma32(*reinterpret_cast<const bf16x8*>(trow + 16 * j), dsb[j], acc[b]);
+                acc[b] = mfma32(lds_tr8<D, f16x8>(ks, 32 * sb + 16 * j, 32 * b, lane), dsb[j], acc[b]);
         }
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
     const bf16* __restrict__ o, const bf16* __restrict__ dO, const float* __restrict__ lse,
     const float* __restrict__ cs, const float* __restrict__ sn, bf16* __restrict__ dq,
-    float* __restrict__ delta, int BH, int T, int nqb, float sc, float scale) {
+    float* __restrict__ ws, int BH, int T, int nqb, float sc, float scale) {
     using C = BwdTile<D>;
-    constexpr int NB = C::NBUF;
-    __shared__ __attribute__((aligned(16))) f16 Ks[NB][C::KN * C::RS];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[NB][C::KN * C::RS];
-    __shared__ __attribute__((aligned(16))) bf16 Kt[NB][D * C::KTS];
+    constexpr int NS = C::NS;
+    __shared__ __attribute__((aligned(1024))) char smem[NS][2 * C::TILE];
 
     const int bid = blockIdx.x;
     const int bh = bid % BH;
@@ -116,19 +109,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c32 = lane & 31, hf = lane >> 5;
     const size_t hoff = (size_t)bh * T * D;
-    const HeadBufs<D> qh(q + hoff, cs, sn, T), kh(k + hoff, cs, sn, T), vh(v + hoff, cs, sn, T);
-    const rsrc_t gr = make_rsrc(dO + hoff, (uint32_t)T * D * 2);
-    const rsrc_t orr = make_rsrc(o + hoff, (uint32_t)T * D * 2);
+    const uint32_t hbytes = (uint32_t)T * D * 2;
+    const rsrc_t qh = make_rsrc(qr + hoff, hbytes), kh = make_rsrc(kr + hoff, hbytes),
+                 vh = make_rsrc(v + hoff, hbytes), gh = make_rsrc(dO + hoff, hbytes),
+                 oh = make_rsrc(o + hoff, hbytes);
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
-
-    const int kend = min(T, q0 + C::QM);
-    const int ntiles = (kend + C::KN - 1) / C::KN;
-    const int nfull = min(ntiles, q0 / C::KN);
-    RowStage<D, C::KN, C::NT, true> kst;
-    RowStage<D, C::KN, C::NT, false> vst;
-    kst.load(kh, 0, tid);
-    vst.load(vh, 0, tid);
 
     // this lane's query: rotated q (fp16), dO (bf16), and delta = sum_d dO o
     f16x8 qf[C::DK];
@@ -136,50 +122,47 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
     float dot = 0.f;
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) {
-        const int d0 = 16 * c + 8 * hf;
-        qf[c] = rope_operand<D, f16>(qh, tq, d0);
-        const u32x4 g = buf_load16(gr, (uint32_t)(tq * D + d0) * 2);
-        const u32x4 y = buf_load16(orr, (uint32_t)(tq * D + d0) * 2);
+        const uint32_t off = (uint32_t)(tq * D + 16 * c + 8 * hf) * 2;
+        qf[c] = __builtin_bit_cast(f16x8, buf_load16(qh, off));
+        const u32x4 g = buf_load16(gh, off);
+        const u32x4 y = buf_load16(oh, off);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             dot += bf16_lo(g[e]) * bf16_lo(y[e]) + bf16_hi(g[e]) * bf16_hi(y[e]);
         df[c] = as_bf16x8(g);
     }
     const float dl = sum_across_halves(dot);
-    const float nlt = tq < T ? -lse[(size_t)bh * T + tq] * kLog2e : 0.f;
-    if (tq < T && hf == 0) delta[(size_t)bh * T + tq] = dl;
+    const float lt = tq < T ? lse[(size_t)bh * T + tq] * kLog2e : 0.f;
+    if (tq < T && hf == 0) *reinterpret_cast<f32x2*>(ws + 2 * ((size_t)bh * T + tq)) = f32x2{lt, dl};
+
+    const int kend = min(T, q0 + C::QM);
+    const int ntiles = (kend + C::KN - 1) / C::KN;
+    const int nfull = min(ntiles, q0 / C::KN);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) {
+        issue_tile<D, C::KN, C::NW>(kh, s * C::KN, smem[s], wave, lane);
+        issue_tile<D, C::KN, C::NW>(vh, s * C::KN, smem[s] + C::TILE, wave, lane);
+    }
 
     f32x16 acc[C::DB];
 #pragma unroll
     for (int b = 0; b < C::DB; ++b) acc[b] = f32x16{};
 
-    kst.template store<f16, bf16>(Ks[0], Kt[0], tid);
-    vst.template store<bf16, void>(Vs[0], nullptr, tid);
-    __syncthreads();
-
     for (int n = 0; n < ntiles; ++n) {
-        const int k0 = n * C::KN;
-        const int cur = n % NB;
-        const bool more = n + 1 < ntiles;
-        if (NB == 2 && more) {
-            kst.load(kh, k0 + C::KN, tid);
-            vst.load(vh, k0 + C::KN, tid);
-        }
-        if (n < nfull)
-            dq_tile<D, false>(acc, qf, df, Ks[cur], Vs[cur], Kt[cur], k0, wq0, c32, hf, sc, nlt, dl);
-        else if (k0 <= wq0)
-            dq_tile<D, true>(acc, qf, df, Ks[cur], Vs[cur], Kt[cur], k0, wq0, c32, hf, sc, nlt, dl);
-        if (more) {
-            if (NB == 1) {  // no prefetch: wait for every wave, then load and store
-                __syncthreads();
-                kst.load(kh, k0 + C::KN, tid);
-                vst.load(vh, k0 + C::KN, tid);
-            }
-            kst.template store<f16, bf16>(Ks[(n + 1) % NB], Kt[(n + 1) % NB], tid);
-            vst.template store<bf16, void>(Vs[(n + 1) % NB], nullptr, tid);
-        }
+        wait_vmcnt<C::LPT * (NS - 2)>();
         __syncthreads();
+        const int nx = n + NS - 1;
+        issue_tile<D, C::KN, C::NW>(kh, nx * C::KN, smem[nx % NS], wave, lane);
+        issue_tile<D, C::KN, C::NW>(vh, nx * C::KN, smem[nx % NS] + C::TILE, wave, lane);
+        const char* ks = smem[n % NS];
+        const char* vs = ks + C::TILE;
+        const int k0 = n * C::KN;
+        if (n < nfull)
+            dq_tile<D, false>(acc, qf, df, ks, vs, k0, wq0, lane, sc, lt, dl);
+        else if (k0 <= wq0)
+            dq_tile<D, true>(acc, qf, df, ks, vs, k0, wq0, lane, sc, lt, dl);
     }
+    wait_vmcnt<0>();
 
     if (tq < T) {
         bf16* out = dq + hoff + (size_t)tq * D;
@@ -207,63 +190,62 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
 
 // One 64-query tile of the dk/dv kernel for one wave (32 keys). DIAG: the tile
 // may reach this wave's diagonal (32-query blocks wholly before the wave's
-// first key skipped, the diagonal one masked).
+// first key skipped, the diagonal one masked). ld holds (lse*log2 e, delta)
+// for the tile's 64 queries.
 template <int D, bool DIAG>
 __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8* kf,
-                                          const bf16x8* vf, const f16* qs, const bf16* gs,
-                                          const bf16* qt, const bf16* gt, const float* ls,
-                                          const float* dls, int qbase, int wk0, int c32, int hf,
+                                          const bf16x8* vf, const char* qs, const char* gs,
+                                          const float* ld, int qbase, int wk0, int lane,
                                           float sc) {
     using C = BwdTile<D>;
+    const int c32 = lane & 31, hf = lane >> 5;
 #pragma unroll
     for (int sb = 0; sb < C::QN / 32; ++sb) {
         const int qb = qbase + 32 * sb;
         if (DIAG && qb + 31 < wk0) continue;
-        const f16* qrow = qs + (32 * sb + c32) * C::RS + 8 * hf;
-        const bf16* grow = gs + (32 * sb + c32) * C::RS + 8 * hf;
-        f32x16 s = mfma32(*reinterpret_cast<const f16x8*>(qrow), kf[0], f32x16{});
-        f32x16 dp = mfma32(*reinterpret_cast<const bf16x8*>(grow), vf[0], f32x16{});
+        const int row = 32 * sb + c32;
+        f32x16 s = mfma32(lds_row8<D, f16x8>(qs, row, 8 * hf), kf[0], f32x16{});
+        f32x16 dp = mfma32(lds_row8<D, bf16x8>(gs, row, 8 * hf), vf[0], f32x16{});
 #pragma unroll
         for (int c = 1; c < C::DK; ++c) {
-            s = mfma32(*reinterpret_cast<const f16x8*>(qrow + 16 * c), kf[c], s);
-            dp = mfma32(*reinterpret_cast<const bf16x8*>(grow + 16 * c), vf[c], dp);
+            s = mfma32(lds_row8<D, f16x8>(qs, row, 16 * c + 8 * hf), kf[c], s);
+            dp = mfma32(lds_row8<D, bf16x8>(gs, row, 16 * c + 8 * hf), vf[c], dp);
         }
         if (DIAG && qb == wk0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 if (item_row(i, hf) < c32) s[i] = -INFINITY;
         }
-        bf16x8 pb[2], dsb[2];
+        bf16x8 pb[2];
+        f16x8 dsb[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             u32x4 wp, wd;
 #pragma unroll
             for (int g2 = 0; g2 < 2; ++g2) {
                 // items 8j + 4*g2 .. +3 belong to queries 16j + 8*g2 + 4*hf .. +3
-                const int qo = 32 * sb + 16 * j + 8 * g2 + 4 * hf;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
-                const f32x4 e4 = *reinterpret_cast<const f32x4*>(dls + qo);
-#pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    const int i = 8 * j + 4 * g2 + 2 * x;
-                    const float p0 = exp2_fast(fmaf(s[i], sc, l4[2 * x]));
-                    const float p1 = exp2_fast(fmaf(s[i + 1], sc, l4[2 * x + 1]));
-                    wp[2 * g2 + x] = pack_bf16x2(p0, p1);
-                    wd[2 * g2 + x] = pack_bf16x2(p0 * (dp[i] - e4[2 * x]),
-                                                 p1 * (dp[i + 1] - e4[2 * x + 1]));
-                }
+                const float* lq = ld + 2 * (32 * sb + 16 * j + 8 * g2 + 4 * hf);
+                const f32x4 a01 = *reinterpret_cast<const f32x4*>(lq);      // l0 d0 l1 d1
+                const f32x4 a23 = *reinterpret_cast<const f32x4*>(lq + 4);  // l2 d2 l3 d3
+                const int i = 8 * j + 4 * g2;
+                const float p0 = exp2_fast(fmaf(s[i], sc, -a01[0]));
+                const float p1 = exp2_fast(fmaf(s[i + 1], sc, -a01[2]));
+                const float p2 = exp2_fast(fmaf(s[i + 2], sc, -a23[0]));
+                const float p3 = exp2_fast(fmaf(s[i + 3], sc, -a23[2]));
+                wp[2 * g2] = pack_bf16x2(p0, p1);
+                wp[2 * g2 + 1] = pack_bf16x2(p2, p3);
+                wd[2 * g2] = pack2<f16>(p0 * (dp[i] - a01[1]), p1 * (dp[i + 1] - a01[3]));
+                wd[2 * g2 + 1] = pack2<f16>(p2 * (dp[i + 2] - a23[1]), p3 * (dp[i + 3] - a23[3]));
             }
             pb[j] = as_bf16x8(wp);
-            dsb[j] = as_bf16x8(wd);
+            dsb[j] = as_vec8<f16x8>(wd);
         }
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
-            const bf16* gtr = gt + (32 * b + c32) * C::QTS + 32 * sb + 8 * hf;
-            const bf16* qtr = qt + (32 * b + c32) * C::QTS + 32 * sb + 8 * hf;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                dva[b] = mfma32(*reinterpret_cast<const bf16x8*>(gtr + 16 * j), pb[j], dva[b]);
-                dka[b] = mfma32(*reinterpret_cast<const bf16x8*>(qtr + 16 * j), dsb[j], dka[b]);
+                dva[b] = mfma32(lds_tr8<D, bf16x8>(gs, 32 * sb + 16 * j, 32 * b, lane), pb[j], dva[b]);
+                dka[b] = mfma32(lds_tr8<D, f16x8>(qs, 32 * sb + 16 * j, 32 * b, lane), dsb[j], dka[b]);
             }
         }
     }
@@ -271,19 +253,14 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8*
 
 template <int D>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ dO, const float* __restrict__ lse,
-    const float* __restrict__ delta, const float* __restrict__ cs,
+    const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
+    const bf16* __restrict__ dO, const float* __restrict__ ws, const float* __restrict__ cs,
     const float* __restrict__ sn, bf16* __restrict__ dk, bf16* __restrict__ dv, int BH, int T,
     int nkb, float sc, float scale) {
     using C = BwdTile<D>;
-    constexpr int NB = C::NBUF;
-    __shared__ __attribute__((aligned(16))) f16 Qs[NB][C::QN * C::RS];
-    __shared__ __attribute__((aligned(16))) bf16 Gs[NB][C::QN * C::RS];
-    __shared__ __attribute__((aligned(16))) bf16 Qt[NB][D * C::QTS];
-    __shared__ __attribute__((aligned(16))) bf16 Gt[NB][D * C::QTS];
-    __shared__ __attribute__((aligned(16))) float Ls[NB][C::QN];
-    __shared__ __attribute__((aligned(16))) float Dl[NB][C::QN];
+    constexpr int NS = C::NS;
+    constexpr int STAGE = 2 * C::TILE + 512;  // Q tile, dO tile, 64 x (lse*log2 e, delta)
+    __shared__ __attribute__((aligned(1024))) char smem[NS][STAGE];
 
     const int bid = blockIdx.x;
     const int bh = bid % BH;
@@ -293,74 +270,56 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c32 = lane & 31, hf = lane >> 5;
     const size_t hoff = (size_t)bh * T * D;
-    const size_t roff = (size_t)bh * T;
-    const HeadBufs<D> qh(q + hoff, cs, sn, T), kh(k + hoff, cs, sn, T), vh(v + hoff, cs, sn, T),
-        gh(dO + hoff, cs, sn, T);
+    const uint32_t hbytes = (uint32_t)T * D * 2;
+    const rsrc_t qh = make_rsrc(qr + hoff, hbytes), kh = make_rsrc(kr + hoff, hbytes),
+                 vh = make_rsrc(v + hoff, hbytes), gh = make_rsrc(dO + hoff, hbytes),
+                 lh = make_rsrc(ws + 2 * (size_t)bh * T, (uint32_t)T * 8);
     const int wk0 = k0 + wave * 32;
     const int tk = wk0 + c32;
 
     const int qt0 = k0 / C::QN;
     const int nqt = (T + C::QN - 1) / C::QN;
     const int qfull = min(nqt, (k0 + C::KM) / C::QN);  // from here on no query precedes a key
-    RowStage<D, C::QN, C::NT, true> qst;
-    RowStage<D, C::QN, C::NT, false> gst;
-    float l_pre = 0.f, d_pre = 0.f;
-    auto load_tile = [&](int qt) {
-        const int qbase = qt * C::QN;
-        qst.load(qh, qbase, tid);
-        gst.load(gh, qbase, tid);
-        if (tid < C::QN) {
-            const int t = qbase + tid;
-            l_pre = t < T ? -lse[roff + t] * kLog2e : -INFINITY;
-            d_pre = t < T ? delta[roff + t] : 0.f;
-        }
+    // one tile = Q, dO (row-major) and the (lse*log2 e, delta) pairs of its 64
+    // queries; each wave fetches 16 of those pairs with one dword load
+    auto issue = [&](int qt, char* st) {
+        issue_tile<D, C::QN, C::NW>(qh, qt * C::QN, st, wave, lane);
+        issue_tile<D, C::QN, C::NW>(gh, qt * C::QN, st + C::TILE, wave, lane);
+        if (lane < 32)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                lh, LDS_PTR(st + 2 * C::TILE + 128 * wave), 4,
+                (uint32_t)((qt * C::QN + 16 * wave) * 8 + 4 * lane), 0, 0, 0);
     };
-    auto store_tile = [&](int buf) {
-        qst.template store<f16, bf16>(Qs[buf], Qt[buf], tid);
-        gst.template store<bf16, bf16>(Gs[buf], Gt[buf], tid);
-        if (tid < C::QN) {
-            Ls[buf][tid] = l_pre;
-            Dl[buf][tid] = d_pre;
-        }
-    };
-    load_tile(qt0);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(qt0 + s, smem[s]);
 
     f16x8 kf[C::DK];
     bf16x8 vf[C::DK];
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) {
-        const int d0 = 16 * c + 8 * hf;
-        kf[c] = rope_operand<D, f16>(kh, tk, d0);
-        vf[c] = as_bf16x8(buf_load16(vh.x, (uint32_t)(tk * D + d0) * 2));
+        const uint32_t off = (uint32_t)(tk * D + 16 * c + 8 * hf) * 2;
+        kf[c] = __builtin_bit_cast(f16x8, buf_load16(kh, off));
+        vf[c] = as_bf16x8(buf_load16(vh, off));
     }
     f32x16 dva[C::DB], dka[C::DB];
 #pragma unroll
     for (int b = 0; b < C::DB; ++b) dva[b] = dka[b] = f32x16{};
 
-    store_tile(0);
-    __syncthreads();
-
     for (int qt = qt0; qt < nqt; ++qt) {
-        const int qbase = qt * C::QN;
         const int it = qt - qt0;
-        const int cur = it % NB;
-        const bool more = qt + 1 < nqt;
-        if (NB == 2 && more) load_tile(qt + 1);
-        if (qt >= qfull)
-            dkdv_tile<D, false>(dva, dka, kf, vf, Qs[cur], Gs[cur], Qt[cur], Gt[cur], Ls[cur],
-                                Dl[cur], qbase, wk0, c32, hf, sc);
-        else if (qbase + C::QN - 1 >= wk0)
-            dkdv_tile<D, true>(dva, dka, kf, vf, Qs[cur], Gs[cur], Qt[cur], Gt[cur], Ls[cur],
-                               Dl[cur], qbase, wk0, c32, hf, sc);
-        if (more) {
-            if (NB == 1) {  // no prefetch: wait for every wave, then load and store
-                __syncthreads();
-                load_tile(qt + 1);
-            }
-            store_tile((it + 1) % NB);
-        }
+        wait_vmcnt<(C::LPT + 1) * (NS - 2)>();
         __syncthreads();
+        issue(qt + NS - 1, smem[(it + NS - 1) % NS]);
+        const char* qs = smem[it % NS];
+        const char* gs = qs + C::TILE;
+        const float* ld = reinterpret_cast<const float*>(qs + 2 * C::TILE);
+        const int qbase = qt * C::QN;
+        if (qt >= qfull)
+            dkdv_tile<D, false>(dva, dka, kf, vf, qs, gs, ld, qbase, wk0, lane, sc);
+        else if (qbase + C::QN - 1 >= wk0)
+            dkdv_tile<D, true>(dva, dka, kf, vf, qs, gs, ld, qbase, wk0, lane, sc);
     }
+    wait_vmcnt<0>();
 
     if (tk < T) {
         bf16* ko = dk + hoff + (size_t)tk * D;
@@ -395,10 +354,11 @@ static hipError_t launch_dq(const BwdArgs& a) {
     const int BH = a.B * a.H;
     const int nqb = (a.T + C::QM - 1) / C::QM;
     const float scale = 1.f / sqrtf((float)D);
-    hipLaunchKernelGGL(bwd_dq_bf16_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.o,
-                       (const bf16*)a.dO, a.lse, a.cs, a.sn, (bf16*)a.dq, a.delta, BH, a.T, nqb,
-                       scale * kLog2e, scale);
+    const size_t n = (size_t)a.B * a.H * a.T * a.D;
+    const f16* rot = static_cast<const f16*>(a.rot);
+    hipLaunchKernelGGL(bwd_dq_bf16_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream, rot,
+                       rot + n, (const bf16*)a.v, (const bf16*)a.o, (const bf16*)a.dO, a.lse,
+                       a.cs, a.sn, (bf16*)a.dq, a.ws, BH, a.T, nqb, scale * kLog2e, scale);
     return hipGetLastError();
 }
 
@@ -408,10 +368,11 @@ static hipError_t launch_dkdv(const BwdArgs& a) {
     const int BH = a.B * a.H;
     const int nkb = (a.T + C::KM - 1) / C::KM;
     const float scale = 1.f / sqrtf((float)D);
-    hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<D>, dim3(nkb * BH), dim3(C::NT), 0, a.stream,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dO,
-                       a.lse, a.delta, a.cs, a.sn, (bf16*)a.dk, (bf16*)a.dv, BH, a.T, nkb,
-                       scale * kLog2e, scale);
+    const size_t n = (size_t)a.B * a.H * a.T * a.D;
+    const f16* rot = static_cast<const f16*>(a.rot);
+    hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<D>, dim3(nkb * BH), dim3(C::NT), 0, a.stream, rot,
+                       rot + n, (const bf16*)a.v, (const bf16*)a.dO, a.ws, a.cs, a.sn,
+                       (bf16*)a.dk, (bf16*)a.dv, BH, a.T, nkb, scale * kLog2e, scale);
     return hipGetLastError();
 }
 

@@ -212,3 +212,83 @@ struct RowStage {
 };
 
 }  // namespace attn
+
+namespace attn {
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS tile streaming and LDS operand reads.
+//
+// Tiles of ROWS rows x D 16-bit values are stored row-major in LDS without
+// padding; within a row the 16-byte chunks are permuted by an XOR swizzle of
+// the row index so that the MFMA operand reads below hit distinct banks.
+// Loads use buffer_load ... lds: lane l of a wave instruction writes its 16
+// bytes at (wave base + 16 l), so one instruction fills 1 KB; each lane fetches
+// the global chunk that belongs at its LDS position. Offsets past the end of
+// the buffer (rows >= T) read as zeros.
+// ---------------------------------------------------------------------------
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// swizzled 16-byte chunk position of chunk c in tile row r
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
+
+// Byte offset inside a tile of element (r, col) (col a multiple of 4).
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {
+    return r * (D * 2) + 16 * swz(r, col >> 3) + 2 * (col & 7);
+}
+
+// Issue the loads of one ROWS x D tile (rows r0 .. r0+ROWS-1 of a [T, D] head
+// held by buffer `src`) into LDS at `tile`. NW waves share the work; every wave
+// issues exactly ROWS * D / (64 * 8 * NW) instructions.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void issue_tile(rsrc_t src, int r0, char* tile, int wave, int lane) {
+    constexpr int NC = D / 8;                       // 16-byte chunks per row
+    constexpr int INSTR = ROWS * NC / 64;           // 1 KB instructions per tile
+    static_assert(INSTR % NW == 0, "tile instructions must divide among waves");
+    constexpr int IPW = INSTR / NW;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int blk = wave * IPW + i;
+        const int p = blk * 64 + lane;              // LDS chunk index
+        const int r = p / NC, pos = p % NC;
+        const int c = swz(r, pos) & (NC - 1);       // global chunk stored at this position
+        const uint32_t voff = (uint32_t)((r0 + r) * D + 8 * c) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, LDS_PTR(tile + blk * 1024), 16, voff, 0, 0, 0);
+    }
+}
+
+// 8 consecutive 16-bit values of row r starting at column col (a multiple of 8).
+template <int D, typename V>
+__device__ __forceinline__ V lds_row8(const char* tile, int r, int col) {
+    return *reinterpret_cast<const V*>(tile + tile_off<D>(r, col));
+}
+
+// A operand X^T for a 32x32x16 MFMA from a row-major tile X[rows][D]:
+// lane (c = lane & 31, h = lane >> 5) receives X[row0 + 8*(i>>2) + 4h + (i&3)][col0 + c]
+// for items i = 0..7 - the row order of the items of a 32x32 result (item i of
+// lane half h is row 8*(i>>2) + 4h + (i&3)), so that rounded result items can be
+// the B operand. Two ds_read_b64_tr_b16: within each 16-lane group, lane m gets
+// element m&3 of the 8-byte reads of lanes 4j + (m>>2), j = 0..3.
+template <int D, typename V>
+__device__ __forceinline__ V lds_tr8(const char* tile, int row0, int col0, int lane) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int g = lane >> 4, m = lane & 15;
+    const int row = row0 + 4 * (g >> 1) + (m >> 2);
+    const int col = col0 + 16 * (g & 1) + 4 * (m & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(tile + tile_off<D>(row, col)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(tile + tile_off<D>(row + 8, col)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(V, r);
+}
+
+}  // namespace attn

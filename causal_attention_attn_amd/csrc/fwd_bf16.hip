@@ -3,25 +3,26 @@
 // FlashAttention-style exact attention ("Show HN: NanoEuler", paragraph 2): the
 // score matrix is produced tile by tile in registers, a running row maximum and
 // row sum implement the softmax online, and only o and the per-row log-sum-exp
-// reach HBM. RoPE ("Tiny Hackable CUDA", section 3) is applied while q and k are
-// loaded. Causality (keys u <= query t) is enforced by skipping every 32x32 block
-// that lies wholly above the diagonal and masking only the diagonal blocks.
+// reach HBM. RoPE ("Tiny Hackable CUDA", section 3) has already been applied by
+// the rotation pass: q and k arrive rotated, in fp16. Causality (keys u <=
+// query t) is enforced by skipping every 32x32 block wholly above the diagonal
+// and masking only the diagonal blocks.
 //
 // Work decomposition (one workgroup = 4 waves = 128 queries of one head):
 //   * each wave owns 32 queries; its rotated queries live in registers as the
-//     B operand of S^T = K Q^T (v_mfma_f32_32x32x16_f16, k = head dim);
-//   * 64-key tiles of rotated K (row-major) and of V (transposed, [d][key]) are
-//     staged in LDS and shared by the four waves;
-//   * rotated q and k are no longer bf16 values, so they are rounded once to
-//     fp16 (11-bit significand) for the score product: the softmax turns score
-//     errors into relative weight errors, and with bf16 operands they reach
-//     ~3e-2 on O for logits of standard deviation ~9. P and V stay bf16
-//     (v_mfma_f32_32x32x16_bf16). fp16 bounds |rotated q|, |rotated k| by 65504;
+//     B operand of S^T = K Q^T (v_mfma_f32_32x32x16_f16, k = head dim). The
+//     rotated q and k are not bf16 values; fp16's 11-bit significand keeps the
+//     score error small where the softmax is sharp (bf16 operands give ~3e-2
+//     error on O for logits of standard deviation ~9). P and V stay bf16.
+//   * 64-key tiles of rotated K (fp16) and V (bf16) stream straight from
+//     global memory into an NS-stage LDS ring (buffer_load ... lds), issued
+//     NS-1 tiles ahead of use: no registers hold tiles in flight, and one
+//     barrier per tile both publishes a tile and frees the oldest stage;
 //   * S^T puts one query per lane column, so each lane owns one query's running
 //     max/sum and only one cross-lane exchange (lane ^ 32) is needed per tile;
-//   * V is stored transposed with its key columns in col_perm order, so the
-//     rounded probabilities of S^T are directly the B operand of
-//     O^T += V^T P^T and each A operand is one 16-byte LDS read;
+//   * the rounded probabilities of S^T are directly the B operand of
+//     O^T += V^T P^T; the V^T operand comes from the row-major V tile through
+//     the LDS transpose read (ds_read_b64_tr_b16);
 //   * tiles wholly below the block's first query take a branch-free path; only
 //     the last one or two tiles check for skipped and masked 32-key blocks;
 //   * workgroups are issued heaviest q-block first; consecutive block ids walk
@@ -34,14 +35,16 @@ namespace attn {
 
 template <int D>
 struct FwdTile {
-    static constexpr int BM = 128;     // queries per workgroup
-    static constexpr int BN = 64;      // keys per LDS tile
-    static constexpr int NT = 256;     // threads per workgroup
-    static constexpr int DK = D / 16;  // MFMA k-chunks over the head dimension
-    static constexpr int DB = D / 32;  // 32-row blocks of the head dimension
-    static constexpr int KS = D + 8;   // LDS row stride of the K tile (elements)
-    static constexpr int VS = BN + 8;  // LDS row stride of the transposed V tile
+    static constexpr int BM = 128;      // queries per workgroup
+    static constexpr int BN = 64;       // keys per LDS tile
+    static constexpr int NT = 256;      // threads per workgroup
+    static constexpr int NW = 4;        // waves per workgroup
+    static constexpr int DK = D / 16;   // MFMA k-chunks over the head dimension
+    static constexpr int DB = D / 32;   // 32-row blocks of the head dimension
     static constexpr int NSB = BN / 32;
+    static constexpr int TILE = BN * D * 2;            // bytes of one K or V tile
+    static constexpr int NS = D == 64 ? 3 : 2;         // LDS ring stages
+    static constexpr int LPT = 2 * TILE / 1024 / NW;   // load instructions per wave per tile
 };
 
 // Running state of one lane's query: O^T accumulator (this lane's half of the
@@ -55,20 +58,20 @@ struct FwdState {
 // One 64-key tile for one wave. DIAG: the tile may reach this wave's diagonal,
 // so 32-key sub-blocks above it are skipped and the diagonal one is masked.
 template <int D, bool DIAG>
-__device__ __forceinline__ void fwd_tile(FwdState<D>& st, const f16x8* qf, const f16* ks,
-                                         const bf16* vt, int k0, int wq0, int c32, int hf,
-                                         float sc) {
+__device__ __forceinline__ void fwd_tile(FwdState<D>& st, const f16x8* qf, const char* ks,
+                                         const char* vs, int k0, int wq0, int lane, float sc) {
     using C = FwdTile<D>;
     constexpr float kRescale = 8.f;
+    const int c32 = lane & 31, hf = lane >> 5;
     f32x16 s[C::NSB];
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
         if (DIAG && k0 + 32 * sb > wq0) break;
-        const f16* krow = ks + (32 * sb + c32) * C::KS + 8 * hf;
-        f32x16 acc = mfma32(*reinterpret_cast<const f16x8*>(krow), qf[0], f32x16{});
+        const int row = 32 * sb + c32;
+        f32x16 acc = mfma32(lds_row8<D, f16x8>(ks, row, 8 * hf), qf[0], f32x16{});
 #pragma unroll
         for (int c = 1; c < C::DK; ++c)
-            acc = mfma32(*reinterpret_cast<const f16x8*>(krow + 16 * c), qf[c], acc);
+            acc = mfma32(lds_row8<D, f16x8>(ks, row, 16 * c + 8 * hf), qf[c], acc);
         s[sb] = acc;
     }
     float mx = -INFINITY;
@@ -113,23 +116,21 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const f16x8* qf, const
         }
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
-            const bf16* vrow = vt + (32 * b + c32) * C::VS + 32 * sb + 8 * hf;
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                st.o[b] = mfma32(*reinterpret_cast<const bf16x8*>(vrow + 16 * j), pb[j], st.o[b]);
+                st.o[b] = mfma32(lds_tr8<D, bf16x8>(vs, 32 * sb + 16 * j, 32 * b, lane), pb[j],
+                                 st.o[b]);
         }
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ cs, const float* __restrict__ sn, bf16* __restrict__ o,
-    float* __restrict__ lse, int BH, int T, int nqb, float sc) {
+    const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
+    bf16* __restrict__ o, float* __restrict__ lse, int BH, int T, int nqb, float sc) {
     using C = FwdTile<D>;
-    // two buffers of (rotated K row-major, V transposed); one barrier per tile
-    __shared__ __attribute__((aligned(16))) f16 Ks[2][C::BN * C::KS];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * C::VS];
+    constexpr int NS = C::NS;
+    __shared__ __attribute__((aligned(1024))) char smem[NS][2 * C::TILE];
 
     const int bid = blockIdx.x;
     const int bh = bid % BH;
@@ -139,21 +140,27 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c32 = lane & 31, hf = lane >> 5;
     const size_t hoff = (size_t)bh * T * D;
-    const HeadBufs<D> qb_(q + hoff, cs, sn, T), kb_(k + hoff, cs, sn, T), vb_(v + hoff, cs, sn, T);
+    const uint32_t hbytes = (uint32_t)T * D * 2;
+    const rsrc_t qh = make_rsrc(qr + hoff, hbytes), kh = make_rsrc(kr + hoff, hbytes),
+                 vh = make_rsrc(v + hoff, hbytes);
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
 
     const int kend = min(T, q0 + C::BM);
     const int ntiles = (kend + C::BN - 1) / C::BN;
     const int nfull = min(ntiles, q0 / C::BN);  // tiles wholly below every query of the block
-    RowStage<D, C::BN, C::NT, true> kst;
-    RowStage<D, C::BN, C::NT, false> vst;
-    kst.load(kb_, 0, tid);
-    vst.load(vb_, 0, tid);
+
+    // prologue: tiles 0 .. NS-2 in flight (tiles past the end are harmless reads)
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) {
+        issue_tile<D, C::BN, C::NW>(kh, s * C::BN, smem[s], wave, lane);
+        issue_tile<D, C::BN, C::NW>(vh, s * C::BN, smem[s] + C::TILE, wave, lane);
+    }
 
     f16x8 qf[C::DK];
 #pragma unroll
-    for (int c = 0; c < C::DK; ++c) qf[c] = rope_operand<D, f16>(qb_, tq, 16 * c + 8 * hf);
+    for (int c = 0; c < C::DK; ++c)
+        qf[c] = __builtin_bit_cast(f16x8, buf_load16(qh, (uint32_t)(tq * D + 16 * c + 8 * hf) * 2));
 
     FwdState<D> st;
 #pragma unroll
@@ -161,28 +168,24 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     st.m = -INFINITY;
     st.l = 0.f;
 
-    kst.template store<f16, void>(Ks[0], nullptr, tid);
-    vst.template store<void, bf16>(nullptr, Vt[0], tid);
-    __syncthreads();
-
     for (int n = 0; n < ntiles; ++n) {
-        const int k0 = n * C::BN;
-        const int cur = n & 1;
-        const bool more = n + 1 < ntiles;
-        if (more) {
-            kst.load(kb_, k0 + C::BN, tid);
-            vst.load(vb_, k0 + C::BN, tid);
-        }
-        if (n < nfull)
-            fwd_tile<D, false>(st, qf, Ks[cur], Vt[cur], k0, wq0, c32, hf, sc);
-        else if (k0 <= wq0)
-            fwd_tile<D, true>(st, qf, Ks[cur], Vt[cur], k0, wq0, c32, hf, sc);
-        if (more) {
-            kst.template store<f16, void>(Ks[cur ^ 1], nullptr, tid);
-            vst.template store<void, bf16>(nullptr, Vt[cur ^ 1], tid);
-        }
+        // this wave's loads of tile n are complete once at most NS-2 tiles'
+        // worth of its loads remain; the barrier publishes every wave's share
+        // and guarantees that stage (n-1) % NS is no longer read
+        wait_vmcnt<C::LPT * (NS - 2)>();
         __syncthreads();
+        const int nx = n + NS - 1;
+        issue_tile<D, C::BN, C::NW>(kh, nx * C::BN, smem[nx % NS], wave, lane);
+        issue_tile<D, C::BN, C::NW>(vh, nx * C::BN, smem[nx % NS] + C::TILE, wave, lane);
+        const char* ks = smem[n % NS];
+        const char* vs = ks + C::TILE;
+        const int k0 = n * C::BN;
+        if (n < nfull)
+            fwd_tile<D, false>(st, qf, ks, vs, k0, wq0, lane, sc);
+        else if (k0 <= wq0)
+            fwd_tile<D, true>(st, qf, ks, vs, k0, wq0, lane, sc);
     }
+    wait_vmcnt<0>();  // no LDS writes may land after this workgroup's LDS is released
 
     const float l_tot = sum_across_halves(st.l);
     if (tq < T) {
@@ -208,9 +211,10 @@ static hipError_t launch_fwd(const FwdArgs& a) {
     const int BH = a.B * a.H;
     const int nqb = (a.T + C::BM - 1) / C::BM;
     const float sc = kLog2e / sqrtf((float)D);
-    hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.cs, a.sn,
-                       (bf16*)a.o, a.lse, BH, a.T, nqb, sc);
+    const size_t n = (size_t)a.B * a.H * a.T * a.D;
+    const f16* rot = static_cast<const f16*>(a.rot);
+    hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream, rot,
+                       rot + n, (const bf16*)a.v, (bf16*)a.o, a.lse, BH, a.T, nqb, sc);
     return hipGetLastError();
 }
 

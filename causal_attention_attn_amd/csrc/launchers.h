@@ -10,6 +10,7 @@ namespace attn {
 struct FwdArgs {
     const void *q, *k, *v;
     const float *cs, *sn;
+    const void* rot;  // bf16 path: rotated q then rotated k, [B, H, T, D] fp16 each
     void* o;
     float* lse;
     int B, H, T, D;
@@ -19,13 +20,16 @@ struct FwdArgs {
 struct BwdArgs {
     const void *q, *k, *v, *o, *dO;
     const float *lse, *cs, *sn;
+    const void* rot;  // bf16 path: rotated q then rotated k, [B, H, T, D] fp16 each
     void *dq, *dk, *dv;
-    float* delta;  // [B, H, T] fp32 workspace
+    float* ws;  // workspace: bf16 path [B, H, T] x (lse*log2 e, delta); fp32 path [B, H, T] delta
     int B, H, T, D;
     hipStream_t stream;
 };
 
 hipError_t launch_rope_tables(float* cs, float* sn, int T, int D, double base, hipStream_t s);
+hipError_t launch_rotate_qk(const void* q, const void* k, const float* cs, const float* sn,
+                            void* out, int B, int H, int T, int D, hipStream_t s);
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a);

@@ -26,8 +26,9 @@
  *   - Every tensor pointer is a DEVICE pointer, 16-byte aligned; tensors are
  *     contiguous row-major [B, H, T, D] with D innermost; lse and the backward
  *     workspace hold [B, H, T] fp32; cos/sin tables are [T, D/2] fp32.
- *   - dtype is ATTN_BF16 (bf16 storage, fp32 accumulation) or ATTN_F32 (fp32
- *     everywhere); it applies to q, k, v, o, dO, dq, dk and dv.
+ *   - dtype is ATTN_BF16 (bf16 storage, fp32 accumulation; rotated q/k and dS
+ *     are carried in fp16 inside the kernels) or ATTN_F32 (fp32 everywhere); it
+ *     applies to q, k, v, o, dO, dq, dk and dv.
  *   - D in {64, 128}; T >= 1; B*H >= 1; B*H*T*D < 2^31. The scale is fixed at
  *     1/sqrt(D). There is no dropout, bias, padding mask or grouped-query sharing.
  *   - The caller owns all memory. The library never allocates, frees or
@@ -59,7 +60,8 @@ enum attn_status {
     ATTN_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required         */
     ATTN_ERR_HIP = 6,        /* a HIP launch failed (see attn_last_hip_error)      */
     ATTN_ERR_ALIAS = 7,      /* an output pointer equals an input pointer          */
-    ATTN_ERR_VALUE = 8       /* a scalar argument (e.g. the RoPE base) is invalid   */
+    ATTN_ERR_VALUE = 8,      /* a scalar argument (e.g. the RoPE base) is invalid   */
+    ATTN_ERR_SAVED = 9       /* the saved rotated q/k buffer is too small           */
 };
 
 /*
@@ -75,24 +77,57 @@ int attn_rope_tables(float* cos_tab, float* sin_tab, int T, int D, double base,
                      void* stream);
 
 /*
- * attn_fwd - forward pass. Reads the pre-RoPE q, k and v, rotates q and k on
- * load, and writes o = softmax(S) v and lse (natural log-sum-exp of each row's
- * scaled, masked scores; saved for the backward). FlashAttention-style: the
- * T x T score matrix is never stored ("Show HN: NanoEuler", paragraph 2).
+ * attn_saved_bytes - size of the "saved" buffer that attn_fwd fills and the
+ * backward reads: for ATTN_BF16 the RoPE-rotated q and k, each [B,H,T,D] fp16
+ * (4*B*H*T*D bytes, rounded up to 256); 0 for ATTN_F32, whose kernels rotate on
+ * load. Returns 0 for arguments the other calls would reject.
+ */
+size_t attn_saved_bytes(int B, int H, int T, int D, int dtype);
+
+/*
+ * attn_rotate_qk - apply RoPE once ("Tiny Hackable CUDA", section 3): writes
+ * R_t q_t then R_t k_t into `saved` ([2][B,H,T,D] fp16), each value rotated in
+ * fp32 and rounded once to fp16. The rotated q and k are no longer bf16 values;
+ * fp16's 11-bit significand keeps the score products accurate where the
+ * softmax is sharp, and bounds |rotated q|, |rotated k| by 65504.
+ * For ATTN_F32 it does nothing and returns ATTN_OK.
+ */
+int attn_rotate_qk(const void* q, const void* k, const float* cos_tab, const float* sin_tab,
+                   void* saved, size_t saved_bytes, int B, int H, int T, int D, int dtype,
+                   void* stream);
+
+/*
+ * attn_fwd - forward pass. Reads the pre-RoPE q, k and v, and writes
+ * o = softmax(S) v and lse (natural log-sum-exp of each row's scaled, masked
+ * scores; saved for the backward). FlashAttention-style: the T x T score
+ * matrix is never stored ("Show HN: NanoEuler", paragraph 2).
  *   q, k, v   [B,H,T,D] dtype, inputs
  *   cos_tab, sin_tab  [T,D/2] fp32 from attn_rope_tables (or equal values)
  *   o         [B,H,T,D] dtype, output
  *   lse       [B,H,T] fp32, output
+ *   saved     ATTN_BF16: device buffer of attn_saved_bytes(); receives the
+ *             rotated q and k (attn_rotate_qk) and must be handed to the
+ *             backward. ATTN_F32: ignored, may be NULL.
+ * ATTN_BF16 enqueues attn_rotate_qk then attn_fwd_rotated.
  */
 int attn_fwd(const void* q, const void* k, const void* v,
              const float* cos_tab, const float* sin_tab,
-             void* o, float* lse,
+             void* o, float* lse, void* saved, size_t saved_bytes,
              int B, int H, int T, int D, int dtype, void* stream);
 
 /*
- * attn_bwd_workspace_bytes - device workspace attn_bwd needs: the per-row
- * delta_t = sum_d dO[t,d] o[t,d] in fp32, 4*B*H*T bytes rounded up to 256.
- * Returns 0 for arguments attn_bwd would reject.
+ * attn_fwd_rotated - the forward kernel alone (ATTN_BF16 only; ATTN_F32 gets
+ * ATTN_ERR_DTYPE): o and lse from the rotated q and k already in `saved`
+ * (attn_rotate_qk) and from v.
+ */
+int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void* o, float* lse,
+                     int B, int H, int T, int D, int dtype, void* stream);
+
+/*
+ * attn_bwd_workspace_bytes - device workspace the backward needs: per row
+ * (lse_t * log2 e, delta_t) as two fp32 for ATTN_BF16 (8*B*H*T bytes), or
+ * delta_t alone for ATTN_F32 (4*B*H*T bytes), rounded up to 256, where
+ * delta_t = sum_d dO[t,d] o[t,d]. Returns 0 for arguments attn_bwd would reject.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype);
 
@@ -102,37 +137,46 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype);
  * analytic gradient, RoPE's included, is checked against centred differences).
  * Recompute-based: P is rebuilt from q, k and lse; nothing of size T x T is
  * stored. Runs attn_bwd_dq then attn_bwd_dkdv on `stream`.
- *   q, k, v, o, dO  [B,H,T,D] dtype, inputs (o and lse from attn_fwd)
+ *   q, k, v, o, dO  [B,H,T,D] dtype, inputs (o and lse from attn_fwd); the
+ *                   ATTN_BF16 kernels take the rotated q and k from `saved`
  *   lse             [B,H,T] fp32, input
+ *   saved           ATTN_BF16: the buffer attn_fwd filled for these q and k
+ *                   (or attn_rotate_qk); ATTN_F32: ignored, may be NULL
  *   dq, dk, dv      [B,H,T,D] dtype, outputs (overwritten)
  *   workspace       device buffer of at least attn_bwd_workspace_bytes()
+ * ATTN_BF16 rounds dS = P (dP - delta) to fp16 for the dq/dk products, so
+ * |dS| must stay below 65504 (true whenever |dO_t|*|v_u| < 32752 in L2 norm).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const void* dO, const float* lse,
              const float* cos_tab, const float* sin_tab,
+             const void* saved, size_t saved_bytes,
              void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes,
              int B, int H, int T, int D, int dtype, void* stream);
 
 /*
- * attn_bwd_dq - first stage of attn_bwd: writes delta_t = sum_d dO[t,d] o[t,d]
- * into the workspace and dq (gradient w.r.t. the pre-RoPE q) into dq.
- * Same arguments and rules as attn_bwd, minus dk and dv.
+ * attn_bwd_dq - first stage of attn_bwd: writes the per-row workspace entries
+ * (delta_t = sum_d dO[t,d] o[t,d], and for ATTN_BF16 lse_t * log2 e) and dq
+ * (gradient w.r.t. the pre-RoPE q). Same arguments and rules as attn_bwd,
+ * minus dk and dv.
  */
 int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
                 const void* dO, const float* lse,
                 const float* cos_tab, const float* sin_tab,
+                const void* saved, size_t saved_bytes,
                 void* dq, void* workspace, size_t workspace_bytes,
                 int B, int H, int T, int D, int dtype, void* stream);
 
 /*
  * attn_bwd_dkdv - second stage of attn_bwd: writes dk (w.r.t. the pre-RoPE k)
- * and dv. Reads delta from the workspace, so attn_bwd_dq must have been
+ * and dv. Reads the workspace entries of attn_bwd_dq, which must have been
  * enqueued before it on the same stream (or completed) with the same inputs.
  */
 int attn_bwd_dkdv(const void* q, const void* k, const void* v,
                   const void* dO, const float* lse,
                   const float* cos_tab, const float* sin_tab,
+                  const void* saved, size_t saved_bytes,
                   void* dk, void* dv, const void* workspace, size_t workspace_bytes,
                   int B, int H, int T, int D, int dtype, void* stream);
 

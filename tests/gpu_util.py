@@ -17,8 +17,8 @@ def gpu_run(x, base=10000.0):
     """x: dict of CPU tensors q, k, v, do. Returns dict of CPU tensors o, lse, dq, dk, dv."""
     dev = torch.device("cuda", 0)
     g = {n: t.to(dev) for n, t in x.items()}
-    o, lse = attn.forward(g["q"], g["k"], g["v"], base=base)
-    dq, dk, dv = attn.backward(g["q"], g["k"], g["v"], o, g["do"], lse, base=base)
+    o, lse, saved = attn.forward(g["q"], g["k"], g["v"], base=base)
+    dq, dk, dv = attn.backward(g["q"], g["k"], g["v"], o, g["do"], lse, saved, base=base)
     torch.cuda.synchronize()
     return {n: t.cpu() for n, t in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv).items()}
 

@@ -35,8 +35,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_rope_tables",
-              "attn_bwd_workspace_bytes", "attn_status_string", "attn_last_hip_error"):
+    for n in ("attn_fwd", "attn_fwd_rotated", "attn_rotate_qk", "attn_saved_bytes", "attn_bwd",
+              "attn_bwd_dq", "attn_bwd_dkdv", "attn_rope_tables", "attn_bwd_workspace_bytes",
+              "attn_status_string", "attn_last_hip_error"):
         assert n in names
 
 
@@ -48,15 +49,19 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         assert attn.attn_status_string(code) != "unknown status"
     assert attn.attn_status_string(99) == "unknown status"
     assert attn.attn_last_hip_error() == 0
 
 
 def test_workspace_size(lib):
-    assert attn.attn_bwd_workspace_bytes(8, 12, 1024, 64, 0) == 4 * 8 * 12 * 1024
+    assert attn.attn_bwd_workspace_bytes(8, 12, 1024, 64, 0) == 8 * 8 * 12 * 1024
+    assert attn.attn_bwd_workspace_bytes(8, 12, 1024, 64, 1) == 4 * 8 * 12 * 1024
     assert attn.attn_bwd_workspace_bytes(1, 1, 3, 64, 0) == 256
+    assert attn.attn_saved_bytes(8, 12, 1024, 64, 0) == 4 * 8 * 12 * 1024 * 64
+    assert attn.attn_saved_bytes(8, 12, 1024, 64, 1) == 0
+    assert attn.attn_saved_bytes(1, 1, 3, 96, 0) == 0
     assert attn.attn_bwd_workspace_bytes(1, 1, 3, 96, 0) == 0
     assert attn.attn_bwd_workspace_bytes(1, 1, 0, 64, 0) == 0
     assert attn.attn_bwd_workspace_bytes(1, 1, 3, 64, 7) == 0
@@ -70,7 +75,8 @@ def status_of(fn, *args):
 
 def fwd_args(**over):
     a = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, cos_tab=FAKE + 48, sin_tab=FAKE + 64,
-             o=FAKE + 80, lse=FAKE + 96, B=1, H=1, T=8, D=64, dtype=0, stream=0)
+             o=FAKE + 80, lse=FAKE + 96, saved=FAKE + 112, saved_bytes=4 * 8 * 64,
+             B=1, H=1, T=8, D=64, dtype=0, stream=0)
     a.update(over)
     return a
 
@@ -88,13 +94,34 @@ def test_fwd_rejects_bad_arguments(lib):
     assert f(k=MIS) == 4
     assert f(o=FAKE) == 7                                 # o aliases q
     assert f(lse=FAKE + 32) == 7                          # lse aliases v
+    assert f(saved=0) == 1                                # bf16 needs the saved buffer
+    assert f(saved=MIS) == 4
+    assert f(saved_bytes=4 * 8 * 64 - 1) == 9
+    assert f(saved=FAKE + 16) == 7                        # saved aliases k
+
+
+def test_fwd_rotated_and_rotate_reject_bad_arguments(lib):
+    f = lambda **o: status_of(lambda: attn.attn_fwd_rotated(
+        **{**dict(saved=FAKE, saved_bytes=4 * 8 * 64, v=FAKE + 16, o=FAKE + 32, lse=FAKE + 48,
+                  B=1, H=1, T=8, D=64, dtype=0, stream=0), **o}))
+    assert f(dtype=1) == 3                                # fp32 has no rotated path
+    assert f(saved=0) == 1
+    assert f(saved_bytes=100) == 9
+    assert f(o=FAKE) == 7
+    g = lambda **o: status_of(lambda: attn.attn_rotate_qk(
+        **{**dict(q=FAKE, k=FAKE + 16, cos_tab=FAKE + 32, sin_tab=FAKE + 48, saved=FAKE + 64,
+                  saved_bytes=4 * 8 * 64, B=1, H=1, T=8, D=64, dtype=0, stream=0), **o}))
+    assert g(q=0) == 1
+    assert g(saved_bytes=0) == 9
+    assert g(saved=FAKE) == 7
+    assert g(D=48) == 2
 
 
 def test_bwd_rejects_bad_arguments(lib):
     base = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, o=FAKE + 48, dO=FAKE + 64, lse=FAKE + 80,
-                cos_tab=FAKE + 96, sin_tab=FAKE + 112, dq=FAKE + 128, dk=FAKE + 144,
-                dv=FAKE + 160, workspace=FAKE + 176, workspace_bytes=256, B=1, H=1, T=8,
-                D=64, dtype=0, stream=0)
+                cos_tab=FAKE + 96, sin_tab=FAKE + 112, saved=FAKE + 192, saved_bytes=4 * 8 * 64,
+                dq=FAKE + 128, dk=FAKE + 144, dv=FAKE + 160, workspace=FAKE + 176,
+                workspace_bytes=256, B=1, H=1, T=8, D=64, dtype=0, stream=0)
     f = lambda **o: status_of(lambda: attn.attn_bwd(**{**base, **o}))
     assert f(dO=0) == 1
     assert f(D=100) == 2
@@ -105,6 +132,9 @@ def test_bwd_rejects_bad_arguments(lib):
     assert f(dk=FAKE) == 7
     assert f(dv=FAKE + 144) == 7                          # dv aliases dk
     assert f(workspace=FAKE + 80) == 7                    # workspace aliases lse
+    assert f(saved=0) == 1
+    assert f(saved_bytes=8) == 9
+    assert f(dq=FAKE + 192) == 7                          # dq aliases saved
 
 
 def test_rope_tables_reject_bad_arguments(lib):

@@ -137,10 +137,14 @@ def test_abi_errors_on_gpu():
     cs, sn = attn.rope_tables(8, 64, 10000.0, "cuda:0")
     o = torch.empty_like(q)
     lse = torch.empty((1, 1, 8), dtype=torch.float32, device="cuda")
+    ns = attn.attn_saved_bytes(1, 1, 8, 64, attn.ATTN_BF16)
+    saved = torch.empty(ns, dtype=torch.uint8, device="cuda")
     with pytest.raises(attn.AttnError):
-        attn.attn_fwd(q, q, q, cs, sn, o, lse, 1, 1, 8, 96, attn.ATTN_BF16)
+        attn.attn_fwd(q, q, q, cs, sn, o, lse, saved, ns, 1, 1, 8, 96, attn.ATTN_BF16)
     with pytest.raises(attn.AttnError):
-        attn.attn_fwd(q, q, q, cs, sn, q, lse, 1, 1, 8, 64, attn.ATTN_BF16)
-    attn.attn_fwd(q, q, q, cs, sn, o, lse, 1, 1, 8, 64, attn.ATTN_BF16)
+        attn.attn_fwd(q, q, q, cs, sn, q, lse, saved, ns, 1, 1, 8, 64, attn.ATTN_BF16)
+    with pytest.raises(attn.AttnError):
+        attn.attn_fwd(q, q, q, cs, sn, o, lse, saved, ns - 256, 1, 1, 8, 64, attn.ATTN_BF16)
+    attn.attn_fwd(q, q, q, cs, sn, o, lse, saved, ns, 1, 1, 8, 64, attn.ATTN_BF16)
     torch.cuda.synchronize()
     assert torch.all(o == 0)
