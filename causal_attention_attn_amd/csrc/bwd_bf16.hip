@@ -48,21 +48,24 @@ struct BwdTile {
 // reach this wave's diagonal (32-key blocks above it skipped, the diagonal one masked).
 template <int D, bool DIAG>
 __device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const bf16x8* df,
-                                        const char* ks, const char* vs, int k0, int wq0,
-                                        int lane, float sc, float lt, float dl) {
+                                        const char* ks, const char* vs, const OperandOffs<D>& of,
+                                        int k0, int wq0, int lane, float sc, float lt, float dl) {
     using C = BwdTile<D>;
+    constexpr int ROWB = 2 * D;
     const int c32 = lane & 31, hf = lane >> 5;
+    if (DIAG && k0 > wq0) return;
 #pragma unroll
     for (int sb = 0; sb < C::KN / 32; ++sb) {
         const int kb = k0 + 32 * sb;
         if (DIAG && kb > wq0) break;
-        const int row = 32 * sb + c32;
-        f32x16 s = mfma32(lds_row8<D, f16x8>(ks, row, 8 * hf), qf[0], f32x16{});
-        f32x16 dp = mfma32(lds_row8<D, bf16x8>(vs, row, 8 * hf), df[0], f32x16{});
+        const char* kr = ks + 32 * sb * ROWB;
+        const char* vr = vs + 32 * sb * ROWB;
+        f32x16 s = mfma32(*reinterpret_cast<const f16x8*>(kr + of.k[0]), qf[0], f32x16{});
+        f32x16 dp = mfma32(*reinterpret_cast<const bf16x8*>(vr + of.k[0]), df[0], f32x16{});
 #pragma unroll
         for (int c = 1; c < C::DK; ++c) {
-            s = mfma32(lds_row8<D, f16x8>(ks, row, 16 * c + 8 * hf), qf[c], s);
-            dp = mfma32(lds_row8<D, bf16x8>(vs, row, 16 * c + 8 * hf), df[c], dp);
+            s = mfma32(*reinterpret_cast<const f16x8*>(kr + of.k[c]), qf[c], s);
+            dp = mfma32(*reinterpret_cast<const bf16x8*>(vr + of.k[c]), df[c], dp);
         }
         if (DIAG && kb == wq0) {
 #pragma unroll
@@ -85,10 +88,31 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const bf16
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[b] = mfma32(lds_tr8<D, f16x8>(ks, 32 * sb + 16 * j, 32 * b, lane), dsb[j], acc[b]);
+            for (int j = 0; j < 2; ++j) {
+                const char* t = ks + (32 * sb + 16 * j) * ROWB;
+                acc[b] = mfma32(tr_pair<f16x8>(t + of.v[b][0], t + of.v[b][1]), dsb[j], acc[b]);
+            }
         }
     }
+}
+
+// Step n of the dq kernel's key-tile loop on ring stage STG (= n % NS).
+template <int D, int STG, bool DIAG>
+__device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const bf16x8* df,
+                                        char (*smem)[2 * BwdTile<D>::TILE],
+                                        const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
+                                        const f16* kr, const bf16* v, int T, int n, int wq0,
+                                        int lane, int wave, float sc, float lt, float dl) {
+    using C = BwdTile<D>;
+    constexpr int NS = C::NS;
+    constexpr int NXT = (STG + NS - 1) % NS;
+    wait_vmcnt<C::LPT * (NS - 2)>();
+    __syncthreads();
+    const int nx = n + NS - 1;
+    ld.issue(kr, T, nx * C::KN, smem[NXT], wave);
+    ld.issue(v, T, nx * C::KN, smem[NXT] + C::TILE, wave);
+    dq_tile<D, DIAG>(acc, qf, df, smem[STG], smem[STG] + C::TILE, of, n * C::KN, wq0, lane, sc,
+                     lt, dl);
 }
 
 template <int D>
@@ -110,11 +134,23 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
     const int c32 = lane & 31, hf = lane >> 5;
     const size_t hoff = (size_t)bh * T * D;
     const uint32_t hbytes = (uint32_t)T * D * 2;
-    const rsrc_t qh = make_rsrc(qr + hoff, hbytes), kh = make_rsrc(kr + hoff, hbytes),
-                 vh = make_rsrc(v + hoff, hbytes), gh = make_rsrc(dO + hoff, hbytes),
-                 oh = make_rsrc(o + hoff, hbytes);
+    const f16* kh = kr + hoff;
+    const bf16* vh = v + hoff;
+    const rsrc_t qbuf = make_rsrc(qr + hoff, hbytes), gbuf = make_rsrc(dO + hoff, hbytes),
+                 obuf = make_rsrc(o + hoff, hbytes);
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
+    const TileLoads<D, 64, 4> ld(wave, lane);
+    const OperandOffs<D> of(lane);
+
+    const int kend = min(T, q0 + C::QM);
+    const int ntiles = (kend + C::KN - 1) / C::KN;
+    const int nfull = min(ntiles, q0 / C::KN);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) {
+        ld.issue(kh, T, s * C::KN, smem[s], wave);
+        ld.issue(vh, T, s * C::KN, smem[s] + C::TILE, wave);
+    }
 
     // this lane's query: rotated q (fp16), dO (bf16), and delta = sum_d dO o
     f16x8 qf[C::DK];
@@ -123,9 +159,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) {
         const uint32_t off = (uint32_t)(tq * D + 16 * c + 8 * hf) * 2;
-        qf[c] = __builtin_bit_cast(f16x8, buf_load16(qh, off));
-        const u32x4 g = buf_load16(gh, off);
-        const u32x4 y = buf_load16(oh, off);
+        qf[c] = __builtin_bit_cast(f16x8, buf_load16(qbuf, off));
+        const u32x4 g = buf_load16(gbuf, off);
+        const u32x4 y = buf_load16(obuf, off);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             dot += bf16_lo(g[e]) * bf16_lo(y[e]) + bf16_hi(g[e]) * bf16_hi(y[e]);
@@ -135,32 +171,25 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
     const float lt = tq < T ? lse[(size_t)bh * T + tq] * kLog2e : 0.f;
     if (tq < T && hf == 0) *reinterpret_cast<f32x2*>(ws + 2 * ((size_t)bh * T + tq)) = f32x2{lt, dl};
 
-    const int kend = min(T, q0 + C::QM);
-    const int ntiles = (kend + C::KN - 1) / C::KN;
-    const int nfull = min(ntiles, q0 / C::KN);
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s) {
-        issue_tile<D, C::KN, C::NW>(kh, s * C::KN, smem[s], wave, lane);
-        issue_tile<D, C::KN, C::NW>(vh, s * C::KN, smem[s] + C::TILE, wave, lane);
-    }
-
     f32x16 acc[C::DB];
 #pragma unroll
     for (int b = 0; b < C::DB; ++b) acc[b] = f32x16{};
 
-    for (int n = 0; n < ntiles; ++n) {
-        wait_vmcnt<C::LPT * (NS - 2)>();
-        __syncthreads();
-        const int nx = n + NS - 1;
-        issue_tile<D, C::KN, C::NW>(kh, nx * C::KN, smem[nx % NS], wave, lane);
-        issue_tile<D, C::KN, C::NW>(vh, nx * C::KN, smem[nx % NS] + C::TILE, wave, lane);
-        const char* ks = smem[n % NS];
-        const char* vs = ks + C::TILE;
-        const int k0 = n * C::KN;
-        if (n < nfull)
-            dq_tile<D, false>(acc, qf, df, ks, vs, k0, wq0, lane, sc, lt, dl);
-        else if (k0 <= wq0)
-            dq_tile<D, true>(acc, qf, df, ks, vs, k0, wq0, lane, sc, lt, dl);
+    int n = 0;
+    for (; n + NS <= nfull; n += NS) {
+        dq_step<D, 0, false>(acc, qf, df, smem, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
+        dq_step<D, 1, false>(acc, qf, df, smem, ld, of, kh, vh, T, n + 1, wq0, lane, wave, sc, lt, dl);
+        if constexpr (NS > 2)
+            dq_step<D, 2, false>(acc, qf, df, smem, ld, of, kh, vh, T, n + 2, wq0, lane, wave, sc, lt, dl);
+    }
+    for (; n < ntiles; ++n) {
+        const int stg = n % NS;
+        if (stg == 0)
+            dq_step<D, 0, true>(acc, qf, df, smem, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
+        else if (stg == 1)
+            dq_step<D, 1, true>(acc, qf, df, smem, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
+        else if constexpr (NS > 2)
+            dq_step<D, 2, true>(acc, qf, df, smem, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
     }
     wait_vmcnt<0>();
 
@@ -195,21 +224,24 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
 template <int D, bool DIAG>
 __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8* kf,
                                           const bf16x8* vf, const char* qs, const char* gs,
-                                          const float* ld, int qbase, int wk0, int lane,
-                                          float sc) {
+                                          const float* ld, const OperandOffs<D>& of, int qbase,
+                                          int wk0, int lane, float sc) {
     using C = BwdTile<D>;
+    constexpr int ROWB = 2 * D;
     const int c32 = lane & 31, hf = lane >> 5;
+    if (DIAG && qbase + C::QN - 1 < wk0) return;
 #pragma unroll
     for (int sb = 0; sb < C::QN / 32; ++sb) {
         const int qb = qbase + 32 * sb;
         if (DIAG && qb + 31 < wk0) continue;
-        const int row = 32 * sb + c32;
-        f32x16 s = mfma32(lds_row8<D, f16x8>(qs, row, 8 * hf), kf[0], f32x16{});
-        f32x16 dp = mfma32(lds_row8<D, bf16x8>(gs, row, 8 * hf), vf[0], f32x16{});
+        const char* qr = qs + 32 * sb * ROWB;
+        const char* gr = gs + 32 * sb * ROWB;
+        f32x16 s = mfma32(*reinterpret_cast<const f16x8*>(qr + of.k[0]), kf[0], f32x16{});
+        f32x16 dp = mfma32(*reinterpret_cast<const bf16x8*>(gr + of.k[0]), vf[0], f32x16{});
 #pragma unroll
         for (int c = 1; c < C::DK; ++c) {
-            s = mfma32(lds_row8<D, f16x8>(qs, row, 16 * c + 8 * hf), kf[c], s);
-            dp = mfma32(lds_row8<D, bf16x8>(gs, row, 16 * c + 8 * hf), vf[c], dp);
+            s = mfma32(*reinterpret_cast<const f16x8*>(qr + of.k[c]), kf[c], s);
+            dp = mfma32(*reinterpret_cast<const bf16x8*>(gr + of.k[c]), vf[c], dp);
         }
         if (DIAG && qb == wk0) {
 #pragma unroll
@@ -244,11 +276,52 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8*
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                dva[b] = mfma32(lds_tr8<D, bf16x8>(gs, 32 * sb + 16 * j, 32 * b, lane), pb[j], dva[b]);
-                dka[b] = mfma32(lds_tr8<D, f16x8>(qs, 32 * sb + 16 * j, 32 * b, lane), dsb[j], dka[b]);
+                const char* gt = gs + (32 * sb + 16 * j) * ROWB;
+                const char* qt = qs + (32 * sb + 16 * j) * ROWB;
+                dva[b] = mfma32(tr_pair<bf16x8>(gt + of.v[b][0], gt + of.v[b][1]), pb[j], dva[b]);
+                dka[b] = mfma32(tr_pair<f16x8>(qt + of.v[b][0], qt + of.v[b][1]), dsb[j], dka[b]);
             }
         }
     }
+}
+
+template <int D>
+struct DkdvCtx {
+    const f16* qh;
+    const bf16* gh;
+    const float* lh;  // (lse*log2 e, delta) pairs of this head's rows
+    int T, wk0, lane, wave;
+    float sc;
+
+    // query tile qt -> LDS stage st: rotated Q and dO tiles, then the
+    // (lse*log2 e, delta) pairs of its 64 queries (each wave fetches 16 pairs)
+    __device__ __forceinline__ void issue(const TileLoads<D, 64, 4>& ld, int qt, char* st) const {
+        constexpr int QN = BwdTile<D>::QN, TILE = BwdTile<D>::TILE;
+        ld.issue(qh, T, qt * QN, st, wave);
+        ld.issue(gh, T, qt * QN, st + TILE, wave);
+        if (lane < 32)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                make_rsrc(lh, (uint32_t)T * 8), LDS_PTR(st + 2 * TILE + 128 * wave), 4,
+                (uint32_t)((qt * QN + 16 * wave) * 8 + 4 * lane), 0, 0, 0);
+    }
+};
+
+// Step of the dk/dv kernel's query-tile loop on ring stage STG.
+template <int D, int STG, bool DIAG>
+__device__ __forceinline__ void dkdv_step(f32x16* dva, f32x16* dka, const f16x8* kf,
+                                          const bf16x8* vf, char (*smem)[2 * BwdTile<D>::TILE + 512],
+                                          const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
+                                          const DkdvCtx<D>& x, int qt) {
+    using C = BwdTile<D>;
+    constexpr int NS = C::NS;
+    constexpr int NXT = (STG + NS - 1) % NS;
+    wait_vmcnt<(C::LPT + 1) * (NS - 2)>();
+    __syncthreads();
+    x.issue(ld, qt + NS - 1, smem[NXT]);
+    const char* qs = smem[STG];
+    dkdv_tile<D, DIAG>(dva, dka, kf, vf, qs, qs + C::TILE,
+                       reinterpret_cast<const float*>(qs + 2 * C::TILE), of, qt * C::QN, x.wk0,
+                       x.lane, x.sc);
 }
 
 template <int D>
@@ -259,8 +332,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
     int nkb, float sc, float scale) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
-    constexpr int STAGE = 2 * C::TILE + 512;  // Q tile, dO tile, 64 x (lse*log2 e, delta)
-    __shared__ __attribute__((aligned(1024))) char smem[NS][STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[NS][2 * C::TILE + 512];
 
     const int bid = blockIdx.x;
     const int bh = bid % BH;
@@ -271,53 +343,55 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
     const int c32 = lane & 31, hf = lane >> 5;
     const size_t hoff = (size_t)bh * T * D;
     const uint32_t hbytes = (uint32_t)T * D * 2;
-    const rsrc_t qh = make_rsrc(qr + hoff, hbytes), kh = make_rsrc(kr + hoff, hbytes),
-                 vh = make_rsrc(v + hoff, hbytes), gh = make_rsrc(dO + hoff, hbytes),
-                 lh = make_rsrc(ws + 2 * (size_t)bh * T, (uint32_t)T * 8);
     const int wk0 = k0 + wave * 32;
     const int tk = wk0 + c32;
+    const DkdvCtx<D> x = {qr + hoff, dO + hoff, ws + 2 * (size_t)bh * T, T, wk0, lane, wave, sc};
+    const TileLoads<D, 64, 4> ld(wave, lane);
+    const OperandOffs<D> of(lane);
 
     const int qt0 = k0 / C::QN;
     const int nqt = (T + C::QN - 1) / C::QN;
     const int qfull = min(nqt, (k0 + C::KM) / C::QN);  // from here on no query precedes a key
-    // one tile = Q, dO (row-major) and the (lse*log2 e, delta) pairs of its 64
-    // queries; each wave fetches 16 of those pairs with one dword load
-    auto issue = [&](int qt, char* st) {
-        issue_tile<D, C::QN, C::NW>(qh, qt * C::QN, st, wave, lane);
-        issue_tile<D, C::QN, C::NW>(gh, qt * C::QN, st + C::TILE, wave, lane);
-        if (lane < 32)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                lh, LDS_PTR(st + 2 * C::TILE + 128 * wave), 4,
-                (uint32_t)((qt * C::QN + 16 * wave) * 8 + 4 * lane), 0, 0, 0);
-    };
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(qt0 + s, smem[s]);
+    for (int s = 0; s < NS - 1; ++s) x.issue(ld, qt0 + s, smem[s]);
 
+    const rsrc_t kbuf = make_rsrc(kr + hoff, hbytes), vbuf = make_rsrc(v + hoff, hbytes);
     f16x8 kf[C::DK];
     bf16x8 vf[C::DK];
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) {
         const uint32_t off = (uint32_t)(tk * D + 16 * c + 8 * hf) * 2;
-        kf[c] = __builtin_bit_cast(f16x8, buf_load16(kh, off));
-        vf[c] = as_bf16x8(buf_load16(vh, off));
+        kf[c] = __builtin_bit_cast(f16x8, buf_load16(kbuf, off));
+        vf[c] = as_bf16x8(buf_load16(vbuf, off));
     }
     f32x16 dva[C::DB], dka[C::DB];
 #pragma unroll
     for (int b = 0; b < C::DB; ++b) dva[b] = dka[b] = f32x16{};
 
-    for (int qt = qt0; qt < nqt; ++qt) {
-        const int it = qt - qt0;
-        wait_vmcnt<(C::LPT + 1) * (NS - 2)>();
-        __syncthreads();
-        issue(qt + NS - 1, smem[(it + NS - 1) % NS]);
-        const char* qs = smem[it % NS];
-        const char* gs = qs + C::TILE;
-        const float* ld = reinterpret_cast<const float*>(qs + 2 * C::TILE);
-        const int qbase = qt * C::QN;
-        if (qt >= qfull)
-            dkdv_tile<D, false>(dva, dka, kf, vf, qs, gs, ld, qbase, wk0, lane, sc);
-        else if (qbase + C::QN - 1 >= wk0)
-            dkdv_tile<D, true>(dva, dka, kf, vf, qs, gs, ld, qbase, wk0, lane, sc);
+    // ring stage of query tile qt is (qt - qt0) % NS; the diagonal tiles come first
+    int qt = qt0;
+    for (; qt < min(qfull, nqt); ++qt) {
+        const int stg = (qt - qt0) % NS;
+        if (stg == 0) dkdv_step<D, 0, true>(dva, dka, kf, vf, smem, ld, of, x, qt);
+        else if (stg == 1) dkdv_step<D, 1, true>(dva, dka, kf, vf, smem, ld, of, x, qt);
+        else if constexpr (NS > 2) dkdv_step<D, 2, true>(dva, dka, kf, vf, smem, ld, of, x, qt);
+    }
+    // the full tiles, rotated so that the unrolled body starts on stage 0
+    for (; qt < nqt && (qt - qt0) % NS != 0; ++qt) {
+        const int stg = (qt - qt0) % NS;
+        if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
+        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
+    }
+    for (; qt + NS <= nqt; qt += NS) {
+        dkdv_step<D, 0, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
+        dkdv_step<D, 1, false>(dva, dka, kf, vf, smem, ld, of, x, qt + 1);
+        if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, smem, ld, of, x, qt + 2);
+    }
+    for (; qt < nqt; ++qt) {
+        const int stg = (qt - qt0) % NS;
+        if (stg == 0) dkdv_step<D, 0, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
+        else if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
+        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
     }
     wait_vmcnt<0>();
 

@@ -235,34 +235,59 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-// swizzled 16-byte chunk position of chunk c in tile row r
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
+// Swizzled 16-byte chunk position of chunk c in row r of a tile with D-element
+// (2*D-byte) rows. LDS serves 256 bytes per cycle: 16 lanes of a 16-byte read,
+// 32 lanes of an 8-byte read. The XOR pattern keeps both operand reads
+// conflict-free: the row-operand read (16 consecutive rows, same chunk) and the
+// transpose read (rows R..R+3, four consecutive chunks; R a multiple of 4).
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+    if constexpr (D == 64)
+        return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    else
+        return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+}
 
 // Byte offset inside a tile of element (r, col) (col a multiple of 4).
 template <int D>
 __device__ __forceinline__ int tile_off(int r, int col) {
-    return r * (D * 2) + 16 * swz(r, col >> 3) + 2 * (col & 7);
+    return r * (D * 2) + 16 * swz<D>(r, col >> 3) + 2 * (col & 7);
 }
 
-// Issue the loads of one ROWS x D tile (rows r0 .. r0+ROWS-1 of a [T, D] head
-// held by buffer `src`) into LDS at `tile`. NW waves share the work; every wave
-// issues exactly ROWS * D / (64 * 8 * NW) instructions.
+// Per-lane voffsets of the loads that fill one ROWS x D tile: NW waves share
+// the tile, each issuing IPW 1 KB instructions; instruction i of this wave
+// fills LDS bytes [1024 (wave IPW + i), +1024) of the tile and takes its
+// global chunk at voff[i] from the tile's first row. Each tile gets its own
+// buffer resource starting at that row and ending at row T, so rows past the
+// end of the sequence read as zeros (the range check covers the per-lane
+// offset, not a scalar one).
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void issue_tile(rsrc_t src, int r0, char* tile, int wave, int lane) {
-    constexpr int NC = D / 8;                       // 16-byte chunks per row
-    constexpr int INSTR = ROWS * NC / 64;           // 1 KB instructions per tile
+struct TileLoads {
+    static constexpr int NC = D / 8;                 // 16-byte chunks per row
+    static constexpr int INSTR = ROWS * NC / 64;     // 1 KB instructions per tile
     static_assert(INSTR % NW == 0, "tile instructions must divide among waves");
-    constexpr int IPW = INSTR / NW;
+    static constexpr int IPW = INSTR / NW;
+    uint32_t voff[IPW];
+    __device__ __forceinline__ TileLoads(int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int blk = wave * IPW + i;
-        const int p = blk * 64 + lane;              // LDS chunk index
-        const int r = p / NC, pos = p % NC;
-        const int c = swz(r, pos) & (NC - 1);       // global chunk stored at this position
-        const uint32_t voff = (uint32_t)((r0 + r) * D + 8 * c) * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, LDS_PTR(tile + blk * 1024), 16, voff, 0, 0, 0);
+        for (int i = 0; i < IPW; ++i) {
+            const int p = (wave * IPW + i) * 64 + lane;  // LDS chunk index
+            const int r = p / NC, pos = p % NC;
+            voff[i] = (uint32_t)(r * D + 8 * swz<D>(r, pos)) * 2;
+        }
     }
-}
+    // rows r0 .. r0+ROWS-1 of a [T, D] 16-bit head -> LDS `tile`
+    __device__ __forceinline__ void issue(const void* head, int T, int r0, char* tile,
+                                          int wave) const {
+        const int rows = T > r0 ? T - r0 : 0;
+        const rsrc_t src = make_rsrc(static_cast<const char*>(head) + (size_t)r0 * D * 2,
+                                     (uint32_t)rows * D * 2);
+#pragma unroll
+        for (int i = 0; i < IPW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src, LDS_PTR(tile + (wave * IPW + i) * 1024),
+                                                     16, voff[i], 0, 0, 0);
+    }
+};
 
 // 8 consecutive 16-bit values of row r starting at column col (a multiple of 8).
 template <int D, typename V>
@@ -288,6 +313,41 @@ __device__ __forceinline__ V lds_tr8(const char* tile, int row0, int col0, int l
         (__attribute__((address_space(3))) s16x4*)(tile + tile_off<D>(row + 8, col)));
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     const s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(V, r);
+}
+
+// Byte offsets, inside a tile, of this lane's operand reads (see tile_off):
+// k[c]     the row operand (A of a 32x32x16 MFMA contracting over the head
+//          dimension) for head-dimension chunk c, row = lane & 31;
+// v[b][h]  the two transpose reads of an X^T operand (A of an MFMA contracting
+//          over tile rows) for head-dimension block b, see lds_tr8.
+// Moving 16 or 32 rows down a tile leaves the swizzle unchanged, so the other
+// 16-key chunks and 32-key sub-blocks are these offsets plus a constant.
+template <int D>
+struct OperandOffs {
+    int k[D / 16];
+    int v[D / 32][2];
+    __device__ __forceinline__ OperandOffs(int lane) {
+        const int c32 = lane & 31, hf = lane >> 5, g = lane >> 4, m = lane & 15;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) k[c] = tile_off<D>(c32, 16 * c + 8 * hf);
+        const int row = 4 * (g >> 1) + (m >> 2);
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) {
+            const int col = 32 * b + 16 * (g & 1) + 4 * (m & 3);
+            v[b][0] = tile_off<D>(row, col);
+            v[b][1] = tile_off<D>(row + 8, col);
+        }
+    }
+};
+
+template <typename V>
+__device__ __forceinline__ V tr_pair(const char* lo, const char* hi) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)lo);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)hi);
+    const s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     return __builtin_bit_cast(V, r);
 }
 

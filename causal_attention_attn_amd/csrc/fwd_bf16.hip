@@ -59,19 +59,22 @@ struct FwdState {
 // so 32-key sub-blocks above it are skipped and the diagonal one is masked.
 template <int D, bool DIAG>
 __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const f16x8* qf, const char* ks,
-                                         const char* vs, int k0, int wq0, int lane, float sc) {
+                                         const char* vs, const OperandOffs<D>& of, int k0, int wq0,
+                                         int lane, float sc) {
     using C = FwdTile<D>;
     constexpr float kRescale = 8.f;
+    constexpr int ROWB = 2 * D;  // bytes per tile row
     const int c32 = lane & 31, hf = lane >> 5;
+    if (DIAG && k0 > wq0) return;  // whole tile above this wave's diagonal
     f32x16 s[C::NSB];
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
         if (DIAG && k0 + 32 * sb > wq0) break;
-        const int row = 32 * sb + c32;
-        f32x16 acc = mfma32(lds_row8<D, f16x8>(ks, row, 8 * hf), qf[0], f32x16{});
+        const char* kb = ks + 32 * sb * ROWB;
+        f32x16 acc = mfma32(*reinterpret_cast<const f16x8*>(kb + of.k[0]), qf[0], f32x16{});
 #pragma unroll
         for (int c = 1; c < C::DK; ++c)
-            acc = mfma32(lds_row8<D, f16x8>(ks, row, 16 * c + 8 * hf), qf[c], acc);
+            acc = mfma32(*reinterpret_cast<const f16x8*>(kb + of.k[c]), qf[c], acc);
         s[sb] = acc;
     }
     float mx = -INFINITY;
@@ -117,11 +120,38 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const f16x8* qf, const
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                st.o[b] = mfma32(lds_tr8<D, bf16x8>(vs, 32 * sb + 16 * j, 32 * b, lane), pb[j],
-                                 st.o[b]);
+            for (int j = 0; j < 2; ++j) {
+                const char* vb = vs + (32 * sb + 16 * j) * ROWB;
+                st.o[b] = mfma32(tr_pair<bf16x8>(vb + of.v[b][0], vb + of.v[b][1]), pb[j], st.o[b]);
+            }
         }
     }
+}
+
+// Shared state of one workgroup's pass over its key tiles.
+template <int D>
+struct FwdCtx {
+    const f16* kr;
+    const bf16* v;
+    int T, wq0, lane, wave;
+    float sc;
+};
+
+// Step n of the tile loop on ring stage STG (= n % NS): wait for tile n,
+// publish it, refill the stage freed by tile n-1 with tile n+NS-1, compute.
+template <int D, int STG, bool DIAG>
+__device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, char (*smem)[2 * FwdTile<D>::TILE],
+                                         const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
+                                         const FwdCtx<D>& x, int n) {
+    using C = FwdTile<D>;
+    constexpr int NS = C::NS;
+    constexpr int NXT = (STG + NS - 1) % NS;
+    wait_vmcnt<C::LPT * (NS - 2)>();
+    __syncthreads();
+    const int nx = n + NS - 1;
+    ld.issue(x.kr, x.T, nx * C::BN, smem[NXT], x.wave);
+    ld.issue(x.v, x.T, nx * C::BN, smem[NXT] + C::TILE, x.wave);
+    fwd_tile<D, DIAG>(st, qf, smem[STG], smem[STG] + C::TILE, of, n * C::BN, x.wq0, x.lane, x.sc);
 }
 
 template <int D>
@@ -140,23 +170,24 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c32 = lane & 31, hf = lane >> 5;
     const size_t hoff = (size_t)bh * T * D;
-    const uint32_t hbytes = (uint32_t)T * D * 2;
-    const rsrc_t qh = make_rsrc(qr + hoff, hbytes), kh = make_rsrc(kr + hoff, hbytes),
-                 vh = make_rsrc(v + hoff, hbytes);
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
+    const FwdCtx<D> x = {kr + hoff, v + hoff, T, wq0, lane, wave, sc};
+    const TileLoads<D, 64, 4> ld(wave, lane);
+    const OperandOffs<D> of(lane);
 
     const int kend = min(T, q0 + C::BM);
     const int ntiles = (kend + C::BN - 1) / C::BN;
     const int nfull = min(ntiles, q0 / C::BN);  // tiles wholly below every query of the block
 
-    // prologue: tiles 0 .. NS-2 in flight (tiles past the end are harmless reads)
+    // prologue: tiles 0 .. NS-2 in flight (tiles past the end read as zeros)
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) {
-        issue_tile<D, C::BN, C::NW>(kh, s * C::BN, smem[s], wave, lane);
-        issue_tile<D, C::BN, C::NW>(vh, s * C::BN, smem[s] + C::TILE, wave, lane);
+        ld.issue(x.kr, T, s * C::BN, smem[s], wave);
+        ld.issue(x.v, T, s * C::BN, smem[s] + C::TILE, wave);
     }
 
+    const rsrc_t qh = make_rsrc(qr + hoff, (uint32_t)T * D * 2);
     f16x8 qf[C::DK];
 #pragma unroll
     for (int c = 0; c < C::DK; ++c)
@@ -168,22 +199,19 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     st.m = -INFINITY;
     st.l = 0.f;
 
-    for (int n = 0; n < ntiles; ++n) {
-        // this wave's loads of tile n are complete once at most NS-2 tiles'
-        // worth of its loads remain; the barrier publishes every wave's share
-        // and guarantees that stage (n-1) % NS is no longer read
-        wait_vmcnt<C::LPT * (NS - 2)>();
-        __syncthreads();
-        const int nx = n + NS - 1;
-        issue_tile<D, C::BN, C::NW>(kh, nx * C::BN, smem[nx % NS], wave, lane);
-        issue_tile<D, C::BN, C::NW>(vh, nx * C::BN, smem[nx % NS] + C::TILE, wave, lane);
-        const char* ks = smem[n % NS];
-        const char* vs = ks + C::TILE;
-        const int k0 = n * C::BN;
-        if (n < nfull)
-            fwd_tile<D, false>(st, qf, ks, vs, k0, wq0, lane, sc);
-        else if (k0 <= wq0)
-            fwd_tile<D, true>(st, qf, ks, vs, k0, wq0, lane, sc);
+    int n = 0;
+    // full tiles: branch-free bodies, ring stages as compile-time constants
+    for (; n + NS <= nfull; n += NS) {
+        fwd_step<D, 0, false>(st, qf, smem, ld, of, x, n);
+        fwd_step<D, 1, false>(st, qf, smem, ld, of, x, n + 1);
+        if constexpr (NS > 2) fwd_step<D, 2, false>(st, qf, smem, ld, of, x, n + 2);
+    }
+    // the rest (at most NS-1 full tiles, then the diagonal tiles)
+    for (; n < ntiles; ++n) {
+        const int stg = n % NS;
+        if (stg == 0) fwd_step<D, 0, true>(st, qf, smem, ld, of, x, n);
+        else if (stg == 1) fwd_step<D, 1, true>(st, qf, smem, ld, of, x, n);
+        else if constexpr (NS > 2) fwd_step<D, 2, true>(st, qf, smem, ld, of, x, n);
     }
     wait_vmcnt<0>();  // no LDS writes may land after this workgroup's LDS is released
 

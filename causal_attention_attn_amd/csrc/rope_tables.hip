@@ -34,39 +34,47 @@ hipError_t launch_rope_tables(float* cs, float* sn, int T, int D, double base, h
 
 // Rotate q and k once: out[0] = R q, out[1] = R k, both [B, H, T, D] fp16
 // (rounded once from the fp32 rotation). The bf16 kernels read these instead of
-// applying RoPE per tile. One thread per 8 consecutive features.
+// applying RoPE per tile. One thread per 8 consecutive features of one row,
+// for q and k together (one cos/sin read serves both).
+template <int D>
 __global__ __launch_bounds__(256) void rotate_qk_kernel(const bf16* __restrict__ q,
                                                         const bf16* __restrict__ k,
                                                         const float* __restrict__ cs,
                                                         const float* __restrict__ sn,
-                                                        f16* __restrict__ out, int T, int D,
-                                                        long chunks) {
-    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= 2 * chunks) return;
-    const int which = idx >= chunks;
-    const long c = which ? idx - chunks : idx;
-    const long e0 = 8 * c;
-    const int d0 = (int)(e0 % D);
-    const int t = (int)((e0 / D) % T);
-    const bf16* src = which ? k : q;
-    const u32x4 w = *reinterpret_cast<const u32x4*>(src + e0);
-    const f32x4 cv = *reinterpret_cast<const f32x4*>(cs + (size_t)t * (D / 2) + d0 / 2);
-    const f32x4 sv = *reinterpret_cast<const f32x4*>(sn + (size_t)t * (D / 2) + d0 / 2);
-    u32x4 r;
+                                                        f16* __restrict__ out, int T,
+                                                        int chunks) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= chunks) return;
+    constexpr int NC = D / 8;
+    const int c = idx % NC;
+    const int t = (idx / NC) % T;
+    const size_t e0 = (size_t)idx * 8;
+    const u32x4 wq = *reinterpret_cast<const u32x4*>(q + e0);
+    const u32x4 wk = *reinterpret_cast<const u32x4*>(k + e0);
+    const f32x4 cv = *reinterpret_cast<const f32x4*>(cs + t * (D / 2) + 4 * c);
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(sn + t * (D / 2) + 4 * c);
+    u32x4 rq, rk;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const float x0 = bf16_lo(w[p]), x1 = bf16_hi(w[p]);
-        r[p] = pack2<f16>(x0 * cv[p] - x1 * sv[p], x0 * sv[p] + x1 * cv[p]);
+        const float q0 = bf16_lo(wq[p]), q1 = bf16_hi(wq[p]);
+        const float k0 = bf16_lo(wk[p]), k1 = bf16_hi(wk[p]);
+        rq[p] = pack2<f16>(q0 * cv[p] - q1 * sv[p], q0 * sv[p] + q1 * cv[p]);
+        rk[p] = pack2<f16>(k0 * cv[p] - k1 * sv[p], k0 * sv[p] + k1 * cv[p]);
     }
-    *reinterpret_cast<u32x4*>(out + which * chunks * 8 + e0) = r;
+    *reinterpret_cast<u32x4*>(out + e0) = rq;
+    *reinterpret_cast<u32x4*>(out + (size_t)chunks * 8 + e0) = rk;
 }
 
 hipError_t launch_rotate_qk(const void* q, const void* k, const float* cs, const float* sn,
                             void* out, int B, int H, int T, int D, hipStream_t st) {
-    const long chunks = (long)B * H * T * D / 8;
-    const long blocks = (2 * chunks + 255) / 256;
-    hipLaunchKernelGGL(rotate_qk_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const bf16*)q, (const bf16*)k, cs, sn, (f16*)out, T, D, chunks);
+    const int chunks = (int)((long)B * H * T * D / 8);
+    const int blocks = (chunks + 255) / 256;
+    if (D == 64)
+        hipLaunchKernelGGL(rotate_qk_kernel<64>, dim3(blocks), dim3(256), 0, st, (const bf16*)q,
+                           (const bf16*)k, cs, sn, (f16*)out, T, chunks);
+    else
+        hipLaunchKernelGGL(rotate_qk_kernel<128>, dim3(blocks), dim3(256), 0, st, (const bf16*)q,
+                           (const bf16*)k, cs, sn, (f16*)out, T, chunks);
     return hipGetLastError();
 }
 
