@@ -99,7 +99,7 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const bf16
 // Step n of the dq kernel's key-tile loop on ring stage STG (= n % NS).
 template <int D, int STG, bool DIAG>
 __device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const bf16x8* df,
-                                        char (*smem)[2 * BwdTile<D>::TILE],
+                                        const Ring& rg,
                                         const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
                                         const f16* kr, const bf16* v, int T, int n, int wq0,
                                         int lane, int wave, float sc, float lt, float dl) {
@@ -107,11 +107,11 @@ __device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const bf16
     constexpr int NS = C::NS;
     constexpr int NXT = (STG + NS - 1) % NS;
     wait_vmcnt<C::LPT * (NS - 2)>();
-    __syncthreads();
+    ring_barrier();
     const int nx = n + NS - 1;
-    ld.issue(kr, T, nx * C::KN, smem[NXT], wave);
-    ld.issue(v, T, nx * C::KN, smem[NXT] + C::TILE, wave);
-    dq_tile<D, DIAG>(acc, qf, df, smem[STG], smem[STG] + C::TILE, of, n * C::KN, wq0, lane, sc,
+    ld.issue(kr, T, nx * C::KN, rg.k[NXT], wave);
+    ld.issue(v, T, nx * C::KN, rg.v[NXT], wave);
+    dq_tile<D, DIAG>(acc, qf, df, rg.k[STG], rg.v[STG], of, n * C::KN, wq0, lane, sc,
                      lt, dl);
 }
 
@@ -123,7 +123,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
     float* __restrict__ ws, int BH, int T, int nqb, float sc, float scale) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
-    __shared__ __attribute__((aligned(1024))) char smem[NS][2 * C::TILE];
+    constexpr int T3 = NS > 2 ? C::TILE : 1024;
+    __shared__ __attribute__((aligned(1024))) char k0[C::TILE], k1[C::TILE], k2[T3];
+    __shared__ __attribute__((aligned(1024))) char v0[C::TILE], v1[C::TILE], v2[T3];
+    const Ring rg = {{k0, k1, k2}, {v0, v1, v2}, {nullptr, nullptr, nullptr}};
 
     const int bid = blockIdx.x;
     const int bh = bid % BH;
@@ -148,8 +151,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
     const int nfull = min(ntiles, q0 / C::KN);
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) {
-        ld.issue(kh, T, s * C::KN, smem[s], wave);
-        ld.issue(vh, T, s * C::KN, smem[s] + C::TILE, wave);
+        ld.issue(kh, T, s * C::KN, rg.k[s], wave);
+        ld.issue(vh, T, s * C::KN, rg.v[s], wave);
     }
 
     // this lane's query: rotated q (fp16), dO (bf16), and delta = sum_d dO o
@@ -177,19 +180,19 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
 
     int n = 0;
     for (; n + NS <= nfull; n += NS) {
-        dq_step<D, 0, false>(acc, qf, df, smem, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
-        dq_step<D, 1, false>(acc, qf, df, smem, ld, of, kh, vh, T, n + 1, wq0, lane, wave, sc, lt, dl);
+        dq_step<D, 0, false>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
+        dq_step<D, 1, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 1, wq0, lane, wave, sc, lt, dl);
         if constexpr (NS > 2)
-            dq_step<D, 2, false>(acc, qf, df, smem, ld, of, kh, vh, T, n + 2, wq0, lane, wave, sc, lt, dl);
+            dq_step<D, 2, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 2, wq0, lane, wave, sc, lt, dl);
     }
     for (; n < ntiles; ++n) {
         const int stg = n % NS;
         if (stg == 0)
-            dq_step<D, 0, true>(acc, qf, df, smem, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
+            dq_step<D, 0, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
         else if (stg == 1)
-            dq_step<D, 1, true>(acc, qf, df, smem, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
+            dq_step<D, 1, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
         else if constexpr (NS > 2)
-            dq_step<D, 2, true>(acc, qf, df, smem, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
+            dq_step<D, 2, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
     }
     wait_vmcnt<0>();
 
@@ -295,13 +298,14 @@ struct DkdvCtx {
 
     // query tile qt -> LDS stage st: rotated Q and dO tiles, then the
     // (lse*log2 e, delta) pairs of its 64 queries (each wave fetches 16 pairs)
-    __device__ __forceinline__ void issue(const TileLoads<D, 64, 4>& ld, int qt, char* st) const {
-        constexpr int QN = BwdTile<D>::QN, TILE = BwdTile<D>::TILE;
-        ld.issue(qh, T, qt * QN, st, wave);
-        ld.issue(gh, T, qt * QN, st + TILE, wave);
+    __device__ __forceinline__ void issue(const TileLoads<D, 64, 4>& ld, int qt, char* qs,
+                                          char* gs, char* ls) const {
+        constexpr int QN = BwdTile<D>::QN;
+        ld.issue(qh, T, qt * QN, qs, wave);
+        ld.issue(gh, T, qt * QN, gs, wave);
         if (lane < 32)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                make_rsrc(lh, (uint32_t)T * 8), LDS_PTR(st + 2 * TILE + 128 * wave), 4,
+                make_rsrc(lh, (uint32_t)T * 8), LDS_PTR(ls + 128 * wave), 4,
                 (uint32_t)((qt * QN + 16 * wave) * 8 + 4 * lane), 0, 0, 0);
     }
 };
@@ -309,19 +313,18 @@ struct DkdvCtx {
 // Step of the dk/dv kernel's query-tile loop on ring stage STG.
 template <int D, int STG, bool DIAG>
 __device__ __forceinline__ void dkdv_step(f32x16* dva, f32x16* dka, const f16x8* kf,
-                                          const bf16x8* vf, char (*smem)[2 * BwdTile<D>::TILE + 512],
+                                          const bf16x8* vf, const Ring& rg,
                                           const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
                                           const DkdvCtx<D>& x, int qt) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int NXT = (STG + NS - 1) % NS;
     wait_vmcnt<(C::LPT + 1) * (NS - 2)>();
-    __syncthreads();
-    x.issue(ld, qt + NS - 1, smem[NXT]);
-    const char* qs = smem[STG];
-    dkdv_tile<D, DIAG>(dva, dka, kf, vf, qs, qs + C::TILE,
-                       reinterpret_cast<const float*>(qs + 2 * C::TILE), of, qt * C::QN, x.wk0,
-                       x.lane, x.sc);
+    ring_barrier();
+    x.issue(ld, qt + NS - 1, rg.k[NXT], rg.v[NXT], rg.x[NXT]);
+    dkdv_tile<D, DIAG>(dva, dka, kf, vf, rg.k[STG], rg.v[STG],
+                       reinterpret_cast<const float*>(rg.x[STG]), of, qt * C::QN, x.wk0, x.lane,
+                       x.sc);
 }
 
 template <int D>
@@ -332,7 +335,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
     int nkb, float sc, float scale) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
-    __shared__ __attribute__((aligned(1024))) char smem[NS][2 * C::TILE + 512];
+    constexpr int T3 = NS > 2 ? C::TILE : 1024;
+    __shared__ __attribute__((aligned(1024))) char q0s[C::TILE], q1s[C::TILE], q2s[T3];
+    __shared__ __attribute__((aligned(1024))) char g0s[C::TILE], g1s[C::TILE], g2s[T3];
+    __shared__ __attribute__((aligned(512))) char l0s[512], l1s[512], l2s[512];
+    const Ring rg = {{q0s, q1s, q2s}, {g0s, g1s, g2s}, {l0s, l1s, l2s}};
 
     const int bid = blockIdx.x;
     const int bh = bid % BH;
@@ -353,7 +360,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
     const int nqt = (T + C::QN - 1) / C::QN;
     const int qfull = min(nqt, (k0 + C::KM) / C::QN);  // from here on no query precedes a key
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) x.issue(ld, qt0 + s, smem[s]);
+    for (int s = 0; s < NS - 1; ++s) x.issue(ld, qt0 + s, rg.k[s], rg.v[s], rg.x[s]);
 
     const rsrc_t kbuf = make_rsrc(kr + hoff, hbytes), vbuf = make_rsrc(v + hoff, hbytes);
     f16x8 kf[C::DK];
@@ -372,26 +379,26 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
     int qt = qt0;
     for (; qt < min(qfull, nqt); ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 0) dkdv_step<D, 0, true>(dva, dka, kf, vf, smem, ld, of, x, qt);
-        else if (stg == 1) dkdv_step<D, 1, true>(dva, dka, kf, vf, smem, ld, of, x, qt);
-        else if constexpr (NS > 2) dkdv_step<D, 2, true>(dva, dka, kf, vf, smem, ld, of, x, qt);
+        if (stg == 0) dkdv_step<D, 0, true>(dva, dka, kf, vf, rg, ld, of, x, qt);
+        else if (stg == 1) dkdv_step<D, 1, true>(dva, dka, kf, vf, rg, ld, of, x, qt);
+        else if constexpr (NS > 2) dkdv_step<D, 2, true>(dva, dka, kf, vf, rg, ld, of, x, qt);
     }
     // the full tiles, rotated so that the unrolled body starts on stage 0
     for (; qt < nqt && (qt - qt0) % NS != 0; ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
-        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
+        if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
+        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
     }
     for (; qt + NS <= nqt; qt += NS) {
-        dkdv_step<D, 0, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
-        dkdv_step<D, 1, false>(dva, dka, kf, vf, smem, ld, of, x, qt + 1);
-        if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, smem, ld, of, x, qt + 2);
+        dkdv_step<D, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
+        dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 1);
+        if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 2);
     }
     for (; qt < nqt; ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 0) dkdv_step<D, 0, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
-        else if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
-        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, smem, ld, of, x, qt);
+        if (stg == 0) dkdv_step<D, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
+        else if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
+        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
     }
     wait_vmcnt<0>();
 

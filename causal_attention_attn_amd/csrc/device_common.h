@@ -235,6 +235,28 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
+// Workgroup barrier for the LDS ring. Each wave first waits for its own LDS
+// reads (lgkmcnt) - its direct-to-LDS loads were already waited for with
+// wait_vmcnt - so a plain s_barrier both publishes the tiles those loads
+// filled and guarantees the stage about to be refilled is no longer read.
+// __syncthreads() would add a release fence that also waits for every
+// direct-to-LDS load still in flight (vmcnt(0)), emptying the prefetch ring.
+// The "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The LDS ring: every stage's tiles are separate __shared__ objects, so the
+// compiler can tell that reading one stage does not depend on the
+// direct-to-LDS loads still filling another (with one array it waits for every
+// load in flight before each operand read). k and v are the two 64-row tiles of
+// a stage, x an optional small extra block.
+struct Ring {
+    char* k[3];
+    char* v[3];
+    char* x[3];
+};
+
 // Swizzled 16-byte chunk position of chunk c in row r of a tile with D-element
 // (2*D-byte) rows. LDS serves 256 bytes per cycle: 16 lanes of a 16-byte read,
 // 32 lanes of an 8-byte read. The XOR pattern keeps both operand reads

@@ -140,18 +140,18 @@ struct FwdCtx {
 // Step n of the tile loop on ring stage STG (= n % NS): wait for tile n,
 // publish it, refill the stage freed by tile n-1 with tile n+NS-1, compute.
 template <int D, int STG, bool DIAG>
-__device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, char (*smem)[2 * FwdTile<D>::TILE],
+__device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, const Ring& rg,
                                          const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
                                          const FwdCtx<D>& x, int n) {
     using C = FwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int NXT = (STG + NS - 1) % NS;
     wait_vmcnt<C::LPT * (NS - 2)>();
-    __syncthreads();
+    ring_barrier();
     const int nx = n + NS - 1;
-    ld.issue(x.kr, x.T, nx * C::BN, smem[NXT], x.wave);
-    ld.issue(x.v, x.T, nx * C::BN, smem[NXT] + C::TILE, x.wave);
-    fwd_tile<D, DIAG>(st, qf, smem[STG], smem[STG] + C::TILE, of, n * C::BN, x.wq0, x.lane, x.sc);
+    ld.issue(x.kr, x.T, nx * C::BN, rg.k[NXT], x.wave);
+    ld.issue(x.v, x.T, nx * C::BN, rg.v[NXT], x.wave);
+    fwd_tile<D, DIAG>(st, qf, rg.k[STG], rg.v[STG], of, n * C::BN, x.wq0, x.lane, x.sc);
 }
 
 template <int D>
@@ -160,7 +160,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     bf16* __restrict__ o, float* __restrict__ lse, int BH, int T, int nqb, float sc) {
     using C = FwdTile<D>;
     constexpr int NS = C::NS;
-    __shared__ __attribute__((aligned(1024))) char smem[NS][2 * C::TILE];
+    constexpr int T3 = NS > 2 ? C::TILE : 1024;
+    __shared__ __attribute__((aligned(1024))) char k0[C::TILE], k1[C::TILE], k2[T3];
+    __shared__ __attribute__((aligned(1024))) char v0[C::TILE], v1[C::TILE], v2[T3];
+    const Ring rg = {{k0, k1, k2}, {v0, v1, v2}};
 
     const int bid = blockIdx.x;
     const int bh = bid % BH;
@@ -183,8 +186,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     // prologue: tiles 0 .. NS-2 in flight (tiles past the end read as zeros)
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) {
-        ld.issue(x.kr, T, s * C::BN, smem[s], wave);
-        ld.issue(x.v, T, s * C::BN, smem[s] + C::TILE, wave);
+        ld.issue(x.kr, T, s * C::BN, rg.k[s], wave);
+        ld.issue(x.v, T, s * C::BN, rg.v[s], wave);
     }
 
     const rsrc_t qh = make_rsrc(qr + hoff, (uint32_t)T * D * 2);
@@ -202,16 +205,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     int n = 0;
     // full tiles: branch-free bodies, ring stages as compile-time constants
     for (; n + NS <= nfull; n += NS) {
-        fwd_step<D, 0, false>(st, qf, smem, ld, of, x, n);
-        fwd_step<D, 1, false>(st, qf, smem, ld, of, x, n + 1);
-        if constexpr (NS > 2) fwd_step<D, 2, false>(st, qf, smem, ld, of, x, n + 2);
+        fwd_step<D, 0, false>(st, qf, rg, ld, of, x, n);
+        fwd_step<D, 1, false>(st, qf, rg, ld, of, x, n + 1);
+        if constexpr (NS > 2) fwd_step<D, 2, false>(st, qf, rg, ld, of, x, n + 2);
     }
     // the rest (at most NS-1 full tiles, then the diagonal tiles)
     for (; n < ntiles; ++n) {
         const int stg = n % NS;
-        if (stg == 0) fwd_step<D, 0, true>(st, qf, smem, ld, of, x, n);
-        else if (stg == 1) fwd_step<D, 1, true>(st, qf, smem, ld, of, x, n);
-        else if constexpr (NS > 2) fwd_step<D, 2, true>(st, qf, smem, ld, of, x, n);
+        if (stg == 0) fwd_step<D, 0, true>(st, qf, rg, ld, of, x, n);
+        else if (stg == 1) fwd_step<D, 1, true>(st, qf, rg, ld, of, x, n);
+        else if constexpr (NS > 2) fwd_step<D, 2, true>(st, qf, rg, ld, of, x, n);
     }
     wait_vmcnt<0>();  // no LDS writes may land after this workgroup's LDS is released
 
