@@ -15,6 +15,12 @@
 //                from the diagonal down): with the same P and dS,
 //                dV += P^T dO, dK^r += s dS^T Q^r, and finally dk = R_u^T dK^r.
 //
+// The saved query carries the factor log2(e)/sqrt(D), so a score product is
+// S log2(e) and P = 2^(S log2(e) - lse log2(e)). The per-query offsets
+// -lse log2(e) and -delta are the initial accumulators of the S and dP
+// products, which leaves one exp2 and one multiply per element for dS; the
+// factor on the query is undone in dK^r (ln 2 instead of s).
+//
 // Every product is a 32x32x16 MFMA contraction with fp32 accumulation. The
 // rotated q and k and dS are fp16 (the score recompute needs the 11-bit
 // significand, see the forward; dS then shares the fp16 MFMA with them, which
@@ -49,7 +55,8 @@ struct BwdTile {
 template <int D, bool DIAG>
 __device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const bf16x8* df,
                                         const char* ks, const char* vs, const OperandOffs<D>& of,
-                                        int k0, int wq0, int lane, float sc, float lt, float dl) {
+                                        int k0, int wq0, int lane, const f32x16& nl,
+                                        const f32x16& nd) {
     using C = BwdTile<D>;
     constexpr int ROWB = 2 * D;
     const int c32 = lane & 31, hf = lane >> 5;
@@ -60,17 +67,19 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const bf16
         if (DIAG && kb > wq0) break;
         const char* kr = ks + 32 * sb * ROWB;
         const char* vr = vs + 32 * sb * ROWB;
-        f32x16 s = mfma32(*reinterpret_cast<const f16x8*>(kr + of.k[0]), qf[0], f32x16{});
-        f32x16 dp = mfma32(*reinterpret_cast<const bf16x8*>(vr + of.k[0]), df[0], f32x16{});
+        // x = S log2(e) - lse log2(e) and dp = dP - delta: the offsets are the
+        // accumulators' initial values
+        f32x16 x = mfma32(*reinterpret_cast<const f16x8*>(kr + of.k[0]), qf[0], nl);
+        f32x16 dp = mfma32(*reinterpret_cast<const bf16x8*>(vr + of.k[0]), df[0], nd);
 #pragma unroll
         for (int c = 1; c < C::DK; ++c) {
-            s = mfma32(*reinterpret_cast<const f16x8*>(kr + of.k[c]), qf[c], s);
+            x = mfma32(*reinterpret_cast<const f16x8*>(kr + of.k[c]), qf[c], x);
             dp = mfma32(*reinterpret_cast<const bf16x8*>(vr + of.k[c]), df[c], dp);
         }
         if (DIAG && kb == wq0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (item_row(i, hf) > c32) s[i] = -INFINITY;
+                if (item_row(i, hf) > c32) x[i] = -INFINITY;
         }
         f16x8 dsb[2];
 #pragma unroll
@@ -79,9 +88,7 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const bf16
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 8 * j + 2 * e;
-                const float p0 = exp2_fast(fmaf(s[i], sc, -lt));
-                const float p1 = exp2_fast(fmaf(s[i + 1], sc, -lt));
-                w[e] = pack2<f16>(p0 * (dp[i] - dl), p1 * (dp[i + 1] - dl));
+                w[e] = pack2<f16>(exp2_fast(x[i]) * dp[i], exp2_fast(x[i + 1]) * dp[i + 1]);
             }
             dsb[j] = as_vec8<f16x8>(w);
         }
@@ -102,7 +109,7 @@ __device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const bf16
                                         const Ring& rg,
                                         const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
                                         const f16* kr, const bf16* v, int T, int n, int wq0,
-                                        int lane, int wave, float sc, float lt, float dl) {
+                                        int lane, int wave, const f32x16& nl, const f32x16& nd) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int NXT = (STG + NS - 1) % NS;
@@ -111,8 +118,7 @@ __device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const bf16
     const int nx = n + NS - 1;
     ld.issue(kr, T, nx * C::KN, rg.k[NXT], wave);
     ld.issue(v, T, nx * C::KN, rg.v[NXT], wave);
-    dq_tile<D, DIAG>(acc, qf, df, rg.k[STG], rg.v[STG], of, n * C::KN, wq0, lane, sc,
-                     lt, dl);
+    dq_tile<D, DIAG>(acc, qf, df, rg.k[STG], rg.v[STG], of, n * C::KN, wq0, lane, nl, nd);
 }
 
 template <int D>
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
     const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
     const bf16* __restrict__ o, const bf16* __restrict__ dO, const float* __restrict__ lse,
     const float* __restrict__ cs, const float* __restrict__ sn, bf16* __restrict__ dq,
-    float* __restrict__ ws, int BH, int T, int nqb, float sc, float scale) {
+    float* __restrict__ ws, int BH, int T, int nqb, float scale) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int T3 = NS > 2 ? C::TILE : 1024;
@@ -170,9 +176,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
             dot += bf16_lo(g[e]) * bf16_lo(y[e]) + bf16_hi(g[e]) * bf16_hi(y[e]);
         df[c] = as_bf16x8(g);
     }
-    const float dl = sum_across_halves(dot);
-    const float lt = tq < T ? lse[(size_t)bh * T + tq] * kLog2e : 0.f;
-    if (tq < T && hf == 0) *reinterpret_cast<f32x2*>(ws + 2 * ((size_t)bh * T + tq)) = f32x2{lt, dl};
+    const float ndl = -sum_across_halves(dot);
+    const float nlt = tq < T ? -lse[(size_t)bh * T + tq] * kLog2e : 0.f;
+    // workspace: -lse*log2(e) of every row, then -delta of every row
+    if (tq < T && hf == 0) {
+        ws[(size_t)bh * T + tq] = nlt;
+        ws[(size_t)BH * T + (size_t)bh * T + tq] = ndl;
+    }
+    const f32x16 nl = splat16(nlt), nd = splat16(ndl);
 
     f32x16 acc[C::DB];
 #pragma unroll
@@ -180,19 +191,19 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
 
     int n = 0;
     for (; n + NS <= nfull; n += NS) {
-        dq_step<D, 0, false>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
-        dq_step<D, 1, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 1, wq0, lane, wave, sc, lt, dl);
+        dq_step<D, 0, false>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, nl, nd);
+        dq_step<D, 1, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 1, wq0, lane, wave, nl, nd);
         if constexpr (NS > 2)
-            dq_step<D, 2, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 2, wq0, lane, wave, sc, lt, dl);
+            dq_step<D, 2, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 2, wq0, lane, wave, nl, nd);
     }
     for (; n < ntiles; ++n) {
         const int stg = n % NS;
         if (stg == 0)
-            dq_step<D, 0, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
+            dq_step<D, 0, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, nl, nd);
         else if (stg == 1)
-            dq_step<D, 1, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
+            dq_step<D, 1, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, nl, nd);
         else if constexpr (NS > 2)
-            dq_step<D, 2, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, sc, lt, dl);
+            dq_step<D, 2, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, nl, nd);
     }
     wait_vmcnt<0>();
 
@@ -222,13 +233,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
 
 // One 64-query tile of the dk/dv kernel for one wave (32 keys). DIAG: the tile
 // may reach this wave's diagonal (32-query blocks wholly before the wave's
-// first key skipped, the diagonal one masked). ld holds (lse*log2 e, delta)
-// for the tile's 64 queries.
+// first key skipped, the diagonal one masked). ld holds -lse*log2(e) of the
+// tile's 64 queries, then their -delta; in S and dP a lane is a key and the
+// items are queries, so these per-query offsets, read as the accumulators'
+// initial values, give x = S log2(e) - lse log2(e) and dp = dP - delta.
 template <int D, bool DIAG>
 __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8* kf,
                                           const bf16x8* vf, const char* qs, const char* gs,
                                           const float* ld, const OperandOffs<D>& of, int qbase,
-                                          int wk0, int lane, float sc) {
+                                          int wk0, int lane) {
     using C = BwdTile<D>;
     constexpr int ROWB = 2 * D;
     const int c32 = lane & 31, hf = lane >> 5;
@@ -239,17 +252,29 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8*
         if (DIAG && qb + 31 < wk0) continue;
         const char* qr = qs + 32 * sb * ROWB;
         const char* gr = gs + 32 * sb * ROWB;
-        f32x16 s = mfma32(*reinterpret_cast<const f16x8*>(qr + of.k[0]), kf[0], f32x16{});
-        f32x16 dp = mfma32(*reinterpret_cast<const bf16x8*>(gr + of.k[0]), vf[0], f32x16{});
+        // items 4g .. 4g+3 of a lane half hf are queries 8g + 4hf .. +3 of the block
+        f32x16 nl, nd;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(ld + 32 * sb + 8 * g + 4 * hf);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(ld + 64 + 32 * sb + 8 * g + 4 * hf);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                nl[4 * g + e] = a[e];
+                nd[4 * g + e] = b[e];
+            }
+        }
+        f32x16 x = mfma32(*reinterpret_cast<const f16x8*>(qr + of.k[0]), kf[0], nl);
+        f32x16 dp = mfma32(*reinterpret_cast<const bf16x8*>(gr + of.k[0]), vf[0], nd);
 #pragma unroll
         for (int c = 1; c < C::DK; ++c) {
-            s = mfma32(*reinterpret_cast<const f16x8*>(qr + of.k[c]), kf[c], s);
+            x = mfma32(*reinterpret_cast<const f16x8*>(qr + of.k[c]), kf[c], x);
             dp = mfma32(*reinterpret_cast<const bf16x8*>(gr + of.k[c]), vf[c], dp);
         }
         if (DIAG && qb == wk0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (item_row(i, hf) < c32) s[i] = -INFINITY;
+                if (item_row(i, hf) < c32) x[i] = -INFINITY;
         }
         bf16x8 pb[2];
         f16x8 dsb[2];
@@ -257,20 +282,11 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8*
         for (int j = 0; j < 2; ++j) {
             u32x4 wp, wd;
 #pragma unroll
-            for (int g2 = 0; g2 < 2; ++g2) {
-                // items 8j + 4*g2 .. +3 belong to queries 16j + 8*g2 + 4*hf .. +3
-                const float* lq = ld + 2 * (32 * sb + 16 * j + 8 * g2 + 4 * hf);
-                const f32x4 a01 = *reinterpret_cast<const f32x4*>(lq);      // l0 d0 l1 d1
-                const f32x4 a23 = *reinterpret_cast<const f32x4*>(lq + 4);  // l2 d2 l3 d3
-                const int i = 8 * j + 4 * g2;
-                const float p0 = exp2_fast(fmaf(s[i], sc, -a01[0]));
-                const float p1 = exp2_fast(fmaf(s[i + 1], sc, -a01[2]));
-                const float p2 = exp2_fast(fmaf(s[i + 2], sc, -a23[0]));
-                const float p3 = exp2_fast(fmaf(s[i + 3], sc, -a23[2]));
-                wp[2 * g2] = pack_bf16x2(p0, p1);
-                wp[2 * g2 + 1] = pack_bf16x2(p2, p3);
-                wd[2 * g2] = pack2<f16>(p0 * (dp[i] - a01[1]), p1 * (dp[i + 1] - a01[3]));
-                wd[2 * g2 + 1] = pack2<f16>(p2 * (dp[i + 2] - a23[1]), p3 * (dp[i + 3] - a23[3]));
+            for (int e = 0; e < 4; ++e) {
+                const int i = 8 * j + 2 * e;
+                const float p0 = exp2_fast(x[i]), p1 = exp2_fast(x[i + 1]);
+                wp[e] = pack_bf16x2(p0, p1);
+                wd[e] = pack2<f16>(p0 * dp[i], p1 * dp[i + 1]);
             }
             pb[j] = as_bf16x8(wp);
             dsb[j] = as_vec8<f16x8>(wd);
@@ -292,12 +308,11 @@ template <int D>
 struct DkdvCtx {
     const f16* qh;
     const bf16* gh;
-    const float* lh;  // (lse*log2 e, delta) pairs of this head's rows
+    const float* oh;  // this wave's per-row offsets: -lse*log2(e) (waves 0, 1) or -delta (2, 3)
     int T, wk0, lane, wave;
-    float sc;
 
-    // query tile qt -> LDS stage st: rotated Q and dO tiles, then the
-    // (lse*log2 e, delta) pairs of its 64 queries (each wave fetches 16 pairs)
+    // query tile qt -> LDS stage: rotated Q and dO tiles, then 32 of the 128
+    // per-query offsets of its 64 queries from each wave (rows past T read 0)
     __device__ __forceinline__ void issue(const TileLoads<D, 64, 4>& ld, int qt, char* qs,
                                           char* gs, char* ls) const {
         constexpr int QN = BwdTile<D>::QN;
@@ -305,8 +320,8 @@ struct DkdvCtx {
         ld.issue(gh, T, qt * QN, gs, wave);
         if (lane < 32)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                make_rsrc(lh, (uint32_t)T * 8), LDS_PTR(ls + 128 * wave), 4,
-                (uint32_t)((qt * QN + 16 * wave) * 8 + 4 * lane), 0, 0, 0);
+                make_rsrc(oh, (uint32_t)T * 4), LDS_PTR(ls + 128 * wave), 4,
+                (uint32_t)((qt * QN + 32 * (wave & 1)) * 4 + 4 * lane), 0, 0, 0);
     }
 };
 
@@ -323,8 +338,7 @@ __device__ __forceinline__ void dkdv_step(f32x16* dva, f32x16* dka, const f16x8*
     ring_barrier();
     x.issue(ld, qt + NS - 1, rg.k[NXT], rg.v[NXT], rg.x[NXT]);
     dkdv_tile<D, DIAG>(dva, dka, kf, vf, rg.k[STG], rg.v[STG],
-                       reinterpret_cast<const float*>(rg.x[STG]), of, qt * C::QN, x.wk0, x.lane,
-                       x.sc);
+                       reinterpret_cast<const float*>(rg.x[STG]), of, qt * C::QN, x.wk0, x.lane);
 }
 
 template <int D>
@@ -332,7 +346,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
     const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ ws, const float* __restrict__ cs,
     const float* __restrict__ sn, bf16* __restrict__ dk, bf16* __restrict__ dv, int BH, int T,
-    int nkb, float sc, float scale) {
+    int nkb, float scale) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int T3 = NS > 2 ? C::TILE : 1024;
@@ -352,7 +366,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
     const uint32_t hbytes = (uint32_t)T * D * 2;
     const int wk0 = k0 + wave * 32;
     const int tk = wk0 + c32;
-    const DkdvCtx<D> x = {qr + hoff, dO + hoff, ws + 2 * (size_t)bh * T, T, wk0, lane, wave, sc};
+    const DkdvCtx<D> x = {qr + hoff, dO + hoff, ws + (size_t)(wave >> 1) * BH * T + (size_t)bh * T,
+                          T, wk0, lane, wave};
     const TileLoads<D, 64, 4> ld(wave, lane);
     const OperandOffs<D> of(lane);
 
@@ -439,7 +454,7 @@ static hipError_t launch_dq(const BwdArgs& a) {
     const f16* rot = static_cast<const f16*>(a.rot);
     hipLaunchKernelGGL(bwd_dq_bf16_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream, rot,
                        rot + n, (const bf16*)a.v, (const bf16*)a.o, (const bf16*)a.dO, a.lse,
-                       a.cs, a.sn, (bf16*)a.dq, a.ws, BH, a.T, nqb, scale * kLog2e, scale);
+                       a.cs, a.sn, (bf16*)a.dq, a.ws, BH, a.T, nqb, scale);
     return hipGetLastError();
 }
 
@@ -448,12 +463,11 @@ static hipError_t launch_dkdv(const BwdArgs& a) {
     using C = BwdTile<D>;
     const int BH = a.B * a.H;
     const int nkb = (a.T + C::KM - 1) / C::KM;
-    const float scale = 1.f / sqrtf((float)D);
     const size_t n = (size_t)a.B * a.H * a.T * a.D;
     const f16* rot = static_cast<const f16*>(a.rot);
     hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<D>, dim3(nkb * BH), dim3(C::NT), 0, a.stream, rot,
                        rot + n, (const bf16*)a.v, (const bf16*)a.dO, a.ws, a.cs, a.sn,
-                       (bf16*)a.dk, (bf16*)a.dv, BH, a.T, nkb, scale * kLog2e, scale);
+                       (bf16*)a.dk, (bf16*)a.dv, BH, a.T, nkb, kLn2);
     return hipGetLastError();
 }
 

@@ -33,6 +33,28 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A 32x32 accumulator with every entry equal to x. Used as the initial value
+// of a score product, it subtracts a per-lane offset (a running maximum, a
+// log-sum-exp, a row dot product) inside the MFMA instead of once per element.
+__device__ __forceinline__ f32x16 splat16(float x) {
+    f32x16 r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = x;
+    return r;
+}
+
+// acc + lo(w) + hi(w) for a packed bf16 pair w (v_dot2c_f32_bf16 against 1, 1):
+// two probabilities summed per instruction, exactly the rounded values that
+// feed the following MFMA.
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w),
+                                           __builtin_bit_cast(b2, 0x3f803f80u), acc, false);
+}
+
+// True on every lane when the predicate holds on any active lane of the wave.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

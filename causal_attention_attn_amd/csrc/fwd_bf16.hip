@@ -19,7 +19,10 @@
 //     NS-1 tiles ahead of use: no registers hold tiles in flight, and one
 //     barrier per tile both publishes a tile and frees the oldest stage;
 //   * S^T puts one query per lane column, so each lane owns one query's running
-//     max/sum and only one cross-lane exchange (lane ^ 32) is needed per tile;
+//     max/sum; the running maximum enters as the MFMA's initial accumulator, so
+//     the per-element softmax work is exp2, bf16 rounding and a packed pair sum
+//     (the exact tile maximum is only taken when the probabilities would leave
+//     their bound, see fwd_tile);
 //   * the rounded probabilities of S^T are directly the B operand of
 //     O^T += V^T P^T; the V^T operand comes from the row-major V tile through
 //     the LDS transpose read (ds_read_b64_tr_b16);
@@ -48,81 +51,129 @@ struct FwdTile {
 };
 
 // Running state of one lane's query: O^T accumulator (this lane's half of the
-// head dimension), reference maximum m (log2 units) and partial row sum l.
+// head dimension), reference maximum m (log2 units), -m in every entry of an
+// accumulator (the initial value of the score MFMAs) and the partial row sum l.
 template <int D>
 struct FwdState {
     f32x16 o[D / 32];
+    f32x16 negm;
     float m, l;
 };
 
+// Probabilities p = 2^x of the tile's live 32-key blocks, rounded to bf16 and
+// packed as the B operand of O^T += V^T P^T; returns this lane's sum of the
+// rounded values.
+template <int D, bool DIAG>
+__device__ __forceinline__ float fwd_probs(const f32x16* x, bf16x8 (*pb)[2], int k0, int wq0) {
+    using C = FwdTile<D>;
+    float part[C::NSB][2];
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+        if (DIAG && k0 + 32 * sb > wq0) break;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            u32x4 w;
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w[e] = pack_bf16x2(exp2_fast(x[sb][8 * j + 2 * e]),
+                                   exp2_fast(x[sb][8 * j + 2 * e + 1]));
+                a = add_bf16x2(w[e], a);
+            }
+            pb[sb][j] = as_bf16x8(w);
+            part[sb][j] = a;
+        }
+    }
+    float t = part[0][0] + part[0][1];
+#pragma unroll
+    for (int sb = 1; sb < C::NSB; ++sb) {
+        if (DIAG && k0 + 32 * sb > wq0) break;
+        t += part[sb][0] + part[sb][1];
+    }
+    return t;
+}
+
 // One 64-key tile for one wave. DIAG: the tile may reach this wave's diagonal,
 // so 32-key sub-blocks above it are skipped and the diagonal one is masked.
+//
+// The scores arrive in log2 units (the query carries log2(e)/sqrt(D)) with the
+// reference maximum already subtracted by the MFMA, x = S*log2(e) - m. The
+// online softmax needs no per-tile maximum while the probabilities stay
+// bounded: if every lane's sum of this tile's p = 2^x is at most 2^8, no single
+// x exceeds 8, so O and l may keep the reference m (the bound on unnormalised
+// probabilities is the same as a lazy rescale with threshold 8). Otherwise
+// (and on the wave's first tile, which sets m) the exact maximum is taken, O
+// and l are rescaled and the tile's probabilities are recomputed.
 template <int D, bool DIAG>
 __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const f16x8* qf, const char* ks,
                                          const char* vs, const OperandOffs<D>& of, int k0, int wq0,
-                                         int lane, float sc) {
+                                         int lane, bool first) {
     using C = FwdTile<D>;
-    constexpr float kRescale = 8.f;
+    constexpr float kLimit = 256.f;
     constexpr int ROWB = 2 * D;  // bytes per tile row
     const int c32 = lane & 31, hf = lane >> 5;
     if (DIAG && k0 > wq0) return;  // whole tile above this wave's diagonal
-    f32x16 s[C::NSB];
+    f32x16 x[C::NSB];
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
         if (DIAG && k0 + 32 * sb > wq0) break;
         const char* kb = ks + 32 * sb * ROWB;
-        f32x16 acc = mfma32(*reinterpret_cast<const f16x8*>(kb + of.k[0]), qf[0], f32x16{});
+        f32x16 acc = mfma32(*reinterpret_cast<const f16x8*>(kb + of.k[0]), qf[0], st.negm);
 #pragma unroll
         for (int c = 1; c < C::DK; ++c)
             acc = mfma32(*reinterpret_cast<const f16x8*>(kb + of.k[c]), qf[c], acc);
-        s[sb] = acc;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
-        if (DIAG && k0 + 32 * sb > wq0) break;
+        x[sb] = acc;
         if (DIAG && k0 + 32 * sb == wq0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (item_row(i, hf) > c32) s[sb][i] = -INFINITY;
+                if (item_row(i, hf) > c32) x[sb][i] = -INFINITY;
         }
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[sb][i], s[sb][i + 1]));
     }
-    mx = max_across_halves(mx) * sc;
-    // the reference maximum only moves when the tile maximum exceeds it by more
-    // than kRescale (log2 units), so the O/l rescale is rare; unnormalised
-    // probabilities stay below 2^kRescale
-    if (mx > st.m + kRescale) {
-        const float alpha = exp2_fast(st.m - mx);
-        st.m = mx;
-        st.l *= alpha;
-#pragma unroll
-        for (int b = 0; b < C::DB; ++b) st.o[b] *= alpha;
+    bf16x8 pb[C::NSB][2];
+    float ts = 0.f;
+    bool slow = first;
+    if (!first) {
+        ts = fwd_probs<D, DIAG>(x, pb, k0, wq0);
+        slow = wave_any(ts > kLimit);
     }
-    const float mneg = -st.m;
+    if (slow) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < C::NSB; ++sb) {
+            if (DIAG && k0 + 32 * sb > wq0) break;
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(x[sb][i], x[sb][i + 1]));
+        }
+        mx = max_across_halves(mx);
+        // first tile: every query sees key 0, so mx is finite and becomes m;
+        // later tiles only move m up
+        const float d = first ? mx : fmaxf(mx, 0.f);
+        if (!first) {
+            const float alpha = exp2_fast(-d);
+            st.l *= alpha;
+#pragma unroll
+            for (int b = 0; b < C::DB; ++b) st.o[b] *= alpha;
+        }
+        st.m += d;
+        st.negm = splat16(-st.m);
+#pragma unroll
+        for (int sb = 0; sb < C::NSB; ++sb) {
+            if (DIAG && k0 + 32 * sb > wq0) break;
+            x[sb] -= d;
+        }
+        ts = fwd_probs<D, DIAG>(x, pb, k0, wq0);
+    }
+    st.l += ts;
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
         if (DIAG && k0 + 32 * sb > wq0) break;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            u32x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p0 = exp2_fast(fmaf(s[sb][8 * j + 2 * e], sc, mneg));
-                const float p1 = exp2_fast(fmaf(s[sb][8 * j + 2 * e + 1], sc, mneg));
-                st.l += p0 + p1;
-                w[e] = pack_bf16x2(p0, p1);
-            }
-            pb[j] = as_bf16x8(w);
-        }
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const char* vb = vs + (32 * sb + 16 * j) * ROWB;
-                st.o[b] = mfma32(tr_pair<bf16x8>(vb + of.v[b][0], vb + of.v[b][1]), pb[j], st.o[b]);
+                st.o[b] = mfma32(tr_pair<bf16x8>(vb + of.v[b][0], vb + of.v[b][1]), pb[sb][j],
+                                 st.o[b]);
             }
         }
     }
@@ -134,7 +185,6 @@ struct FwdCtx {
     const f16* kr;
     const bf16* v;
     int T, wq0, lane, wave;
-    float sc;
 };
 
 // Step n of the tile loop on ring stage STG (= n % NS): wait for tile n,
@@ -151,13 +201,13 @@ __device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, const
     const int nx = n + NS - 1;
     ld.issue(x.kr, x.T, nx * C::BN, rg.k[NXT], x.wave);
     ld.issue(x.v, x.T, nx * C::BN, rg.v[NXT], x.wave);
-    fwd_tile<D, DIAG>(st, qf, rg.k[STG], rg.v[STG], of, n * C::BN, x.wq0, x.lane, x.sc);
+    fwd_tile<D, DIAG>(st, qf, rg.k[STG], rg.v[STG], of, n * C::BN, x.wq0, x.lane, n == 0);
 }
 
 template <int D>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
-    bf16* __restrict__ o, float* __restrict__ lse, int BH, int T, int nqb, float sc) {
+    bf16* __restrict__ o, float* __restrict__ lse, int BH, int T, int nqb) {
     using C = FwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int T3 = NS > 2 ? C::TILE : 1024;
@@ -175,7 +225,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     const size_t hoff = (size_t)bh * T * D;
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
-    const FwdCtx<D> x = {kr + hoff, v + hoff, T, wq0, lane, wave, sc};
+    const FwdCtx<D> x = {kr + hoff, v + hoff, T, wq0, lane, wave};
     const TileLoads<D, 64, 4> ld(wave, lane);
     const OperandOffs<D> of(lane);
 
@@ -199,7 +249,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     FwdState<D> st;
 #pragma unroll
     for (int b = 0; b < C::DB; ++b) st.o[b] = f32x16{};
-    st.m = -INFINITY;
+    st.negm = f32x16{};
+    st.m = 0.f;
     st.l = 0.f;
 
     int n = 0;
@@ -241,11 +292,10 @@ static hipError_t launch_fwd(const FwdArgs& a) {
     using C = FwdTile<D>;
     const int BH = a.B * a.H;
     const int nqb = (a.T + C::BM - 1) / C::BM;
-    const float sc = kLog2e / sqrtf((float)D);
     const size_t n = (size_t)a.B * a.H * a.T * a.D;
     const f16* rot = static_cast<const f16*>(a.rot);
     hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream, rot,
-                       rot + n, (const bf16*)a.v, (bf16*)a.o, a.lse, BH, a.T, nqb, sc);
+                       rot + n, (const bf16*)a.v, (bf16*)a.o, a.lse, BH, a.T, nqb);
     return hipGetLastError();
 }
 

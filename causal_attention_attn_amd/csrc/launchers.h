@@ -10,7 +10,7 @@ namespace attn {
 struct FwdArgs {
     const void *q, *k, *v;
     const float *cs, *sn;
-    const void* rot;  // bf16 path: rotated q then rotated k, [B, H, T, D] fp16 each
+    const void* rot;  // bf16 path: rotated q * log2(e)/sqrt(D), then rotated k, [B, H, T, D] fp16 each
     void* o;
     float* lse;
     int B, H, T, D;
@@ -20,9 +20,10 @@ struct FwdArgs {
 struct BwdArgs {
     const void *q, *k, *v, *o, *dO;
     const float *lse, *cs, *sn;
-    const void* rot;  // bf16 path: rotated q then rotated k, [B, H, T, D] fp16 each
+    const void* rot;  // bf16 path: rotated q * log2(e)/sqrt(D), then rotated k, [B, H, T, D] fp16 each
     void *dq, *dk, *dv;
-    float* ws;  // workspace: bf16 path [B, H, T] x (lse*log2 e, delta); fp32 path [B, H, T] delta
+    float* ws;  // workspace: bf16 path [B, H, T] -lse*log2(e), then [B, H, T] -delta;
+                // fp32 path [B, H, T] delta
     int B, H, T, D;
     hipStream_t stream;
 };

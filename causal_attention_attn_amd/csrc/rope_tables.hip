@@ -32,17 +32,19 @@ hipError_t launch_rope_tables(float* cs, float* sn, int T, int D, double base, h
     return hipGetLastError();
 }
 
-// Rotate q and k once: out[0] = R q, out[1] = R k, both [B, H, T, D] fp16
-// (rounded once from the fp32 rotation). The bf16 kernels read these instead of
-// applying RoPE per tile. One thread per 8 consecutive features of one row,
-// for q and k together (one cos/sin read serves both).
+// Rotate q and k once: out[0] = qs * R q, out[1] = R k, both [B, H, T, D] fp16
+// (rounded once from the fp32 rotation). qs = log2(e)/sqrt(D) folds the score
+// scale and the change to base-2 exponentials into the query, so a score
+// product comes out of the MFMA directly as S * log2(e). The bf16 kernels read
+// these instead of applying RoPE per tile. One thread per 8 consecutive
+// features of one row, for q and k together (one cos/sin read serves both).
 template <int D>
 __global__ __launch_bounds__(256) void rotate_qk_kernel(const bf16* __restrict__ q,
                                                         const bf16* __restrict__ k,
                                                         const float* __restrict__ cs,
                                                         const float* __restrict__ sn,
                                                         f16* __restrict__ out, int T,
-                                                        int chunks) {
+                                                        int chunks, float qs) {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= chunks) return;
     constexpr int NC = D / 8;
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(256) void rotate_qk_kernel(const bf16* __restrict__
     for (int p = 0; p < 4; ++p) {
         const float q0 = bf16_lo(wq[p]), q1 = bf16_hi(wq[p]);
         const float k0 = bf16_lo(wk[p]), k1 = bf16_hi(wk[p]);
-        rq[p] = pack2<f16>(q0 * cv[p] - q1 * sv[p], q0 * sv[p] + q1 * cv[p]);
+        rq[p] = pack2<f16>((q0 * cv[p] - q1 * sv[p]) * qs, (q0 * sv[p] + q1 * cv[p]) * qs);
         rk[p] = pack2<f16>(k0 * cv[p] - k1 * sv[p], k0 * sv[p] + k1 * cv[p]);
     }
     *reinterpret_cast<u32x4*>(out + e0) = rq;
@@ -69,12 +71,13 @@ hipError_t launch_rotate_qk(const void* q, const void* k, const float* cs, const
                             void* out, int B, int H, int T, int D, hipStream_t st) {
     const int chunks = (int)((long)B * H * T * D / 8);
     const int blocks = (chunks + 255) / 256;
+    const float qs = kLog2e / sqrtf((float)D);
     if (D == 64)
         hipLaunchKernelGGL(rotate_qk_kernel<64>, dim3(blocks), dim3(256), 0, st, (const bf16*)q,
-                           (const bf16*)k, cs, sn, (f16*)out, T, chunks);
+                           (const bf16*)k, cs, sn, (f16*)out, T, chunks, qs);
     else
         hipLaunchKernelGGL(rotate_qk_kernel<128>, dim3(blocks), dim3(256), 0, st, (const bf16*)q,
-                           (const bf16*)k, cs, sn, (f16*)out, T, chunks);
+                           (const bf16*)k, cs, sn, (f16*)out, T, chunks, qs);
     return hipGetLastError();
 }
 

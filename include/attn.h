@@ -78,18 +78,21 @@ int attn_rope_tables(float* cos_tab, float* sin_tab, int T, int D, double base,
 
 /*
  * attn_saved_bytes - size of the "saved" buffer that attn_fwd fills and the
- * backward reads: for ATTN_BF16 the RoPE-rotated q and k, each [B,H,T,D] fp16
- * (4*B*H*T*D bytes, rounded up to 256); 0 for ATTN_F32, whose kernels rotate on
- * load. Returns 0 for arguments the other calls would reject.
+ * backward reads: for ATTN_BF16 the RoPE-rotated q (times log2(e)/sqrt(D)) and
+ * the RoPE-rotated k, each [B,H,T,D] fp16 (4*B*H*T*D bytes, rounded up to 256);
+ * 0 for ATTN_F32, whose kernels rotate on load. Returns 0 for arguments the
+ * other calls would reject.
  */
 size_t attn_saved_bytes(int B, int H, int T, int D, int dtype);
 
 /*
  * attn_rotate_qk - apply RoPE once ("Tiny Hackable CUDA", section 3): writes
- * R_t q_t then R_t k_t into `saved` ([2][B,H,T,D] fp16), each value rotated in
- * fp32 and rounded once to fp16. The rotated q and k are no longer bf16 values;
- * fp16's 11-bit significand keeps the score products accurate where the
- * softmax is sharp, and bounds |rotated q|, |rotated k| by 65504.
+ * c * R_t q_t, c = log2(e)/sqrt(D), then R_t k_t into `saved` ([2][B,H,T,D]
+ * fp16), each value rotated (and scaled) in fp32 and rounded once to fp16. The
+ * factor c makes a score product come out as S*log2(e), ready for base-2
+ * exponentials. The stored values are no longer bf16 values; fp16's 11-bit
+ * significand keeps the score products accurate where the softmax is sharp,
+ * and bounds |c R_t q_t| and |R_t k_t| by 65504.
  * For ATTN_F32 it does nothing and returns ATTN_OK.
  */
 int attn_rotate_qk(const void* q, const void* k, const float* cos_tab, const float* sin_tab,
@@ -124,10 +127,11 @@ int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void*
                      int B, int H, int T, int D, int dtype, void* stream);
 
 /*
- * attn_bwd_workspace_bytes - device workspace the backward needs: per row
- * (lse_t * log2 e, delta_t) as two fp32 for ATTN_BF16 (8*B*H*T bytes), or
- * delta_t alone for ATTN_F32 (4*B*H*T bytes), rounded up to 256, where
- * delta_t = sum_d dO[t,d] o[t,d]. Returns 0 for arguments attn_bwd would reject.
+ * attn_bwd_workspace_bytes - device workspace the backward needs: for
+ * ATTN_BF16 -lse_t * log2 e of every row ([B,H,T] fp32) followed by -delta_t
+ * of every row ([B,H,T] fp32), 8*B*H*T bytes; for ATTN_F32 delta_t alone
+ * (4*B*H*T bytes); rounded up to 256, where delta_t = sum_d dO[t,d] o[t,d].
+ * Returns 0 for arguments attn_bwd would reject.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype);
 
@@ -157,7 +161,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /*
  * attn_bwd_dq - first stage of attn_bwd: writes the per-row workspace entries
- * (delta_t = sum_d dO[t,d] o[t,d], and for ATTN_BF16 lse_t * log2 e) and dq
+ * (delta_t = sum_d dO[t,d] o[t,d], negated for ATTN_BF16, and there also
+ * -lse_t * log2 e) and dq
  * (gradient w.r.t. the pre-RoPE q). Same arguments and rules as attn_bwd,
  * minus dk and dv.
  */
