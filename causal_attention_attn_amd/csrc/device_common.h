@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 typedef __bf16 bf16;
 typedef _Float16 f16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -274,10 +276,20 @@ __device__ __forceinline__ void ring_barrier() {
 // load in flight before each operand read). k and v are the two 64-row tiles of
 // a stage, x an optional small extra block.
 struct Ring {
-    char* k[3];
-    char* v[3];
-    char* x[3];
+    char* k[8];
+    char* v[8];
+    char* x[8];
 };
+
+// Calls f(std::integral_constant<int, S>) for S = 0 .. N-1, in order.
+template <int N, typename F, int... S>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, S...>) {
+    (f(std::integral_constant<int, S>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
 // Swizzled 16-byte chunk position of chunk c in row r of a tile with D-element
 // (2*D-byte) rows. LDS serves 256 bytes per cycle: 16 lanes of a 16-byte read,

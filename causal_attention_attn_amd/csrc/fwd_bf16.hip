@@ -46,7 +46,7 @@ struct FwdTile {
     static constexpr int DB = D / 32;   // 32-row blocks of the head dimension
     static constexpr int NSB = BN / 32;
     static constexpr int TILE = BN * D * 2;            // bytes of one K or V tile
-    static constexpr int NS = D == 64 ? 3 : 2;         // LDS ring stages
+    static constexpr int NS = 3;                       // LDS ring stages
     static constexpr int LPT = 2 * TILE / 1024 / NW;   // load instructions per wave per tile
 };
 
@@ -93,41 +93,73 @@ __device__ __forceinline__ float fwd_probs(const f32x16* x, bf16x8 (*pb)[2], int
     return t;
 }
 
-// One 64-key tile for one wave. DIAG: the tile may reach this wave's diagonal,
-// so 32-key sub-blocks above it are skipped and the diagonal one is masked.
-//
-// The scores arrive in log2 units (the query carries log2(e)/sqrt(D)) with the
-// reference maximum already subtracted by the MFMA, x = S*log2(e) - m. The
-// online softmax needs no per-tile maximum while the probabilities stay
-// bounded: if every lane's sum of this tile's p = 2^x is at most 2^8, no single
-// x exceeds 8, so O and l may keep the reference m (the bound on unnormalised
-// probabilities is the same as a lazy rescale with threshold 8). Otherwise
-// (and on the wave's first tile, which sets m) the exact maximum is taken, O
-// and l are rescaled and the tile's probabilities are recomputed.
-template <int D, bool DIAG>
-__device__ __forceinline__ void fwd_tile(FwdState<D>& st, const f16x8* qf, const char* ks,
-                                         const char* vs, const OperandOffs<D>& of, int k0, int wq0,
-                                         int lane, bool first) {
+// K operands of one 64-key tile for this lane: the A operands of the two
+// 32-key score products, one per 16-wide chunk of the head dimension.
+template <int D>
+struct KOps {
+    f16x8 a[FwdTile<D>::NSB][FwdTile<D>::DK];
+};
+
+template <int D>
+__device__ __forceinline__ void read_k(KOps<D>& kr, const char* ks, const OperandOffs<D>& of) {
     using C = FwdTile<D>;
-    constexpr float kLimit = 256.f;
-    constexpr int ROWB = 2 * D;  // bytes per tile row
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+        for (int c = 0; c < C::DK; ++c)
+            kr.a[sb][c] = *reinterpret_cast<const f16x8*>(ks + 32 * sb * 2 * D + of.k[c]);
+}
+
+// Scores of one 64-key tile, x = S^T log2(e) - m (the query carries
+// log2(e)/sqrt(D) and -m is the initial accumulator). DIAG: 32-key blocks
+// above the wave's diagonal are skipped and the diagonal one is masked.
+template <int D, bool DIAG>
+__device__ __forceinline__ void fwd_scores(f32x16* x, const FwdState<D>& st, const f16x8* qf,
+                                           const KOps<D>& kr, int k0, int wq0, int lane) {
+    using C = FwdTile<D>;
     const int c32 = lane & 31, hf = lane >> 5;
-    if (DIAG && k0 > wq0) return;  // whole tile above this wave's diagonal
-    f32x16 x[C::NSB];
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
         if (DIAG && k0 + 32 * sb > wq0) break;
-        const char* kb = ks + 32 * sb * ROWB;
-        f32x16 acc = mfma32(*reinterpret_cast<const f16x8*>(kb + of.k[0]), qf[0], st.negm);
+        f32x16 acc = mfma32(kr.a[sb][0], qf[0], st.negm);
 #pragma unroll
-        for (int c = 1; c < C::DK; ++c)
-            acc = mfma32(*reinterpret_cast<const f16x8*>(kb + of.k[c]), qf[c], acc);
+        for (int c = 1; c < C::DK; ++c) acc = mfma32(kr.a[sb][c], qf[c], acc);
         x[sb] = acc;
         if (DIAG && k0 + 32 * sb == wq0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 if (item_row(i, hf) > c32) x[sb][i] = -INFINITY;
         }
+    }
+}
+
+// Online softmax and O^T += V^T P^T for one 64-key tile whose scores are x.
+//
+// The online softmax needs no per-tile maximum while the probabilities stay
+// bounded: if every lane's sum of this tile's p = 2^x is at most 2^8, no single
+// x exceeds 8, so O and l may keep the reference m (the bound on unnormalised
+// probabilities is the same as a lazy rescale with threshold 8). Otherwise
+// (and on the wave's first tile, which sets m) the exact maximum is taken, O
+// and l are rescaled and the tile's probabilities are recomputed. The V^T
+// operands are read from LDS first, so their latency overlaps the softmax.
+template <int D, bool DIAG>
+__device__ __forceinline__ void fwd_softmax_pv(FwdState<D>& st, f32x16* x, const char* vs,
+                                               const OperandOffs<D>& of, int k0, int wq0,
+                                               bool first) {
+    using C = FwdTile<D>;
+    constexpr float kLimit = 256.f;
+    constexpr int ROWB = 2 * D;
+    bf16x8 va[C::NSB][C::DB][2];
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+        if (DIAG && k0 + 32 * sb > wq0) break;
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const char* vb = vs + (32 * sb + 16 * j) * ROWB;
+                va[sb][b][j] = tr_pair<bf16x8>(vb + of.v[b][0], vb + of.v[b][1]);
+            }
     }
     bf16x8 pb[C::NSB][2];
     float ts = 0.f;
@@ -168,14 +200,9 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const f16x8* qf, const
     for (int sb = 0; sb < C::NSB; ++sb) {
         if (DIAG && k0 + 32 * sb > wq0) break;
 #pragma unroll
-        for (int b = 0; b < C::DB; ++b) {
+        for (int b = 0; b < C::DB; ++b)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const char* vb = vs + (32 * sb + 16 * j) * ROWB;
-                st.o[b] = mfma32(tr_pair<bf16x8>(vb + of.v[b][0], vb + of.v[b][1]), pb[sb][j],
-                                 st.o[b]);
-            }
-        }
+            for (int j = 0; j < 2; ++j) st.o[b] = mfma32(va[sb][b][j], pb[sb][j], st.o[b]);
     }
 }
 
@@ -187,21 +214,31 @@ struct FwdCtx {
     int T, wq0, lane, wave;
 };
 
-// Step n of the tile loop on ring stage STG (= n % NS): wait for tile n,
-// publish it, refill the stage freed by tile n-1 with tile n+NS-1, compute.
+// Step n of the tile loop; tile n sits in ring stage STG = n % NS and its K
+// operands are already in kr. Scores of tile n first; then wait for tile n+1,
+// publish it with the barrier (which also frees the stage of tile n-1, whose
+// last reads were made before it) and refill that stage with tile n+NS-1;
+// finish tile n (its V operands are read before the softmax, which hides their
+// latency) and read tile n+1's K operands while the PV products run.
 template <int D, int STG, bool DIAG>
-__device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, const Ring& rg,
-                                         const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
-                                         const FwdCtx<D>& x, int n) {
+__device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, KOps<D>& kr,
+                                         const Ring& rg, const TileLoads<D, 64, 4>& ld,
+                                         const OperandOffs<D>& of, const FwdCtx<D>& x, int n) {
     using C = FwdTile<D>;
     constexpr int NS = C::NS;
-    constexpr int NXT = (STG + NS - 1) % NS;
-    wait_vmcnt<C::LPT * (NS - 2)>();
+    constexpr int NXT = (STG + 1) % NS;
+    constexpr int FREE = (STG + NS - 1) % NS;
+    const int k0 = n * C::BN;
+    const bool live = !(DIAG && k0 > x.wq0);  // false: tile wholly above this wave's diagonal
+    f32x16 s[C::NSB];
+    if (live) fwd_scores<D, DIAG>(s, st, qf, kr, k0, x.wq0, x.lane);
+    wait_vmcnt<C::LPT * (NS - 3)>();
     ring_barrier();
     const int nx = n + NS - 1;
-    ld.issue(x.kr, x.T, nx * C::BN, rg.k[NXT], x.wave);
-    ld.issue(x.v, x.T, nx * C::BN, rg.v[NXT], x.wave);
-    fwd_tile<D, DIAG>(st, qf, rg.k[STG], rg.v[STG], of, n * C::BN, x.wq0, x.lane, n == 0);
+    ld.issue(x.kr, x.T, nx * C::BN, rg.k[FREE], x.wave);
+    ld.issue(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave);
+    if (live) fwd_softmax_pv<D, DIAG>(st, s, rg.v[STG], of, k0, x.wq0, n == 0);
+    read_k(kr, rg.k[NXT], of);
 }
 
 template <int D>
@@ -210,10 +247,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     bf16* __restrict__ o, float* __restrict__ lse, int BH, int T, int nqb) {
     using C = FwdTile<D>;
     constexpr int NS = C::NS;
-    constexpr int T3 = NS > 2 ? C::TILE : 1024;
-    __shared__ __attribute__((aligned(1024))) char k0[C::TILE], k1[C::TILE], k2[T3];
-    __shared__ __attribute__((aligned(1024))) char v0[C::TILE], v1[C::TILE], v2[T3];
-    const Ring rg = {{k0, k1, k2}, {v0, v1, v2}};
+    // one __shared__ object per ring stage (see Ring); stages >= NS are stubs
+#define ATTN_STAGE(i) \
+    __shared__ __attribute__((aligned(256))) char k##i[i < NS ? C::TILE : 16]; \
+    __shared__ __attribute__((aligned(256))) char v##i[i < NS ? C::TILE : 16];
+    ATTN_STAGE(0) ATTN_STAGE(1) ATTN_STAGE(2) ATTN_STAGE(3)
+    ATTN_STAGE(4) ATTN_STAGE(5) ATTN_STAGE(6) ATTN_STAGE(7)
+#undef ATTN_STAGE
+    const Ring rg = {{k0, k1, k2, k3, k4, k5, k6, k7}, {v0, v1, v2, v3, v4, v5, v6, v7}, {}};
 
     const int bid = blockIdx.x;
     const int bh = bid % BH;
@@ -253,19 +294,22 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     st.m = 0.f;
     st.l = 0.f;
 
+    // tile 0 published; its K operands in registers
+    wait_vmcnt<C::LPT * (NS - 2)>();
+    ring_barrier();
+    KOps<D> kops;
+    read_k(kops, rg.k[0], of);
+
     int n = 0;
     // full tiles: branch-free bodies, ring stages as compile-time constants
-    for (; n + NS <= nfull; n += NS) {
-        fwd_step<D, 0, false>(st, qf, rg, ld, of, x, n);
-        fwd_step<D, 1, false>(st, qf, rg, ld, of, x, n + 1);
-        if constexpr (NS > 2) fwd_step<D, 2, false>(st, qf, rg, ld, of, x, n + 2);
-    }
+    for (; n + NS <= nfull; n += NS)
+        static_for<NS>([&](auto S) { fwd_step<D, S, false>(st, qf, kops, rg, ld, of, x, n + S); });
     // the rest (at most NS-1 full tiles, then the diagonal tiles)
     for (; n < ntiles; ++n) {
         const int stg = n % NS;
-        if (stg == 0) fwd_step<D, 0, true>(st, qf, rg, ld, of, x, n);
-        else if (stg == 1) fwd_step<D, 1, true>(st, qf, rg, ld, of, x, n);
-        else if constexpr (NS > 2) fwd_step<D, 2, true>(st, qf, rg, ld, of, x, n);
+        static_for<NS>([&](auto S) {
+            if (stg == S) fwd_step<D, S, true>(st, qf, kops, rg, ld, of, x, n);
+        });
     }
     wait_vmcnt<0>();  // no LDS writes may land after this workgroup's LDS is released
 
