@@ -48,6 +48,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96,
                     help="heads of the workload the CPU oracle runs on")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes three times (the "
+                         "reference point that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -65,6 +68,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 3}), flush=True)
+        return
     attn.load()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -145,7 +156,8 @@ def main():
     ach = fl[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom, name)}
 
     cpu = None
     parity = None
@@ -174,6 +186,42 @@ def main():
         "parity": parity,
     }
     print(json.dumps(line), flush=True)
+
+
+# kernel -> the sources that define it; a traffic figure is valid only for these exact sources
+KERNEL_SOURCES = {
+    "fwd_kernel": ["fwd_bf16.hip", "device_common.h"],
+    "dq_kernel": ["bwd_bf16.hip", "device_common.h"],
+    "dkdv_kernel": ["bwd_bf16.hip", "device_common.h"],
+    "rotate_kernel": ["rope_tables.hip", "device_common.h"],
+}
+
+
+def sources_sha256(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "causal_attention_attn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/hbm_traffic_<kernel>_<workload>.md, FETCH_SIZE + WRITE_SIZE scaled
+    by a plain copy of known size), or None when there is none or the kernel's
+    sources changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic-record:"):
+                rec = json.loads(line.split(":", 1)[1])
+    if not rec or rec.get("src_sha256") != sources_sha256(kernel):
+        return None
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(w, x, gpu_out, heads):

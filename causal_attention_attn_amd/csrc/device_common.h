@@ -1,5 +1,6 @@
 // Device-side helpers shared by the gfx950 attention kernels: vector types,
-// MFMA wrappers, 16-bit packing, the RoPE-on-load loader and LDS tile staging.
+// MFMA wrappers, 16-bit packing, lane exchanges, buffer resources, and the
+// direct-to-LDS tile ring with its swizzled operand reads.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -72,22 +73,8 @@ template <typename V>
 __device__ __forceinline__ V as_vec8(u32x4 w) { return __builtin_bit_cast(V, w); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-template <typename T> struct Vec8;
-template <> struct Vec8<bf16> { typedef bf16x8 type; };
-template <> struct Vec8<f16> { typedef f16x8 type; };
-
 // Row (0..31) of the 32x32 MFMA result held in item i of lane half h.
 __device__ __forceinline__ int item_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
-
-// Column order of transposed LDS tiles. Items 8j..8j+7 of a lane half h of a
-// 32x32 result (rows 16j + 8g + 4h + i, g = 0..1, i = 0..3) are the B operand of
-// a following MFMA that contracts over those rows. Storing row u of the
-// contraction at column col_perm(u) (bits 2 and 3 swapped) puts those eight rows
-// at columns 16j + 8h .. 16j + 8h + 7, so the matching A operand is one 16-byte
-// LDS read.
-__device__ __forceinline__ int col_perm(int u) {
-    return (u & ~12) | ((u & 4) << 1) | ((u & 8) >> 1);
-}
 
 }  // namespace attn
 
@@ -113,128 +100,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
-__device__ __forceinline__ f32x4 buf_load_f4(rsrc_t r, uint32_t byte_off) {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-
-// Buffers of one [T, D] bf16 head and of the [T, D/2] fp32 RoPE tables.
-template <int D>
-struct HeadBufs {
-    rsrc_t x, c, s;
-    __device__ __forceinline__ HeadBufs(const bf16* head, const float* cs, const float* sn,
-                                        int T)
-        : x(make_rsrc(head, (uint32_t)T * D * 2)),
-          c(make_rsrc(cs, (uint32_t)T * (D / 2) * 4)),
-          s(make_rsrc(sn, (uint32_t)T * (D / 2) * 4)) {}
-};
-
-// Eight features d0 .. d0+7 of row t (zeros past the end), rotated by R_t in
-// fp32 and rounded once to the 16-bit type T: pair p -> (x0 c - x1 s, x0 s + x1 c).
-template <int D, typename T>
-__device__ __forceinline__ typename Vec8<T>::type rope_operand(const HeadBufs<D>& hb, int t,
-                                                               int d0) {
-    const u32x4 w = buf_load16(hb.x, (uint32_t)(t * D + d0) * 2);
-    const f32x4 c = buf_load_f4(hb.c, (uint32_t)(t * (D / 2) + d0 / 2) * 4);
-    const f32x4 s = buf_load_f4(hb.s, (uint32_t)(t * (D / 2) + d0 / 2) * 4);
-    u32x4 r;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const float x0 = bf16_lo(w[p]), x1 = bf16_hi(w[p]);
-        r[p] = pack2<T>(x0 * c[p] - x1 * s[p], x0 * s[p] + x1 * c[p]);
-    }
-    return as_vec8<typename Vec8<T>::type>(r);
-}
-
-// Register-staged copy of rows [r0, r0 + ROWS) of a head, loaded by NT threads
-// in units of two rows x 8 features (consecutive lanes take consecutive 16-byte
-// pieces of a row, so eight lanes read one 128-byte row). load() issues the global reads (and, with
-// ROT, those of the matching cos/sin entries) so they can complete while the
-// caller computes; store() then rotates by RoPE in fp32 (if ROT), rounds once
-// and writes a row-major copy rm[ROWS][D + 8] of type RM and/or a transposed
-// copy tr[D][ROWS + 8] of type TR (void = not written) whose columns follow
-// col_perm. Rows at or beyond T read as zeros.
-template <int D, int ROWS, int NT, bool ROT>
-struct RowStage {
-    static constexpr int UNITS = (ROWS / 2) * (D / 8);
-    static constexpr int U = UNITS / NT;
-    static_assert(UNITS % NT == 0, "tile units must divide evenly among threads");
-    u32x4 a[U], b[U];
-    f32x4 ca[U], sa[U], cb[U], sb[U];
-
-    __device__ __forceinline__ void load(const HeadBufs<D>& hb, int r0, int tid) {
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const int u = j * NT + tid;
-            const int dc = u % (D / 8), kp = u / (D / 8);
-            const int ra = r0 + 2 * kp;
-            a[j] = buf_load16(hb.x, (uint32_t)(ra * D + 8 * dc) * 2);
-            b[j] = buf_load16(hb.x, (uint32_t)((ra + 1) * D + 8 * dc) * 2);
-            if constexpr (ROT) {
-                ca[j] = buf_load_f4(hb.c, (uint32_t)(ra * (D / 2) + 4 * dc) * 4);
-                sa[j] = buf_load_f4(hb.s, (uint32_t)(ra * (D / 2) + 4 * dc) * 4);
-                cb[j] = buf_load_f4(hb.c, (uint32_t)((ra + 1) * (D / 2) + 4 * dc) * 4);
-                sb[j] = buf_load_f4(hb.s, (uint32_t)((ra + 1) * (D / 2) + 4 * dc) * 4);
-            }
-        }
-    }
-
-    template <typename RM, typename TR>
-    __device__ __forceinline__ void store(void* rm_, void* tr_, int tid) const {
-        constexpr bool HAS_RM = !__is_same(RM, void), HAS_TR = !__is_same(TR, void);
-        constexpr int RS = D + 8, TS = ROWS + 8;
-        uint16_t* rm = static_cast<uint16_t*>(rm_);
-        uint16_t* tr = static_cast<uint16_t*>(tr_);
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const int u = j * NT + tid;
-            const int dc = u % (D / 8), kp = u / (D / 8);
-            u32x4 a_rm, b_rm;
-            uint32_t t_w[8];
-            if constexpr (ROT) {
-                float fa[8], fb[8];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float a0 = bf16_lo(a[j][p]), a1 = bf16_hi(a[j][p]);
-                    const float b0 = bf16_lo(b[j][p]), b1 = bf16_hi(b[j][p]);
-                    fa[2 * p] = a0 * ca[j][p] - a1 * sa[j][p];
-                    fa[2 * p + 1] = a0 * sa[j][p] + a1 * ca[j][p];
-                    fb[2 * p] = b0 * cb[j][p] - b1 * sb[j][p];
-                    fb[2 * p + 1] = b0 * sb[j][p] + b1 * cb[j][p];
-                }
-                if constexpr (HAS_RM) {
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        a_rm[p] = pack2<RM>(fa[2 * p], fa[2 * p + 1]);
-                        b_rm[p] = pack2<RM>(fb[2 * p], fb[2 * p + 1]);
-                    }
-                }
-                if constexpr (HAS_TR) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) t_w[e] = pack2<TR>(fa[e], fb[e]);
-                }
-            } else {
-                a_rm = a[j];
-                b_rm = b[j];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    t_w[2 * e] = (a[j][e] & 0xffffu) | (b[j][e] << 16);
-                    t_w[2 * e + 1] = (a[j][e] >> 16) | (b[j][e] & 0xffff0000u);
-                }
-            }
-            if constexpr (HAS_RM) {
-                *reinterpret_cast<u32x4*>(rm + (2 * kp) * RS + 8 * dc) = a_rm;
-                *reinterpret_cast<u32x4*>(rm + (2 * kp + 1) * RS + 8 * dc) = b_rm;
-            }
-            if constexpr (HAS_TR) {
-                const int col = col_perm(2 * kp);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    *reinterpret_cast<uint32_t*>(tr + (8 * dc + e) * TS + col) = t_w[e];
-            }
-        }
-    }
-};
-
 }  // namespace attn
 
 namespace attn {
@@ -345,38 +210,11 @@ struct TileLoads {
     }
 };
 
-// 8 consecutive 16-bit values of row r starting at column col (a multiple of 8).
-template <int D, typename V>
-__device__ __forceinline__ V lds_row8(const char* tile, int r, int col) {
-    return *reinterpret_cast<const V*>(tile + tile_off<D>(r, col));
-}
-
-// A operand X^T for a 32x32x16 MFMA from a row-major tile X[rows][D]:
-// lane (c = lane & 31, h = lane >> 5) receives X[row0 + 8*(i>>2) + 4h + (i&3)][col0 + c]
-// for items i = 0..7 - the row order of the items of a 32x32 result (item i of
-// lane half h is row 8*(i>>2) + 4h + (i&3)), so that rounded result items can be
-// the B operand. Two ds_read_b64_tr_b16: within each 16-lane group, lane m gets
-// element m&3 of the 8-byte reads of lanes 4j + (m>>2), j = 0..3.
-template <int D, typename V>
-__device__ __forceinline__ V lds_tr8(const char* tile, int row0, int col0, int lane) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    const int g = lane >> 4, m = lane & 15;
-    const int row = row0 + 4 * (g >> 1) + (m >> 2);
-    const int col = col0 + 16 * (g & 1) + 4 * (m & 3);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(tile + tile_off<D>(row, col)));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(tile + tile_off<D>(row + 8, col)));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(V, r);
-}
-
 // Byte offsets, inside a tile, of this lane's operand reads (see tile_off):
 // k[c]     the row operand (A of a 32x32x16 MFMA contracting over the head
 //          dimension) for head-dimension chunk c, row = lane & 31;
 // v[b][h]  the two transpose reads of an X^T operand (A of an MFMA contracting
-//          over tile rows) for head-dimension block b, see lds_tr8.
+//          over tile rows) for head-dimension block b, see tr_pair.
 // Moving 16 or 32 rows down a tile leaves the swizzle unchanged, so the other
 // 16-key chunks and 32-key sub-blocks are these offsets plus a constant.
 template <int D>
@@ -397,6 +235,13 @@ struct OperandOffs {
     }
 };
 
+// A operand X^T for a 32x32x16 MFMA from a row-major tile X[rows][D], read at
+// the two OperandOffs::v offsets of a block: lane (c = lane & 31, h = lane >> 5)
+// receives X[8*(i>>2) + 4h + (i&3)][c] for items i = 0..7 (rows relative to the
+// 16-row chunk, columns to the 32-wide block) - the row order of the items of a
+// 32x32 result, so that rounded result items can be the B operand. Two
+// ds_read_b64_tr_b16: within each 16-lane group, lane m gets element m&3 of the
+// 8-byte reads of lanes 4j + (m>>2), j = 0..3.
 template <typename V>
 __device__ __forceinline__ V tr_pair(const char* lo, const char* hi) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
