@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "attn.h"
 #include "launchers.h"
@@ -99,6 +100,22 @@ attn::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* 
 }
 
 }  // namespace
+
+namespace attn {
+
+int device_cu_count() {
+    static std::mutex mu;
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0 &&
+        hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus[dev] = 0;
+    return cus[dev];
+}
+
+}  // namespace attn
 
 extern "C" {
 

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
     const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
     const bf16* __restrict__ o, const bf16* __restrict__ dO, const float* __restrict__ lse,
     const float* __restrict__ cs, const float* __restrict__ sn, bf16* __restrict__ dq,
-    float* __restrict__ ws, int BH, int T, int nqb, float scale) {
+    float* __restrict__ ws, int BH, int T, int nqb, float scale, int ncu) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int T3 = NS > 2 ? C::TILE : 1024;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) char v0[C::TILE], v1[C::TILE], v2[T3];
     const Ring rg = {{k0, k1, k2}, {v0, v1, v2}, {nullptr, nullptr, nullptr}};
 
-    const int bid = blockIdx.x;
+    const int bid = snake_item(blockIdx.x, ncu, nqb * BH);
     const int bh = bid % BH;
     const int qb = nqb - 1 - bid / BH;
     const int q0 = qb * C::QM;
@@ -211,13 +211,23 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
         bf16* out = dq + hoff + (size_t)tq * D;
         const float* crow = cs + (size_t)tq * (D / 2);
         const float* srow = sn + (size_t)tq * (D / 2);
+        // every table load before the first store (see the dk/dv epilogue)
+        f32x2 c2s[C::DB][4], s2s[C::DB][4];
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * b + 8 * g + 4 * hf;
+                c2s[b][g] = *reinterpret_cast<const f32x2*>(crow + d / 2);
+                s2s[b][g] = *reinterpret_cast<const f32x2*>(srow + d / 2);
+            }
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = 32 * b + 8 * g + 4 * hf;
-                const f32x2 c2 = *reinterpret_cast<const f32x2*>(crow + d / 2);
-                const f32x2 s2 = *reinterpret_cast<const f32x2*>(srow + d / 2);
+                const f32x2 c2 = c2s[b][g], s2 = s2s[b][g];
                 u32x2 w;
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
@@ -346,7 +356,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
     const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ ws, const float* __restrict__ cs,
     const float* __restrict__ sn, bf16* __restrict__ dk, bf16* __restrict__ dv, int BH, int T,
-    int nkb, float scale) {
+    int nkb, float scale, int ncu) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int T3 = NS > 2 ? C::TILE : 1024;
@@ -355,7 +365,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
     __shared__ __attribute__((aligned(512))) char l0s[512], l1s[512], l2s[512];
     const Ring rg = {{q0s, q1s, q2s}, {g0s, g1s, g2s}, {l0s, l1s, l2s}};
 
-    const int bid = blockIdx.x;
+    const int bid = snake_item(blockIdx.x, ncu, nkb * BH);
     const int bh = bid % BH;
     const int kb = bid / BH;  // key block 0 has the most query tiles: issued first
     const int k0 = kb * C::KM;
@@ -422,13 +432,25 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
         bf16* vo = dv + hoff + (size_t)tk * D;
         const float* crow = cs + (size_t)tk * (D / 2);
         const float* srow = sn + (size_t)tk * (D / 2);
+        // every table load before the first store: on this GPU stores count in
+        // vmcnt too, so a load issued after a store could only be waited for
+        // together with that store
+        f32x2 c2s[C::DB][4], s2s[C::DB][4];
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * b + 8 * g + 4 * hf;
+                c2s[b][g] = *reinterpret_cast<const f32x2*>(crow + d / 2);
+                s2s[b][g] = *reinterpret_cast<const f32x2*>(srow + d / 2);
+            }
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = 32 * b + 8 * g + 4 * hf;
-                const f32x2 c2 = *reinterpret_cast<const f32x2*>(crow + d / 2);
-                const f32x2 s2 = *reinterpret_cast<const f32x2*>(srow + d / 2);
+                const f32x2 c2 = c2s[b][g], s2 = s2s[b][g];
                 u32x2 wk, wv;
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
@@ -454,7 +476,7 @@ static hipError_t launch_dq(const BwdArgs& a) {
     const f16* rot = static_cast<const f16*>(a.rot);
     hipLaunchKernelGGL(bwd_dq_bf16_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream, rot,
                        rot + n, (const bf16*)a.v, (const bf16*)a.o, (const bf16*)a.dO, a.lse,
-                       a.cs, a.sn, (bf16*)a.dq, a.ws, BH, a.T, nqb, scale);
+                       a.cs, a.sn, (bf16*)a.dq, a.ws, BH, a.T, nqb, scale, device_cu_count());
     return hipGetLastError();
 }
 
@@ -467,7 +489,7 @@ static hipError_t launch_dkdv(const BwdArgs& a) {
     const f16* rot = static_cast<const f16*>(a.rot);
     hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<D>, dim3(nkb * BH), dim3(C::NT), 0, a.stream, rot,
                        rot + n, (const bf16*)a.v, (const bf16*)a.dO, a.ws, a.cs, a.sn,
-                       (bf16*)a.dk, (bf16*)a.dv, BH, a.T, nkb, kLn2);
+                       (bf16*)a.dk, (bf16*)a.dv, BH, a.T, nkb, kLn2, device_cu_count());
     return hipGetLastError();
 }
 

@@ -55,6 +55,22 @@ __device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
                                            __builtin_bit_cast(b2, 0x3f803f80u), acc, false);
 }
 
+// Work item of workgroup `bid` when items are numbered heaviest first and the
+// dispatcher hands workgroups to the ncu CUs in rounds (workgroup r*ncu + c
+// lands on CU c in round r). Odd rounds take their items in reverse, so a CU
+// that received a heavy item in one round receives a light one in the next
+// and the per-CU sums of work even out. The reversal moves whole groups of 8
+// workgroups, so item i still runs on XCD i mod 8 (the round-robin XCD of its
+// workgroup id), which keeps one head's items on one L2 when the head count is
+// a multiple of 8. Incomplete rounds, or CU counts that are not a multiple of
+// 8, keep the identity order.
+__device__ __forceinline__ int snake_item(int bid, int ncu, int n_items) {
+    if (ncu <= 0 || (ncu & 7)) return bid;
+    const int r = bid / ncu, c = bid - r * ncu;
+    if (!(r & 1) || (r + 1) * ncu > n_items) return bid;
+    return r * ncu + (((ncu >> 3) - 1 - (c >> 3)) << 3) + (c & 7);
+}
+
 // True on every lane when the predicate holds on any active lane of the wave.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 

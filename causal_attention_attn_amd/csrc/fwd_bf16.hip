@@ -244,7 +244,7 @@ __device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, KOps<
 template <int D>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
-    bf16* __restrict__ o, float* __restrict__ lse, int BH, int T, int nqb) {
+    bf16* __restrict__ o, float* __restrict__ lse, int BH, int T, int nqb, int ncu) {
     using C = FwdTile<D>;
     constexpr int NS = C::NS;
     // one __shared__ object per ring stage (see Ring); stages >= NS are stubs
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
 #undef ATTN_STAGE
     const Ring rg = {{k0, k1, k2, k3, k4, k5, k6, k7}, {v0, v1, v2, v3, v4, v5, v6, v7}, {}};
 
-    const int bid = blockIdx.x;
+    const int bid = snake_item(blockIdx.x, ncu, nqb * BH);
     const int bh = bid % BH;
     const int qb = nqb - 1 - bid / BH;
     const int q0 = qb * C::BM;
@@ -339,7 +339,8 @@ static hipError_t launch_fwd(const FwdArgs& a) {
     const size_t n = (size_t)a.B * a.H * a.T * a.D;
     const f16* rot = static_cast<const f16*>(a.rot);
     hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream, rot,
-                       rot + n, (const bf16*)a.v, (bf16*)a.o, a.lse, BH, a.T, nqb);
+                       rot + n, (const bf16*)a.v, (bf16*)a.o, a.lse, BH, a.T, nqb,
+                       device_cu_count());
     return hipGetLastError();
 }
 

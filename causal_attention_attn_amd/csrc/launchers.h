@@ -28,6 +28,9 @@ struct BwdArgs {
     hipStream_t stream;
 };
 
+// Compute units of the current device (cached per device; 0 if HIP cannot say).
+int device_cu_count();
+
 hipError_t launch_rope_tables(float* cs, float* sn, int T, int D, double base, hipStream_t s);
 hipError_t launch_rotate_qk(const void* q, const void* k, const float* cs, const float* sn,
                             void* out, int B, int H, int T, int D, hipStream_t s);
