@@ -3,8 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step = one forward (attn_rotate_qk then attn_fwd_rotated, which is
-exactly what attn_fwd enqueues) and one backward (attn_bwd_dq then
-attn_bwd_dkdv, which is exactly what attn_bwd enqueues) over one batch of
+exactly what attn_fwd enqueues) and one backward (attn_bwd_prep then
+attn_bwd_grads, which is exactly what attn_bwd enqueues) over one batch of
 synthetic input already resident in HBM; the RoPE tables are built before the
 timed region (they depend only on T, D and the base, like weights). Throughput
 uses the causal FLOP convention: forward 2*B*H*T^2*D, backward 2.5x forward.
@@ -34,9 +34,10 @@ PEAK_HBM_GBS = 8000.0
 def causal_flops(B, H, T, D):
     unit = float(B) * H * T * T * D          # one causal product: 2 * (T^2/2) * D per head
     return {"fwd": 2 * unit, "bwd": 5 * unit,
-            # products each kernel evaluates on the causal half (its own algorithmic work)
-            "rotate_kernel": 0.0, "fwd_kernel": 2 * unit, "dq_kernel": 3 * unit,
-            "dkdv_kernel": 4 * unit}
+            # products each kernel evaluates on the causal half (its own algorithmic work):
+            # the gradient kernel recomputes S and dP for dq and again for dk/dv (3 + 4)
+            "rotate_kernel": 0.0, "fwd_kernel": 2 * unit, "bwd_prep_kernel": 0.0,
+            "bwd_grads_kernel": 7 * unit}
 
 
 def main():
@@ -108,15 +109,15 @@ def main():
     def fwd():
         attn.attn_fwd_rotated(saved, nsv, v, o, lse, B, H, T, D, dt, sh)
 
-    def bwd_dq():
-        attn.attn_bwd_dq(q, k, v, o, do, lse, cs, sn, saved, nsv, dq, ws, wsb, B, H, T, D, dt, sh)
+    def bwd_prep():
+        attn.attn_bwd_prep(o, do, lse, ws, wsb, B, H, T, D, dt, sh)
 
-    def bwd_dkdv():
-        attn.attn_bwd_dkdv(q, k, v, do, lse, cs, sn, saved, nsv, dk, dv, ws, wsb, B, H, T, D, dt,
-                           sh)
+    def bwd_grads():
+        attn.attn_bwd_grads(q, k, v, do, lse, cs, sn, saved, nsv, dq, dk, dv, ws, wsb, B, H, T,
+                            D, dt, sh)
 
     for _ in range(args.warmup):
-        rotate(); fwd(); bwd_dq(); bwd_dkdv()
+        rotate(); fwd(); bwd_prep(); bwd_grads()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -129,15 +130,16 @@ def main():
         e = ev[i]
         e[0].record(stream); rotate()
         e[1].record(stream); fwd()
-        e[2].record(stream); bwd_dq()
-        e[3].record(stream); bwd_dkdv()
+        e[2].record(stream); bwd_prep()
+        e[3].record(stream); bwd_grads()
         e[4].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / K
     per = {n: np.array([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)])
-           for j, n in enumerate(("rotate_kernel", "fwd_kernel", "dq_kernel", "dkdv_kernel"))}
+           for j, n in enumerate(("rotate_kernel", "fwd_kernel", "bwd_prep_kernel",
+                                  "bwd_grads_kernel"))}
     print(f"# timed {K} steps in {wall:.3f} s wall", file=sys.stderr, flush=True)
 
     fl = causal_flops(B, H, T, D)
@@ -149,9 +151,12 @@ def main():
         kernels[n] = {"avg_us": round(ms * 1e3, 2), "p10_us": round(float(np.percentile(arr, 10)) * 1e3, 2),
                       "p90_us": round(float(np.percentile(arr, 90)) * 1e3, 2),
                       "tflops": round(fl[n] / (ms * 1e-3) / 1e12, 1)}
-    # the rotation pass is memory-bound: q and k read (bf16), rotated q and k written (fp16)
+    # the memory-bound passes: rotation reads q, k (bf16) and writes q', k' (fp16); the
+    # backward pre-pass reads o, dO (bf16) and lse and writes two fp32 per row
     rot_bytes = 2 * (2 + 2) * B * H * T * D
-    kernels["rotate_kernel"]["gbs"] = round(rot_bytes / (kernels["rotate_kernel"]["avg_us"] * 1e-6) / 1e9, 1)
+    prep_bytes = 2 * 2 * B * H * T * D + 4 * B * H * T + 8 * B * H * T
+    for n, nb in (("rotate_kernel", rot_bytes), ("bwd_prep_kernel", prep_bytes)):
+        kernels[n]["gbs"] = round(nb / (kernels[n]["avg_us"] * 1e-6) / 1e9, 1)
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
     ach = fl[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
@@ -191,8 +196,8 @@ def main():
 # kernel -> the sources that define it; a traffic figure is valid only for these exact sources
 KERNEL_SOURCES = {
     "fwd_kernel": ["fwd_bf16.hip", "device_common.h"],
-    "dq_kernel": ["bwd_bf16.hip", "device_common.h"],
-    "dkdv_kernel": ["bwd_bf16.hip", "device_common.h"],
+    "bwd_grads_kernel": ["bwd_bf16.hip", "device_common.h"],
+    "bwd_prep_kernel": ["bwd_prep.hip", "device_common.h"],
     "rotate_kernel": ["rope_tables.hip", "device_common.h"],
 }
 

@@ -11,8 +11,8 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     AttnError,
     attn_bwd,
-    attn_bwd_dkdv,
-    attn_bwd_dq,
+    attn_bwd_grads,
+    attn_bwd_prep,
     attn_bwd_workspace_bytes,
     attn_fwd,
     attn_fwd_rotated,

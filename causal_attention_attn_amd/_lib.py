@@ -34,10 +34,9 @@ _SIGS = {
     "attn_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _P, _Z,
                       _I, _I, _I, _I, _I, _P]),
-    "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _Z,
-                         _I, _I, _I, _I, _I, _P]),
-    "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _Z,
-                           _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_prep": (_I, [_P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_grads": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _P, _Z,
+                            _I, _I, _I, _I, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
 }
@@ -133,18 +132,16 @@ def attn_bwd(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, dk, 
           _ptr(workspace), int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
 
 
-def attn_bwd_dq(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, workspace,
-                workspace_bytes, B, H, T, D, dtype, stream=None):
-    _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
-          _ptr(cos_tab), _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dq),
+def attn_bwd_prep(o, dO, lse, workspace, workspace_bytes, B, H, T, D, dtype, stream=None):
+    _call("attn_bwd_prep", _ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+          B, H, T, D, dtype, _stream(stream))
+
+
+def attn_bwd_grads(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, dk, dv,
+                   workspace, workspace_bytes, B, H, T, D, dtype, stream=None):
+    _call("attn_bwd_grads", _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(cos_tab),
+          _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dq), _ptr(dk), _ptr(dv),
           _ptr(workspace), int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
-
-
-def attn_bwd_dkdv(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dk, dv, workspace,
-                  workspace_bytes, B, H, T, D, dtype, stream=None):
-    _call("attn_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(cos_tab),
-          _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dk), _ptr(dv), _ptr(workspace),
-          int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
 
 
 def attn_status_string(status):

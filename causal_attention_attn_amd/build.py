@@ -11,7 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.hip", "rope_tables.hip", "fwd_bf16.hip", "bwd_bf16.hip", "attn_f32.hip"]
+SOURCES = ["api.hip", "rope_tables.hip", "fwd_bf16.hip", "bwd_prep.hip", "bwd_bf16.hip",
+           "attn_f32.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are switched off for every device pass; hipcc's host

@@ -195,39 +195,41 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype) {
     return workspace_need(B, H, T, dtype);
 }
 
-int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                const float* lse, const float* cos_tab, const float* sin_tab, const void* saved,
-                size_t saved_bytes, void* dq, void* workspace, size_t workspace_bytes, int B,
-                int H, int T, int D, int dtype, void* stream) {
-    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, workspace,
-                       workspace_bytes, B, H, T, D, dtype);
+int attn_bwd_prep(const void* o, const void* dO, const float* lse, void* workspace,
+                  size_t workspace_bytes, int B, int H, int T, int D, int dtype, void* stream) {
+    int st = check_shape(B, H, T, D, dtype);
     if (st) return st;
-    st = check_ptrs({o, dq});
+    st = check_ptrs({o, dO, lse});
     if (st) return st;
-    if (any_alias({dq, workspace}, {q, k, v, o, dO, lse, cos_tab, sin_tab, saved}))
-        return ATTN_ERR_ALIAS;
-    const attn::BwdArgs a = bwd_args(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, dq, nullptr,
-                                     nullptr, workspace, B, H, T, D, stream);
-    return hip_status(dtype == ATTN_BF16 ? attn::launch_bwd_dq_bf16(a)
-                                         : attn::launch_bwd_dq_f32(a));
+    if (workspace == nullptr || workspace_bytes < workspace_need(B, H, T, dtype))
+        return ATTN_ERR_WORKSPACE;
+    if (misaligned(workspace)) return ATTN_ERR_ALIGN;
+    if (any_alias({workspace}, {o, dO, lse})) return ATTN_ERR_ALIAS;
+    const attn::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr,
+                                     nullptr, nullptr, nullptr, nullptr, workspace, B, H, T, D,
+                                     stream);
+    return hip_status(dtype == ATTN_BF16 ? attn::launch_bwd_prep_bf16(a)
+                                         : attn::launch_bwd_prep_f32(a));
 }
 
-int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
-                  const float* lse, const float* cos_tab, const float* sin_tab,
-                  const void* saved, size_t saved_bytes, void* dk, void* dv,
-                  const void* workspace, size_t workspace_bytes, int B, int H, int T, int D,
-                  int dtype, void* stream) {
+int attn_bwd_grads(const void* q, const void* k, const void* v, const void* dO,
+                   const float* lse, const float* cos_tab, const float* sin_tab,
+                   const void* saved, size_t saved_bytes, void* dq, void* dk, void* dv,
+                   const void* workspace, size_t workspace_bytes, int B, int H, int T, int D,
+                   int dtype, void* stream) {
     int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, workspace,
                        workspace_bytes, B, H, T, D, dtype);
     if (st) return st;
-    st = check_ptrs({dk, dv});
+    st = check_ptrs({dq, dk, dv});
     if (st) return st;
-    if (any_alias({dk, dv}, {q, k, v, dO, lse, cos_tab, sin_tab, saved, workspace}))
+    if (any_alias({dq, dk, dv}, {q, k, v, dO, lse, cos_tab, sin_tab, saved, workspace}))
         return ATTN_ERR_ALIAS;
-    const attn::BwdArgs a = bwd_args(q, k, v, nullptr, dO, lse, cos_tab, sin_tab, saved, nullptr,
-                                     dk, dv, workspace, B, H, T, D, stream);
-    return hip_status(dtype == ATTN_BF16 ? attn::launch_bwd_dkdv_bf16(a)
-                                         : attn::launch_bwd_dkdv_f32(a));
+    const attn::BwdArgs a = bwd_args(q, k, v, nullptr, dO, lse, cos_tab, sin_tab, saved, dq, dk,
+                                     dv, workspace, B, H, T, D, stream);
+    if (dtype == ATTN_BF16) return hip_status(attn::launch_bwd_grads_bf16(a));
+    st = hip_status(attn::launch_bwd_dq_f32(a));
+    if (st) return st;
+    return hip_status(attn::launch_bwd_dkdv_f32(a));
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -241,11 +243,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     if (st) return st;
     if (any_alias({dq, dk, dv, workspace}, {q, k, v, o, dO, lse, cos_tab, sin_tab, saved}))
         return ATTN_ERR_ALIAS;
-    st = attn_bwd_dq(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, workspace,
-                     workspace_bytes, B, H, T, D, dtype, stream);
+    st = attn_bwd_prep(o, dO, lse, workspace, workspace_bytes, B, H, T, D, dtype, stream);
     if (st) return st;
-    return attn_bwd_dkdv(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dk, dv,
-                         workspace, workspace_bytes, B, H, T, D, dtype, stream);
+    return attn_bwd_grads(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, dk, dv,
+                          workspace, workspace_bytes, B, H, T, D, dtype, stream);
 }
 
 const char* attn_status_string(int status) {

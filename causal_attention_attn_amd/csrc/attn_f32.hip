@@ -2,8 +2,8 @@
 //
 // Same method as the bf16 kernels - RoPE applied on load, FlashAttention-style
 // online softmax over LDS key tiles with causal tile skipping, and a
-// recompute-based backward split into a dq kernel (which also writes
-// delta_t = sum_d dO o) and a dk/dv kernel - but evaluated with fp32 VALU
+// recompute-based backward split into a dq kernel and a dk/dv kernel, both
+// reading delta_t = sum_d dO o from the pre-pass - but evaluated with fp32 VALU
 // arithmetic throughout, so that no value is ever rounded to a 16-bit type.
 // This path serves fp32 callers and small shapes; it is not tuned for speed.
 //
@@ -186,9 +186,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ o, const float* __restrict__ dO, const float* __restrict__ lse,
+    const float* __restrict__ dO, const float* __restrict__ lse,
     const float* __restrict__ cs, const float* __restrict__ sn, float* __restrict__ dq,
-    float* __restrict__ delta, int BH, int T, int nqb, float sc, float scale) {
+    const float* __restrict__ delta, int BH, int T, int nqb, float sc, float scale) {
     using C = F32Tile<D>;
     __shared__ __attribute__((aligned(16))) float Ks[C::BN * D];
     __shared__ __attribute__((aligned(16))) float Vs[C::BN * D];
@@ -203,16 +203,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
     float qr[32], g[32], acc[32];
     load32<D, true>(q + hoff, t, d0, T, cs, sn, qr);
     load32<D, false>(dO + hoff, t, d0, T, cs, sn, g);
-    {
-        float ov[32];
-        load32<D, false>(o + hoff, t, d0, T, cs, sn, ov);
-        float part = 0.f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) part = fmaf(g[i], ov[i], part);
-        acc[0] = row_sum<C::LPR>(part);
-    }
-    const float dl = acc[0];
-    if (t < T && d0 == 0) delta[(size_t)bh * T + t] = dl;
+    const float dl = t < T ? delta[(size_t)bh * T + t] : 0.f;  // from the pre-pass
     const float lt = t < T ? lse[(size_t)bh * T + t] * kLog2e : 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = 0.f;
@@ -319,7 +310,7 @@ static hipError_t launch_dq32(const BwdArgs& a) {
     const float scale = 1.f / sqrtf((float)D);
     hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                       (const float*)a.o, (const float*)a.dO, a.lse, a.cs, a.sn, (float*)a.dq,
+                       (const float*)a.dO, a.lse, a.cs, a.sn, (float*)a.dq,
                        a.ws, BH, a.T, nqb, scale * kLog2e, scale);
     return hipGetLastError();
 }

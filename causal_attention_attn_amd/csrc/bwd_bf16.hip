@@ -3,17 +3,19 @@
 // The pages' engine computes every gradient by hand, RoPE's included, and checks
 // them against centred differences ("Show HN: NanoEuler", paragraph 2). Here the
 // backward recomputes the probabilities from the rotated q, k and the saved
-// log-sum-exp instead of storing the T x T matrix, in two deterministic kernels
-// (no atomics):
+// log-sum-exp instead of storing the T x T matrix. After the per-row pre-pass
+// (bwd_prep.hip: -lse*log2(e) and -delta in the workspace) one deterministic
+// launch (no atomics) runs two kinds of work item:
 //
-//   dq kernel   (one workgroup = 128 queries of a head; loops over key tiles
-//                up to the diagonal): delta_t = sum_d dO[t,d] o[t,d] in its
-//                prologue, written with lse_t*log2(e) to the workspace, then
-//                P = exp(S - lse), dP = dO V^T, dS = P (dP - delta),
-//                dQ^r += s dS K^r, and finally dq = R_t^T dQ^r.
-//   dkdv kernel (one workgroup = 128 keys of a head; loops over query tiles
-//                from the diagonal down): with the same P and dS,
-//                dV += P^T dO, dK^r += s dS^T Q^r, and finally dk = R_u^T dK^r.
+//   dq item   (128 queries of a head; loops over key tiles up to the diagonal):
+//             P = exp(S - lse), dP = dO V^T, dS = P (dP - delta),
+//             dQ^r += s dS K^r, and finally dq = R_t^T dQ^r.
+//   dkdv item (128 keys of a head; loops over query tiles from the diagonal
+//             down): with the same P and dS, dV += P^T dO, dK^r += s dS^T Q^r,
+//             and finally dk = R_u^T dK^r.
+//
+// Running both kinds in one grid lets the light items of one kind fill the
+// gaps the other leaves, with a single tail.
 //
 // The saved query carries the factor log2(e)/sqrt(D), so a score product is
 // S log2(e) and P = 2^(S log2(e) - lse log2(e)). The per-query offsets
@@ -24,9 +26,9 @@
 // Every product is a 32x32x16 MFMA contraction with fp32 accumulation. The
 // rotated q and k and dS are fp16 (the score recompute needs the 11-bit
 // significand, see the forward; dS then shares the fp16 MFMA with them, which
-// bounds |dS| by 65504); dO, V and P are bf16. In the dq kernel a lane column
-// is a query (S^T, dP^T, dQ^T), in the dkdv kernel a key (S, dP, dV^T, dK^T).
-// Tiles stream from global memory straight into an NS-stage LDS ring
+// bounds |dS| by 65504); dO, V and P are bf16. In a dq item a lane column is a
+// query (S^T, dP^T, dQ^T), in a dkdv item a key (S, dP, dV^T, dK^T). Tiles
+// stream from global memory straight into an NS-stage LDS ring
 // (buffer_load ... lds); row-major tiles give the row operands with 16-byte
 // reads and the transposed operands through ds_read_b64_tr_b16, so rounded P
 // and dS registers are directly the B operand of the next contraction.
@@ -121,32 +123,42 @@ __device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const bf16
     dq_tile<D, DIAG>(acc, qf, df, rg.k[STG], rg.v[STG], of, n * C::KN, wq0, lane, nl, nd);
 }
 
+// Pointers and sizes shared by the two kinds of work item of the gradient kernel.
+struct BwdPtrs {
+    const f16* qr;     // rotated q * log2(e)/sqrt(D), fp16
+    const f16* kr;     // rotated k, fp16
+    const bf16* v;
+    const bf16* dO;
+    const float* ws;   // -lse*log2(e) of every row, then -delta of every row
+    const float* cs;
+    const float* sn;
+    bf16 *dq, *dk, *dv;
+    int BH, T;
+};
+
+// dq item: the 128 queries of q-block qb of head bh (loops over key tiles up
+// to the diagonal; rg.k / rg.v hold K / V tiles).
 template <int D>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
-    const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
-    const bf16* __restrict__ o, const bf16* __restrict__ dO, const float* __restrict__ lse,
-    const float* __restrict__ cs, const float* __restrict__ sn, bf16* __restrict__ dq,
-    float* __restrict__ ws, int BH, int T, int nqb, float scale, int ncu) {
+__device__ __forceinline__ void dq_item(const BwdPtrs& pp, const Ring& rg, int bh, int qb) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
-    constexpr int T3 = NS > 2 ? C::TILE : 1024;
-    __shared__ __attribute__((aligned(1024))) char k0[C::TILE], k1[C::TILE], k2[T3];
-    __shared__ __attribute__((aligned(1024))) char v0[C::TILE], v1[C::TILE], v2[T3];
-    const Ring rg = {{k0, k1, k2}, {v0, v1, v2}, {nullptr, nullptr, nullptr}};
-
-    const int bid = snake_item(blockIdx.x, ncu, nqb * BH);
-    const int bh = bid % BH;
-    const int qb = nqb - 1 - bid / BH;
+    const int T = pp.T, BH = pp.BH;
+    const f16* __restrict__ qr = pp.qr;
+    const bf16* __restrict__ dO = pp.dO;
+    const float* __restrict__ ws = pp.ws;
+    const float* __restrict__ cs = pp.cs;
+    const float* __restrict__ sn = pp.sn;
+    bf16* __restrict__ dq = pp.dq;
+    const float scale = 1.f / sqrtf((float)D);
     const int q0 = qb * C::QM;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c32 = lane & 31, hf = lane >> 5;
     const size_t hoff = (size_t)bh * T * D;
     const uint32_t hbytes = (uint32_t)T * D * 2;
-    const f16* kh = kr + hoff;
-    const bf16* vh = v + hoff;
-    const rsrc_t qbuf = make_rsrc(qr + hoff, hbytes), gbuf = make_rsrc(dO + hoff, hbytes),
-                 obuf = make_rsrc(o + hoff, hbytes);
+    const f16* kh = pp.kr + hoff;
+    const bf16* vh = pp.v + hoff;
+    const rsrc_t qbuf = make_rsrc(qr + hoff, hbytes), gbuf = make_rsrc(dO + hoff, hbytes);
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
     const TileLoads<D, 64, 4> ld(wave, lane);
@@ -161,28 +173,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(
         ld.issue(vh, T, s * C::KN, rg.v[s], wave);
     }
 
-    // this lane's query: rotated q (fp16), dO (bf16), and delta = sum_d dO o
+    // this lane's query: rotated q (fp16), dO (bf16) and its two row offsets
     f16x8 qf[C::DK];
     bf16x8 df[C::DK];
-    float dot = 0.f;
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) {
         const uint32_t off = (uint32_t)(tq * D + 16 * c + 8 * hf) * 2;
         qf[c] = __builtin_bit_cast(f16x8, buf_load16(qbuf, off));
-        const u32x4 g = buf_load16(gbuf, off);
-        const u32x4 y = buf_load16(obuf, off);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            dot += bf16_lo(g[e]) * bf16_lo(y[e]) + bf16_hi(g[e]) * bf16_hi(y[e]);
-        df[c] = as_bf16x8(g);
+        df[c] = as_bf16x8(buf_load16(gbuf, off));
     }
-    const float ndl = -sum_across_halves(dot);
-    const float nlt = tq < T ? -lse[(size_t)bh * T + tq] * kLog2e : 0.f;
-    // workspace: -lse*log2(e) of every row, then -delta of every row
-    if (tq < T && hf == 0) {
-        ws[(size_t)bh * T + tq] = nlt;
-        ws[(size_t)BH * T + (size_t)bh * T + tq] = ndl;
-    }
+    const float nlt = tq < T ? ws[(size_t)bh * T + tq] : 0.f;
+    const float ndl = tq < T ? ws[(size_t)BH * T + (size_t)bh * T + tq] : 0.f;
     const f32x16 nl = splat16(nlt), nd = splat16(ndl);
 
     f32x16 acc[C::DB];
@@ -351,23 +352,23 @@ __device__ __forceinline__ void dkdv_step(f32x16* dva, f32x16* dka, const f16x8*
                        reinterpret_cast<const float*>(rg.x[STG]), of, qt * C::QN, x.wk0, x.lane);
 }
 
+// dk/dv item: the 128 keys of key block kb of head bh (loops over query tiles
+// from the diagonal down; rg.k / rg.v / rg.x hold Q / dO tiles and offsets).
 template <int D>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
-    const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
-    const bf16* __restrict__ dO, const float* __restrict__ ws, const float* __restrict__ cs,
-    const float* __restrict__ sn, bf16* __restrict__ dk, bf16* __restrict__ dv, int BH, int T,
-    int nkb, float scale, int ncu) {
+__device__ __forceinline__ void dkdv_item(const BwdPtrs& pp, const Ring& rg, int bh, int kb) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
-    constexpr int T3 = NS > 2 ? C::TILE : 1024;
-    __shared__ __attribute__((aligned(1024))) char q0s[C::TILE], q1s[C::TILE], q2s[T3];
-    __shared__ __attribute__((aligned(1024))) char g0s[C::TILE], g1s[C::TILE], g2s[T3];
-    __shared__ __attribute__((aligned(512))) char l0s[512], l1s[512], l2s[512];
-    const Ring rg = {{q0s, q1s, q2s}, {g0s, g1s, g2s}, {l0s, l1s, l2s}};
-
-    const int bid = snake_item(blockIdx.x, ncu, nkb * BH);
-    const int bh = bid % BH;
-    const int kb = bid / BH;  // key block 0 has the most query tiles: issued first
+    const int T = pp.T, BH = pp.BH;
+    const f16* __restrict__ qr = pp.qr;
+    const f16* __restrict__ kr = pp.kr;
+    const bf16* __restrict__ v = pp.v;
+    const bf16* __restrict__ dO = pp.dO;
+    const float* __restrict__ ws = pp.ws;
+    const float* __restrict__ cs = pp.cs;
+    const float* __restrict__ sn = pp.sn;
+    bf16* __restrict__ dk = pp.dk;
+    bf16* __restrict__ dv = pp.dv;
+    const float scale = kLn2;  // dK^r = s dS^T Q^r = ln 2 * dS^T (log2(e) s Q^r)
     const int k0 = kb * C::KM;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -466,39 +467,56 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_bf16_kernel(
     }
 }
 
+// The gradient kernel: one launch runs both kinds of item, so the light items
+// of one kind fill the gaps left by the other and there is a single tail.
+// Item classes alternate dk/dv key block r and dq q-block nqb-1-r
+// (r = 0, 1, ...), which is heaviest first up to the 4:3 ratio of their
+// products per tile; each class holds one item per head.
 template <int D>
-static hipError_t launch_dq(const BwdArgs& a) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_bf16_kernel(BwdPtrs pp, int nqb,
+                                                                         int nkb, int kinds,
+                                                                         int ncu) {
     using C = BwdTile<D>;
-    const int BH = a.B * a.H;
+    constexpr int NS = C::NS;
+    constexpr int T3 = NS > 2 ? C::TILE : 1024;
+    // one __shared__ object per ring stage (see Ring); both kinds use the same ones
+    __shared__ __attribute__((aligned(1024))) char a0[C::TILE], a1[C::TILE], a2[T3];
+    __shared__ __attribute__((aligned(1024))) char b0[C::TILE], b1[C::TILE], b2[T3];
+    __shared__ __attribute__((aligned(512))) char x0[512], x1[512], x2[512];
+    const Ring rg = {{a0, a1, a2}, {b0, b1, b2}, {x0, x1, x2}};
+
+    // kinds: 1 = dq items only, 2 = dk/dv items only, 3 = both
+    const int per = kinds == 3 ? 2 : 1;
+    const int nclass = per * max(nqb, nkb);
+    const int item = snake_item(blockIdx.x, ncu, nclass * pp.BH);
+    const int c = item / pp.BH, bh = item % pp.BH;
+    const int r = c / per;
+    const bool is_dkdv = kinds == 2 || (kinds == 3 && (c % 2) == 0);
+    if (is_dkdv) {
+        if (r < nkb) dkdv_item<D>(pp, rg, bh, r);
+    } else {
+        if (r < nqb) dq_item<D>(pp, rg, bh, nqb - 1 - r);
+    }
+}
+
+template <int D>
+static hipError_t launch_grads(const BwdArgs& a, int kinds) {
+    using C = BwdTile<D>;
+    const size_t n = (size_t)a.B * a.H * a.T * a.D;
+    const f16* rot = static_cast<const f16*>(a.rot);
+    const BwdPtrs pp = {rot, rot + n, (const bf16*)a.v, (const bf16*)a.dO, a.ws, a.cs, a.sn,
+                        (bf16*)a.dq, (bf16*)a.dk, (bf16*)a.dv, a.B * a.H, a.T};
     const int nqb = (a.T + C::QM - 1) / C::QM;
-    const float scale = 1.f / sqrtf((float)D);
-    const size_t n = (size_t)a.B * a.H * a.T * a.D;
-    const f16* rot = static_cast<const f16*>(a.rot);
-    hipLaunchKernelGGL(bwd_dq_bf16_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream, rot,
-                       rot + n, (const bf16*)a.v, (const bf16*)a.o, (const bf16*)a.dO, a.lse,
-                       a.cs, a.sn, (bf16*)a.dq, a.ws, BH, a.T, nqb, scale, device_cu_count());
-    return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_dkdv(const BwdArgs& a) {
-    using C = BwdTile<D>;
-    const int BH = a.B * a.H;
     const int nkb = (a.T + C::KM - 1) / C::KM;
-    const size_t n = (size_t)a.B * a.H * a.T * a.D;
-    const f16* rot = static_cast<const f16*>(a.rot);
-    hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<D>, dim3(nkb * BH), dim3(C::NT), 0, a.stream, rot,
-                       rot + n, (const bf16*)a.v, (const bf16*)a.dO, a.ws, a.cs, a.sn,
-                       (bf16*)a.dk, (bf16*)a.dv, BH, a.T, nkb, kLn2, device_cu_count());
+    const int per = kinds == 3 ? 2 : 1;
+    const int items = per * (nqb > nkb ? nqb : nkb) * a.B * a.H;
+    hipLaunchKernelGGL(bwd_bf16_kernel<D>, dim3(items), dim3(C::NT), 0, a.stream, pp, nqb, nkb,
+                       kinds, device_cu_count());
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
-    return a.D == 64 ? launch_dq<64>(a) : launch_dq<128>(a);
-}
-
-hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a) {
-    return a.D == 64 ? launch_dkdv<64>(a) : launch_dkdv<128>(a);
+hipError_t launch_bwd_grads_bf16(const BwdArgs& a) {
+    return a.D == 64 ? launch_grads<64>(a, 3) : launch_grads<128>(a, 3);
 }
 
 }  // namespace attn

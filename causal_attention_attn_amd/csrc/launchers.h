@@ -22,8 +22,8 @@ struct BwdArgs {
     const float *lse, *cs, *sn;
     const void* rot;  // bf16 path: rotated q * log2(e)/sqrt(D), then rotated k, [B, H, T, D] fp16 each
     void *dq, *dk, *dv;
-    float* ws;  // workspace: bf16 path [B, H, T] -lse*log2(e), then [B, H, T] -delta;
-                // fp32 path [B, H, T] delta
+    float* ws;  // workspace (written by the pre-pass): bf16 path [B, H, T] -lse*log2(e),
+                // then [B, H, T] -delta; fp32 path [B, H, T] delta
     int B, H, T, D;
     hipStream_t stream;
 };
@@ -36,10 +36,11 @@ hipError_t launch_rotate_qk(const void* q, const void* k, const float* cs, const
                             void* out, int B, int H, int T, int D, hipStream_t s);
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
-hipError_t launch_bwd_dq_bf16(const BwdArgs& a);
-hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a);
+hipError_t launch_bwd_prep_bf16(const BwdArgs& a);   // workspace entries (bf16 layout)
+hipError_t launch_bwd_grads_bf16(const BwdArgs& a);  // dq, dk, dv in one launch
 
 hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_bwd_prep_f32(const BwdArgs& a);    // workspace entries (delta)
 hipError_t launch_bwd_dq_f32(const BwdArgs& a);
 hipError_t launch_bwd_dkdv_f32(const BwdArgs& a);
 

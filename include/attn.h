@@ -140,7 +140,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype);
  * respect to the pre-RoPE q, k and v ("Show HN: NanoEuler", paragraph 2: every
  * analytic gradient, RoPE's included, is checked against centred differences).
  * Recompute-based: P is rebuilt from q, k and lse; nothing of size T x T is
- * stored. Runs attn_bwd_dq then attn_bwd_dkdv on `stream`.
+ * stored. Enqueues attn_bwd_prep then attn_bwd_grads on `stream`.
  *   q, k, v, o, dO  [B,H,T,D] dtype, inputs (o and lse from attn_fwd); the
  *                   ATTN_BF16 kernels take the rotated q and k from `saved`
  *   lse             [B,H,T] fp32, input
@@ -160,30 +160,31 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              int B, int H, int T, int D, int dtype, void* stream);
 
 /*
- * attn_bwd_dq - first stage of attn_bwd: writes the per-row workspace entries
- * (delta_t = sum_d dO[t,d] o[t,d], negated for ATTN_BF16, and there also
- * -lse_t * log2 e) and dq
- * (gradient w.r.t. the pre-RoPE q). Same arguments and rules as attn_bwd,
- * minus dk and dv.
+ * attn_bwd_prep - first stage of attn_bwd, the per-row pre-pass of the
+ * recompute-based backward: delta_t = sum_d dO[t,d] o[t,d] (equal to
+ * sum_u P[t,u] dP[t,u], the softmax Jacobian term) and, for ATTN_BF16,
+ * lse_t * log2 e, written to the workspace in the layout of
+ * attn_bwd_workspace_bytes. o, dO [B,H,T,D] dtype and lse [B,H,T] fp32 are
+ * inputs; the workspace must not alias them.
  */
-int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
-                const void* dO, const float* lse,
-                const float* cos_tab, const float* sin_tab,
-                const void* saved, size_t saved_bytes,
-                void* dq, void* workspace, size_t workspace_bytes,
-                int B, int H, int T, int D, int dtype, void* stream);
+int attn_bwd_prep(const void* o, const void* dO, const float* lse,
+                  void* workspace, size_t workspace_bytes,
+                  int B, int H, int T, int D, int dtype, void* stream);
 
 /*
- * attn_bwd_dkdv - second stage of attn_bwd: writes dk (w.r.t. the pre-RoPE k)
- * and dv. Reads the workspace entries of attn_bwd_dq, which must have been
- * enqueued before it on the same stream (or completed) with the same inputs.
+ * attn_bwd_grads - second stage of attn_bwd: writes dq, dk (w.r.t. the pre-RoPE
+ * q and k) and dv. Reads the workspace entries of attn_bwd_prep, which must
+ * have been enqueued before it on the same stream (or completed) for the same
+ * o, dO and lse. Same arguments and rules as attn_bwd, minus o; for ATTN_BF16
+ * dq and dk/dv come from one launch.
  */
-int attn_bwd_dkdv(const void* q, const void* k, const void* v,
-                  const void* dO, const float* lse,
-                  const float* cos_tab, const float* sin_tab,
-                  const void* saved, size_t saved_bytes,
-                  void* dk, void* dv, const void* workspace, size_t workspace_bytes,
-                  int B, int H, int T, int D, int dtype, void* stream);
+int attn_bwd_grads(const void* q, const void* k, const void* v,
+                   const void* dO, const float* lse,
+                   const float* cos_tab, const float* sin_tab,
+                   const void* saved, size_t saved_bytes,
+                   void* dq, void* dk, void* dv,
+                   const void* workspace, size_t workspace_bytes,
+                   int B, int H, int T, int D, int dtype, void* stream);
 
 /* attn_status_string - static, human-readable name of a status code. */
 const char* attn_status_string(int status);

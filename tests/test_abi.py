@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_rotated", "attn_rotate_qk", "attn_saved_bytes", "attn_bwd",
-              "attn_bwd_dq", "attn_bwd_dkdv", "attn_rope_tables", "attn_bwd_workspace_bytes",
+              "attn_bwd_prep", "attn_bwd_grads", "attn_rope_tables", "attn_bwd_workspace_bytes",
               "attn_status_string", "attn_last_hip_error"):
         assert n in names
 
@@ -135,6 +135,33 @@ def test_bwd_rejects_bad_arguments(lib):
     assert f(saved=0) == 1
     assert f(saved_bytes=8) == 9
     assert f(dq=FAKE + 192) == 7                          # dq aliases saved
+
+
+def test_bwd_stages_reject_bad_arguments(lib):
+    f = lambda **o: status_of(lambda: attn.attn_bwd_prep(
+        **{**dict(o=FAKE, dO=FAKE + 16, lse=FAKE + 32, workspace=FAKE + 48, workspace_bytes=256,
+                  B=1, H=1, T=8, D=64, dtype=0, stream=0), **o}))
+    assert f(o=0) == 1
+    assert f(lse=0) == 1
+    assert f(D=32) == 2
+    assert f(dtype=5) == 3
+    assert f(dO=MIS) == 4
+    assert f(workspace=0) == 5
+    assert f(workspace_bytes=255) == 5
+    assert f(workspace=MIS) == 4
+    assert f(workspace=FAKE + 16) == 7                   # workspace aliases dO
+    base = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, dO=FAKE + 64, lse=FAKE + 80,
+                cos_tab=FAKE + 96, sin_tab=FAKE + 112, saved=FAKE + 192, saved_bytes=4 * 8 * 64,
+                dq=FAKE + 128, dk=FAKE + 144, dv=FAKE + 160, workspace=FAKE + 176,
+                workspace_bytes=256, B=1, H=1, T=8, D=64, dtype=0, stream=0)
+    g = lambda **o: status_of(lambda: attn.attn_bwd_grads(**{**base, **o}))
+    assert g(dq=0) == 1
+    assert g(saved=0) == 1
+    assert g(saved_bytes=8) == 9
+    assert g(workspace=0) == 5
+    assert g(dv=FAKE + 32) == 7                           # dv aliases v
+    assert g(dk=FAKE + 128) == 7                          # dk aliases dq
+    assert g(dq=FAKE + 176) == 7                          # dq aliases the workspace
 
 
 def test_rope_tables_reject_bad_arguments(lib):
