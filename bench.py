@@ -9,9 +9,12 @@ synthetic input already resident in HBM; the RoPE tables are built before the
 timed region (they depend only on T, D and the base, like weights). Throughput
 uses the causal FLOP convention: forward 2*B*H*T^2*D, backward 2.5x forward.
 
-Prints ONE JSON line. Besides the headline figures it carries
-  roofline      for the kernel with the longest average duration, timed with
-                HIP events on the stream the kernels run on;
+Prints ONE JSON line. The headline value is the whole step's rate over K
+steps launched back to back between two HIP events. Besides it the line carries
+  kernels       each kernel's average duration, from R back-to-back launches of
+                that kernel alone between two HIP events on the kernels' stream
+                (five rounds);
+  roofline      for the kernel with the longest average duration;
   cpu_baseline  the float64 oracle timed on this host's cores on a bounded
                 sample of the same workload (and a parity check of the GPU
                 outputs on that sample).
@@ -121,26 +124,38 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for i in range(K):
-        e = ev[i]
-        e[0].record(stream); rotate()
-        e[1].record(stream); fwd()
-        e[2].record(stream); bwd_prep()
-        e[3].record(stream); bwd_grads()
-        e[4].record(stream)
+    for _ in range(K):  # the timed region: K whole steps back to back, nothing in between
+        rotate(); fwd(); bwd_prep(); bwd_grads()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / K
-    per = {n: np.array([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)])
-           for j, n in enumerate(("rotate_kernel", "fwd_kernel", "bwd_prep_kernel",
-                                  "bwd_grads_kernel"))}
     print(f"# timed {K} steps in {wall:.3f} s wall", file=sys.stderr, flush=True)
+
+    # per-kernel durations: each kernel launched R times back to back between two HIP
+    # events on the kernels' stream, repeated in rounds (an event between every launch
+    # would add its own gap to each interval); inputs are those of the timed steps
+    R = max(1, min(K, 50))
+    per = {}
+    for n, f in (("rotate_kernel", rotate), ("fwd_kernel", fwd), ("bwd_prep_kernel", bwd_prep),
+                 ("bwd_grads_kernel", bwd_grads)):
+        samples = []
+        for _ in range(5):
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record(stream)
+            for _ in range(R):
+                f()
+            b_ev.record(stream)
+            torch.cuda.synchronize()
+            samples.append(a_ev.elapsed_time(b_ev) / R)
+        per[n] = np.array(samples)
+    # leave every output as one full step writes it (for the parity check below)
+    rotate(); fwd(); bwd_prep(); bwd_grads()
+    torch.cuda.synchronize()
 
     fl = causal_flops(B, H, T, D)
     total = fl["fwd"] + fl["bwd"]
@@ -148,8 +163,8 @@ def main():
     kernels = {}
     for n, arr in per.items():
         ms = float(np.mean(arr))
-        kernels[n] = {"avg_us": round(ms * 1e3, 2), "p10_us": round(float(np.percentile(arr, 10)) * 1e3, 2),
-                      "p90_us": round(float(np.percentile(arr, 90)) * 1e3, 2),
+        kernels[n] = {"avg_us": round(ms * 1e3, 2), "min_us": round(float(arr.min()) * 1e3, 2),
+                      "max_us": round(float(arr.max()) * 1e3, 2),
                       "tflops": round(fl[n] / (ms * 1e-3) / 1e12, 1)}
     # the memory-bound passes: rotation reads q, k (bf16) and writes q', k' (fp16); the
     # backward pre-pass reads o, dO (bf16) and lse and writes two fp32 per row
