@@ -52,6 +52,26 @@ struct BwdTile {
     static constexpr int LPT = 2 * TILE / 1024 / NW;   // tile load instructions per wave
 };
 
+// The RoPE table entries this lane's epilogue needs to rotate its row t back:
+// features d = 32b + 8g + 4h .. +3 (h = lane >> 5), i.e. the cos/sin pairs
+// d/2, d/2 + 1. Loaded when an item starts, so their latency hides behind the
+// item's tile loop. Rows past the end read row 0 (their results are not stored).
+template <int D>
+struct RowTables {
+    f32x2 c[D / 32][4], s[D / 32][4];
+    __device__ __forceinline__ void load(const float* cs, const float* sn, int t, int T, int hf) {
+        const size_t row = (size_t)(t < T ? t : 0) * (D / 2);
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * b + 8 * g + 4 * hf;
+                c[b][g] = *reinterpret_cast<const f32x2*>(cs + row + d / 2);
+                s[b][g] = *reinterpret_cast<const f32x2*>(sn + row + d / 2);
+            }
+    }
+};
+
 // One 64-key tile of the dq kernel for one wave (32 queries). DIAG: the tile may
 // reach this wave's diagonal (32-key blocks above it skipped, the diagonal one masked).
 template <int D, bool DIAG>
@@ -110,16 +130,22 @@ template <int D, int STG, bool DIAG>
 __device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const bf16x8* df,
                                         const Ring& rg,
                                         const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
-                                        const f16* kr, const bf16* v, int T, int n, int wq0,
-                                        int lane, int wave, const f32x16& nl, const f32x16& nd) {
+                                        const f16* kr, const bf16* v, int T, int n, int ntiles,
+                                        int wq0, int lane, int wave, const f32x16& nl,
+                                        const f32x16& nd) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int NXT = (STG + NS - 1) % NS;
-    wait_vmcnt<C::LPT * (NS - 2)>();
+    // tiles past the item's last one are never loaded, so the last step has no
+    // younger tile in flight and waits for everything
+    if (n + 1 < ntiles) wait_vmcnt<C::LPT * (NS - 2)>();
+    else wait_vmcnt<0>();
     ring_barrier();
     const int nx = n + NS - 1;
-    ld.issue(kr, T, nx * C::KN, rg.k[NXT], wave);
-    ld.issue(v, T, nx * C::KN, rg.v[NXT], wave);
+    if (nx < ntiles) {
+        ld.issue(kr, T, nx * C::KN, rg.k[NXT], wave);
+        ld.issue(v, T, nx * C::KN, rg.v[NXT], wave);
+    }
     dq_tile<D, DIAG>(acc, qf, df, rg.k[STG], rg.v[STG], of, n * C::KN, wq0, lane, nl, nd);
 }
 
@@ -167,10 +193,14 @@ __device__ __forceinline__ void dq_item(const BwdPtrs& pp, const Ring& rg, int b
     const int kend = min(T, q0 + C::QM);
     const int ntiles = (kend + C::KN - 1) / C::KN;
     const int nfull = min(ntiles, q0 / C::KN);
+    RowTables<D> tb;
+    tb.load(cs, sn, tq, T, hf);
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) {
-        ld.issue(kh, T, s * C::KN, rg.k[s], wave);
-        ld.issue(vh, T, s * C::KN, rg.v[s], wave);
+        if (s < ntiles) {
+            ld.issue(kh, T, s * C::KN, rg.k[s], wave);
+            ld.issue(vh, T, s * C::KN, rg.v[s], wave);
+        }
     }
 
     // this lane's query: rotated q (fp16), dO (bf16) and its two row offsets
@@ -192,43 +222,30 @@ __device__ __forceinline__ void dq_item(const BwdPtrs& pp, const Ring& rg, int b
 
     int n = 0;
     for (; n + NS <= nfull; n += NS) {
-        dq_step<D, 0, false>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, nl, nd);
-        dq_step<D, 1, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 1, wq0, lane, wave, nl, nd);
+        dq_step<D, 0, false>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
+        dq_step<D, 1, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 1, ntiles, wq0, lane, wave, nl, nd);
         if constexpr (NS > 2)
-            dq_step<D, 2, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 2, wq0, lane, wave, nl, nd);
+            dq_step<D, 2, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 2, ntiles, wq0, lane, wave, nl, nd);
     }
     for (; n < ntiles; ++n) {
         const int stg = n % NS;
         if (stg == 0)
-            dq_step<D, 0, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, nl, nd);
+            dq_step<D, 0, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
         else if (stg == 1)
-            dq_step<D, 1, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, nl, nd);
+            dq_step<D, 1, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
         else if constexpr (NS > 2)
-            dq_step<D, 2, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, wq0, lane, wave, nl, nd);
+            dq_step<D, 2, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
     }
     wait_vmcnt<0>();
 
     if (tq < T) {
         bf16* out = dq + hoff + (size_t)tq * D;
-        const float* crow = cs + (size_t)tq * (D / 2);
-        const float* srow = sn + (size_t)tq * (D / 2);
-        // every table load before the first store (see the dk/dv epilogue)
-        f32x2 c2s[C::DB][4], s2s[C::DB][4];
-#pragma unroll
-        for (int b = 0; b < C::DB; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = 32 * b + 8 * g + 4 * hf;
-                c2s[b][g] = *reinterpret_cast<const f32x2*>(crow + d / 2);
-                s2s[b][g] = *reinterpret_cast<const f32x2*>(srow + d / 2);
-            }
-        asm volatile("" ::: "memory");
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = 32 * b + 8 * g + 4 * hf;
-                const f32x2 c2 = c2s[b][g], s2 = s2s[b][g];
+                const f32x2 c2 = tb.c[b][g], s2 = tb.s[b][g];
                 u32x2 w;
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
@@ -341,13 +358,15 @@ template <int D, int STG, bool DIAG>
 __device__ __forceinline__ void dkdv_step(f32x16* dva, f32x16* dka, const f16x8* kf,
                                           const bf16x8* vf, const Ring& rg,
                                           const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
-                                          const DkdvCtx<D>& x, int qt) {
+                                          const DkdvCtx<D>& x, int qt, int nqt) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int NXT = (STG + NS - 1) % NS;
-    wait_vmcnt<(C::LPT + 1) * (NS - 2)>();
+    // tiles past the last query tile are never loaded (see dq_step)
+    if (qt + 1 < nqt) wait_vmcnt<(C::LPT + 1) * (NS - 2)>();
+    else wait_vmcnt<0>();
     ring_barrier();
-    x.issue(ld, qt + NS - 1, rg.k[NXT], rg.v[NXT], rg.x[NXT]);
+    if (qt + NS - 1 < nqt) x.issue(ld, qt + NS - 1, rg.k[NXT], rg.v[NXT], rg.x[NXT]);
     dkdv_tile<D, DIAG>(dva, dka, kf, vf, rg.k[STG], rg.v[STG],
                        reinterpret_cast<const float*>(rg.x[STG]), of, qt * C::QN, x.wk0, x.lane);
 }
@@ -385,8 +404,11 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs& pp, const Ring& rg, int
     const int qt0 = k0 / C::QN;
     const int nqt = (T + C::QN - 1) / C::QN;
     const int qfull = min(nqt, (k0 + C::KM) / C::QN);  // from here on no query precedes a key
+    RowTables<D> tb;
+    tb.load(cs, sn, tk, T, hf);
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) x.issue(ld, qt0 + s, rg.k[s], rg.v[s], rg.x[s]);
+    for (int s = 0; s < NS - 1; ++s)
+        if (qt0 + s < nqt) x.issue(ld, qt0 + s, rg.k[s], rg.v[s], rg.x[s]);
 
     const rsrc_t kbuf = make_rsrc(kr + hoff, hbytes), vbuf = make_rsrc(v + hoff, hbytes);
     f16x8 kf[C::DK];
@@ -405,53 +427,38 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs& pp, const Ring& rg, int
     int qt = qt0;
     for (; qt < min(qfull, nqt); ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 0) dkdv_step<D, 0, true>(dva, dka, kf, vf, rg, ld, of, x, qt);
-        else if (stg == 1) dkdv_step<D, 1, true>(dva, dka, kf, vf, rg, ld, of, x, qt);
-        else if constexpr (NS > 2) dkdv_step<D, 2, true>(dva, dka, kf, vf, rg, ld, of, x, qt);
+        if (stg == 0) dkdv_step<D, 0, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if (stg == 1) dkdv_step<D, 1, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if constexpr (NS > 2) dkdv_step<D, 2, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
     // the full tiles, rotated so that the unrolled body starts on stage 0
     for (; qt < nqt && (qt - qt0) % NS != 0; ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
-        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
+        if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
     for (; qt + NS <= nqt; qt += NS) {
-        dkdv_step<D, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
-        dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 1);
-        if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 2);
+        dkdv_step<D, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 1, nqt);
+        if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 2, nqt);
     }
     for (; qt < nqt; ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 0) dkdv_step<D, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
-        else if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
-        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt);
+        if (stg == 0) dkdv_step<D, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
     wait_vmcnt<0>();
 
     if (tk < T) {
         bf16* ko = dk + hoff + (size_t)tk * D;
         bf16* vo = dv + hoff + (size_t)tk * D;
-        const float* crow = cs + (size_t)tk * (D / 2);
-        const float* srow = sn + (size_t)tk * (D / 2);
-        // every table load before the first store: on this GPU stores count in
-        // vmcnt too, so a load issued after a store could only be waited for
-        // together with that store
-        f32x2 c2s[C::DB][4], s2s[C::DB][4];
-#pragma unroll
-        for (int b = 0; b < C::DB; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = 32 * b + 8 * g + 4 * hf;
-                c2s[b][g] = *reinterpret_cast<const f32x2*>(crow + d / 2);
-                s2s[b][g] = *reinterpret_cast<const f32x2*>(srow + d / 2);
-            }
-        asm volatile("" ::: "memory");
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = 32 * b + 8 * g + 4 * hf;
-                const f32x2 c2 = c2s[b][g], s2 = s2s[b][g];
+                const f32x2 c2 = tb.c[b][g], s2 = tb.s[b][g];
                 u32x2 wk, wv;
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
