@@ -87,7 +87,7 @@ def main():
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
     B, H, T, D = w.shape
-    dt = attn.ATTN_BF16 if w.dtype == "bf16" else attn.ATTN_F32
+    dt = {"bf16": attn.ATTN_BF16, "f16": attn.ATTN_F16, "f32": attn.ATTN_F32}[w.dtype]
     print(f"# workload {name} B{B} H{H} T{T} D{D} {w.dtype}", file=sys.stderr, flush=True)
     x = workloads.make(w, seed=0)
     g = {n: t.to(dev) for n, t in x.items()}
@@ -102,8 +102,8 @@ def main():
     saved = torch.empty(max(nsv, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    if dt != attn.ATTN_BF16:
-        print("bench.py times the bf16 path", file=sys.stderr)
+    if dt == attn.ATTN_F32:
+        print("bench.py times the 16-bit path", file=sys.stderr)
         sys.exit(2)
 
     def rotate():
@@ -210,8 +210,8 @@ def main():
 
 # kernel -> the sources that define it; a traffic figure is valid only for these exact sources
 KERNEL_SOURCES = {
-    "fwd_kernel": ["fwd_bf16.hip", "device_common.h"],
-    "bwd_grads_kernel": ["bwd_bf16.hip", "device_common.h"],
+    "fwd_kernel": ["fwd_16bit.hip", "device_common.h"],
+    "bwd_grads_kernel": ["bwd_16bit.hip", "device_common.h"],
     "bwd_prep_kernel": ["bwd_prep.hip", "device_common.h"],
     "rotate_kernel": ["rope_tables.hip", "device_common.h"],
 }

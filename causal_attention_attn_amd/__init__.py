@@ -7,6 +7,7 @@ memory and streams only.
 
 from ._lib import (  # noqa: F401
     ATTN_BF16,
+    ATTN_F16,
     ATTN_F32,
     LIB_PATH,
     AttnError,

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libattn.so")
 
 ATTN_BF16 = 0
 ATTN_F32 = 1
+ATTN_F16 = 2
 
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",

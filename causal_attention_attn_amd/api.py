@@ -6,13 +6,14 @@ import torch
 
 from . import _lib
 
-_DTYPES = {torch.bfloat16: _lib.ATTN_BF16, torch.float32: _lib.ATTN_F32}
+_DTYPES = {torch.bfloat16: _lib.ATTN_BF16, torch.float16: _lib.ATTN_F16,
+           torch.float32: _lib.ATTN_F32}
 _tables = {}
 
 
 def _dtype_code(t):
     if t.dtype not in _DTYPES:
-        raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+        raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16, float16 or float32")
     return _DTYPES[t.dtype]
 
 

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.hip", "rope_tables.hip", "fwd_bf16.hip", "bwd_prep.hip", "bwd_bf16.hip",
+SOURCES = ["api.hip", "rope_tables.hip", "fwd_16bit.hip", "bwd_prep.hip", "bwd_16bit.hip",
            "attn_f32.hip"]
 ARCH = "gfx950"
 

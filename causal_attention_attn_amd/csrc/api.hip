@@ -17,7 +17,7 @@ thread_local int g_last_hip_error = 0;
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 int check_shape(int B, int H, int T, int D, int dtype) {
-    if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+    if (dtype != ATTN_BF16 && dtype != ATTN_F16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
     if (D != 64 && D != 128) return ATTN_ERR_SHAPE;
     if (B < 1 || H < 1 || T < 1) return ATTN_ERR_SHAPE;
     const long long elems = (long long)B * H * T * D;
@@ -55,16 +55,16 @@ int hip_status(hipError_t e) {
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t saved_need(int B, int H, int T, int D, int dtype) {
-    return dtype == ATTN_BF16 ? round256((size_t)4 * B * H * T * D) : 0;
+    return dtype != ATTN_F32 ? round256((size_t)4 * B * H * T * D) : 0;
 }
 
 size_t workspace_need(int B, int H, int T, int dtype) {
-    return round256((size_t)(dtype == ATTN_BF16 ? 8 : 4) * B * H * T);
+    return round256((size_t)(dtype != ATTN_F32 ? 8 : 4) * B * H * T);
 }
 
-// the rotated q/k buffer an entry point reads: required for bf16, unused for fp32
+// the rotated q/k buffer an entry point reads: required for bf16 and fp16, unused for fp32
 int check_saved(const void* saved, size_t saved_bytes, int B, int H, int T, int D, int dtype) {
-    if (dtype != ATTN_BF16) return ATTN_OK;
+    if (dtype == ATTN_F32) return ATTN_OK;
     if (saved == nullptr) return ATTN_ERR_NULL;
     if (misaligned(saved)) return ATTN_ERR_ALIGN;
     if (saved_bytes < saved_need(B, H, T, D, dtype)) return ATTN_ERR_SAVED;
@@ -139,21 +139,21 @@ int attn_rotate_qk(const void* q, const void* k, const float* cos_tab, const flo
                    void* stream) {
     int st = check_shape(B, H, T, D, dtype);
     if (st) return st;
-    if (dtype != ATTN_BF16) return ATTN_OK;  // the fp32 path rotates on load
+    if (dtype == ATTN_F32) return ATTN_OK;  // the fp32 path rotates on load
     st = check_ptrs({q, k, cos_tab, sin_tab});
     if (st) return st;
     st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
     if (st) return st;
     if (any_alias({saved}, {q, k, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
     return hip_status(attn::launch_rotate_qk(q, k, cos_tab, sin_tab, saved, B, H, T, D,
-                                             static_cast<hipStream_t>(stream)));
+                                             dtype == ATTN_F16, static_cast<hipStream_t>(stream)));
 }
 
 int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void* o, float* lse,
                      int B, int H, int T, int D, int dtype, void* stream) {
     int st = check_shape(B, H, T, D, dtype);
     if (st) return st;
-    if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (dtype == ATTN_F32) return ATTN_ERR_DTYPE;
     st = check_ptrs({v, o, lse});
     if (st) return st;
     st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
@@ -163,7 +163,7 @@ int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void*
     a.v = v; a.rot = saved; a.o = o; a.lse = lse;
     a.B = B; a.H = H; a.T = T; a.D = D;
     a.stream = static_cast<hipStream_t>(stream);
-    return hip_status(attn::launch_fwd_bf16(a));
+    return hip_status(attn::launch_fwd16(a, dtype == ATTN_F16));
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, const float* cos_tab,
@@ -176,7 +176,7 @@ int attn_fwd(const void* q, const void* k, const void* v, const float* cos_tab,
     st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
     if (st) return st;
     if (any_alias({o, lse}, {q, k, v, cos_tab, sin_tab, saved})) return ATTN_ERR_ALIAS;
-    if (dtype == ATTN_BF16) {
+    if (dtype != ATTN_F32) {
         if (any_alias({saved}, {q, k, v, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
         st = attn_rotate_qk(q, k, cos_tab, sin_tab, saved, saved_bytes, B, H, T, D, dtype,
                             stream);
@@ -208,8 +208,8 @@ int attn_bwd_prep(const void* o, const void* dO, const float* lse, void* workspa
     const attn::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr,
                                      nullptr, nullptr, nullptr, nullptr, workspace, B, H, T, D,
                                      stream);
-    return hip_status(dtype == ATTN_BF16 ? attn::launch_bwd_prep_bf16(a)
-                                         : attn::launch_bwd_prep_f32(a));
+    return hip_status(dtype == ATTN_F32 ? attn::launch_bwd_prep_f32(a)
+                                        : attn::launch_bwd_prep16(a, dtype == ATTN_F16));
 }
 
 int attn_bwd_grads(const void* q, const void* k, const void* v, const void* dO,
@@ -226,7 +226,7 @@ int attn_bwd_grads(const void* q, const void* k, const void* v, const void* dO,
         return ATTN_ERR_ALIAS;
     const attn::BwdArgs a = bwd_args(q, k, v, nullptr, dO, lse, cos_tab, sin_tab, saved, dq, dk,
                                      dv, workspace, B, H, T, D, stream);
-    if (dtype == ATTN_BF16) return hip_status(attn::launch_bwd_grads_bf16(a));
+    if (dtype != ATTN_F32) return hip_status(attn::launch_bwd_grads16(a, dtype == ATTN_F16));
     st = hip_status(attn::launch_bwd_dq_f32(a));
     if (st) return st;
     return hip_status(attn::launch_bwd_dkdv_f32(a));

@@ -1,4 +1,5 @@
-// Backward pass of causal RoPE attention, bf16 storage / fp32 accumulation, gfx950.
+// Backward pass of causal RoPE attention, 16-bit storage (bf16 or fp16, type E)
+// with fp32 accumulation, gfx950.
 //
 // The pages' engine computes every gradient by hand, RoPE's included, and checks
 // them against centred differences ("Show HN: NanoEuler", paragraph 2). Here the
@@ -26,7 +27,7 @@
 // Every product is a 32x32x16 MFMA contraction with fp32 accumulation. The
 // rotated q and k and dS are fp16 (the score recompute needs the 11-bit
 // significand, see the forward; dS then shares the fp16 MFMA with them, which
-// bounds |dS| by 65504); dO, V and P are bf16. In a dq item a lane column is a
+// bounds |dS| by 65504); dO, V and P are of the storage type E. In a dq item a lane column is a
 // query (S^T, dP^T, dQ^T), in a dkdv item a key (S, dP, dV^T, dK^T). Tiles
 // stream from global memory straight into an NS-stage LDS ring
 // (buffer_load ... lds); row-major tiles give the row operands with 16-byte
@@ -74,8 +75,8 @@ struct RowTables {
 
 // One 64-key tile of the dq kernel for one wave (32 queries). DIAG: the tile may
 // reach this wave's diagonal (32-key blocks above it skipped, the diagonal one masked).
-template <int D, bool DIAG>
-__device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const bf16x8* df,
+template <int D, typename E, bool DIAG>
+__device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const vec8<E>* df,
                                         const char* ks, const char* vs, const OperandOffs<D>& of,
                                         int k0, int wq0, int lane, const f32x16& nl,
                                         const f32x16& nd) {
@@ -92,11 +93,11 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const bf16
         // x = S log2(e) - lse log2(e) and dp = dP - delta: the offsets are the
         // accumulators' initial values
         f32x16 x = mfma32(*reinterpret_cast<const f16x8*>(kr + of.k[0]), qf[0], nl);
-        f32x16 dp = mfma32(*reinterpret_cast<const bf16x8*>(vr + of.k[0]), df[0], nd);
+        f32x16 dp = mfma32(*reinterpret_cast<const vec8<E>*>(vr + of.k[0]), df[0], nd);
 #pragma unroll
         for (int c = 1; c < C::DK; ++c) {
             x = mfma32(*reinterpret_cast<const f16x8*>(kr + of.k[c]), qf[c], x);
-            dp = mfma32(*reinterpret_cast<const bf16x8*>(vr + of.k[c]), df[c], dp);
+            dp = mfma32(*reinterpret_cast<const vec8<E>*>(vr + of.k[c]), df[c], dp);
         }
         if (DIAG && kb == wq0) {
 #pragma unroll
@@ -126,11 +127,11 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const bf16
 }
 
 // Step n of the dq kernel's key-tile loop on ring stage STG (= n % NS).
-template <int D, int STG, bool DIAG>
-__device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const bf16x8* df,
+template <int D, typename E, int STG, bool DIAG>
+__device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const vec8<E>* df,
                                         const Ring& rg,
                                         const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
-                                        const f16* kr, const bf16* v, int T, int n, int ntiles,
+                                        const f16* kr, const E* v, int T, int n, int ntiles,
                                         int wq0, int lane, int wave, const f32x16& nl,
                                         const f32x16& nd) {
     using C = BwdTile<D>;
@@ -146,35 +147,36 @@ __device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const bf16
         ld.issue(kr, T, nx * C::KN, rg.k[NXT], wave);
         ld.issue(v, T, nx * C::KN, rg.v[NXT], wave);
     }
-    dq_tile<D, DIAG>(acc, qf, df, rg.k[STG], rg.v[STG], of, n * C::KN, wq0, lane, nl, nd);
+    dq_tile<D, E, DIAG>(acc, qf, df, rg.k[STG], rg.v[STG], of, n * C::KN, wq0, lane, nl, nd);
 }
 
 // Pointers and sizes shared by the two kinds of work item of the gradient kernel.
+template <typename E>
 struct BwdPtrs {
     const f16* qr;     // rotated q * log2(e)/sqrt(D), fp16
     const f16* kr;     // rotated k, fp16
-    const bf16* v;
-    const bf16* dO;
+    const E* v;
+    const E* dO;
     const float* ws;   // -lse*log2(e) of every row, then -delta of every row
     const float* cs;
     const float* sn;
-    bf16 *dq, *dk, *dv;
+    E *dq, *dk, *dv;
     int BH, T;
 };
 
 // dq item: the 128 queries of q-block qb of head bh (loops over key tiles up
 // to the diagonal; rg.k / rg.v hold K / V tiles).
-template <int D>
-__device__ __forceinline__ void dq_item(const BwdPtrs& pp, const Ring& rg, int bh, int qb) {
+template <int D, typename E>
+__device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, int bh, int qb) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     const int T = pp.T, BH = pp.BH;
     const f16* __restrict__ qr = pp.qr;
-    const bf16* __restrict__ dO = pp.dO;
+    const E* __restrict__ dO = pp.dO;
     const float* __restrict__ ws = pp.ws;
     const float* __restrict__ cs = pp.cs;
     const float* __restrict__ sn = pp.sn;
-    bf16* __restrict__ dq = pp.dq;
+    E* __restrict__ dq = pp.dq;
     const float scale = 1.f / sqrtf((float)D);
     const int q0 = qb * C::QM;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -183,7 +185,7 @@ __device__ __forceinline__ void dq_item(const BwdPtrs& pp, const Ring& rg, int b
     const size_t hoff = (size_t)bh * T * D;
     const uint32_t hbytes = (uint32_t)T * D * 2;
     const f16* kh = pp.kr + hoff;
-    const bf16* vh = pp.v + hoff;
+    const E* vh = pp.v + hoff;
     const rsrc_t qbuf = make_rsrc(qr + hoff, hbytes), gbuf = make_rsrc(dO + hoff, hbytes);
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
@@ -203,14 +205,14 @@ __device__ __forceinline__ void dq_item(const BwdPtrs& pp, const Ring& rg, int b
         }
     }
 
-    // this lane's query: rotated q (fp16), dO (bf16) and its two row offsets
+    // this lane's query: rotated q (fp16), dO (E) and its two row offsets
     f16x8 qf[C::DK];
-    bf16x8 df[C::DK];
+    vec8<E> df[C::DK];
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) {
         const uint32_t off = (uint32_t)(tq * D + 16 * c + 8 * hf) * 2;
         qf[c] = __builtin_bit_cast(f16x8, buf_load16(qbuf, off));
-        df[c] = as_bf16x8(buf_load16(gbuf, off));
+        df[c] = as_vec8<vec8<E>>(buf_load16(gbuf, off));
     }
     const float nlt = tq < T ? ws[(size_t)bh * T + tq] : 0.f;
     const float ndl = tq < T ? ws[(size_t)BH * T + (size_t)bh * T + tq] : 0.f;
@@ -222,24 +224,24 @@ __device__ __forceinline__ void dq_item(const BwdPtrs& pp, const Ring& rg, int b
 
     int n = 0;
     for (; n + NS <= nfull; n += NS) {
-        dq_step<D, 0, false>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
-        dq_step<D, 1, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 1, ntiles, wq0, lane, wave, nl, nd);
+        dq_step<D, E, 0, false>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
+        dq_step<D, E, 1, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 1, ntiles, wq0, lane, wave, nl, nd);
         if constexpr (NS > 2)
-            dq_step<D, 2, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 2, ntiles, wq0, lane, wave, nl, nd);
+            dq_step<D, E, 2, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 2, ntiles, wq0, lane, wave, nl, nd);
     }
     for (; n < ntiles; ++n) {
         const int stg = n % NS;
         if (stg == 0)
-            dq_step<D, 0, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
+            dq_step<D, E, 0, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
         else if (stg == 1)
-            dq_step<D, 1, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
+            dq_step<D, E, 1, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
         else if constexpr (NS > 2)
-            dq_step<D, 2, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
+            dq_step<D, E, 2, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
     }
     wait_vmcnt<0>();
 
     if (tq < T) {
-        bf16* out = dq + hoff + (size_t)tq * D;
+        E* out = dq + hoff + (size_t)tq * D;
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
@@ -251,7 +253,7 @@ __device__ __forceinline__ void dq_item(const BwdPtrs& pp, const Ring& rg, int b
                 for (int pr = 0; pr < 2; ++pr) {
                     const float x0 = acc[b][4 * g + 2 * pr] * scale;
                     const float x1 = acc[b][4 * g + 2 * pr + 1] * scale;
-                    w[pr] = pack_bf16x2(x0 * c2[pr] + x1 * s2[pr], x1 * c2[pr] - x0 * s2[pr]);
+                    w[pr] = pack2<E>(x0 * c2[pr] + x1 * s2[pr], x1 * c2[pr] - x0 * s2[pr]);
                 }
                 *reinterpret_cast<u32x2*>(out + d) = w;
             }
@@ -265,9 +267,9 @@ __device__ __forceinline__ void dq_item(const BwdPtrs& pp, const Ring& rg, int b
 // tile's 64 queries, then their -delta; in S and dP a lane is a key and the
 // items are queries, so these per-query offsets, read as the accumulators'
 // initial values, give x = S log2(e) - lse log2(e) and dp = dP - delta.
-template <int D, bool DIAG>
+template <int D, typename E, bool DIAG>
 __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8* kf,
-                                          const bf16x8* vf, const char* qs, const char* gs,
+                                          const vec8<E>* vf, const char* qs, const char* gs,
                                           const float* ld, const OperandOffs<D>& of, int qbase,
                                           int wk0, int lane) {
     using C = BwdTile<D>;
@@ -293,18 +295,18 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8*
             }
         }
         f32x16 x = mfma32(*reinterpret_cast<const f16x8*>(qr + of.k[0]), kf[0], nl);
-        f32x16 dp = mfma32(*reinterpret_cast<const bf16x8*>(gr + of.k[0]), vf[0], nd);
+        f32x16 dp = mfma32(*reinterpret_cast<const vec8<E>*>(gr + of.k[0]), vf[0], nd);
 #pragma unroll
         for (int c = 1; c < C::DK; ++c) {
             x = mfma32(*reinterpret_cast<const f16x8*>(qr + of.k[c]), kf[c], x);
-            dp = mfma32(*reinterpret_cast<const bf16x8*>(gr + of.k[c]), vf[c], dp);
+            dp = mfma32(*reinterpret_cast<const vec8<E>*>(gr + of.k[c]), vf[c], dp);
         }
         if (DIAG && qb == wk0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 if (item_row(i, hf) < c32) x[i] = -INFINITY;
         }
-        bf16x8 pb[2];
+        vec8<E> pb[2];
         f16x8 dsb[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -313,10 +315,10 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8*
             for (int e = 0; e < 4; ++e) {
                 const int i = 8 * j + 2 * e;
                 const float p0 = exp2_fast(x[i]), p1 = exp2_fast(x[i + 1]);
-                wp[e] = pack_bf16x2(p0, p1);
+                wp[e] = pack2<E>(p0, p1);
                 wd[e] = pack2<f16>(p0 * dp[i], p1 * dp[i + 1]);
             }
-            pb[j] = as_bf16x8(wp);
+            pb[j] = as_vec8<vec8<E>>(wp);
             dsb[j] = as_vec8<f16x8>(wd);
         }
 #pragma unroll
@@ -325,17 +327,17 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8*
             for (int j = 0; j < 2; ++j) {
                 const char* gt = gs + (32 * sb + 16 * j) * ROWB;
                 const char* qt = qs + (32 * sb + 16 * j) * ROWB;
-                dva[b] = mfma32(tr_pair<bf16x8>(gt + of.v[b][0], gt + of.v[b][1]), pb[j], dva[b]);
+                dva[b] = mfma32(tr_pair<vec8<E>>(gt + of.v[b][0], gt + of.v[b][1]), pb[j], dva[b]);
                 dka[b] = mfma32(tr_pair<f16x8>(qt + of.v[b][0], qt + of.v[b][1]), dsb[j], dka[b]);
             }
         }
     }
 }
 
-template <int D>
+template <int D, typename E>
 struct DkdvCtx {
     const f16* qh;
-    const bf16* gh;
+    const E* gh;
     const float* oh;  // this wave's per-row offsets: -lse*log2(e) (waves 0, 1) or -delta (2, 3)
     int T, wk0, lane, wave;
 
@@ -354,11 +356,11 @@ struct DkdvCtx {
 };
 
 // Step of the dk/dv kernel's query-tile loop on ring stage STG.
-template <int D, int STG, bool DIAG>
+template <int D, typename E, int STG, bool DIAG>
 __device__ __forceinline__ void dkdv_step(f32x16* dva, f32x16* dka, const f16x8* kf,
-                                          const bf16x8* vf, const Ring& rg,
+                                          const vec8<E>* vf, const Ring& rg,
                                           const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
-                                          const DkdvCtx<D>& x, int qt, int nqt) {
+                                          const DkdvCtx<D, E>& x, int qt, int nqt) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int NXT = (STG + NS - 1) % NS;
@@ -367,26 +369,26 @@ __device__ __forceinline__ void dkdv_step(f32x16* dva, f32x16* dka, const f16x8*
     else wait_vmcnt<0>();
     ring_barrier();
     if (qt + NS - 1 < nqt) x.issue(ld, qt + NS - 1, rg.k[NXT], rg.v[NXT], rg.x[NXT]);
-    dkdv_tile<D, DIAG>(dva, dka, kf, vf, rg.k[STG], rg.v[STG],
+    dkdv_tile<D, E, DIAG>(dva, dka, kf, vf, rg.k[STG], rg.v[STG],
                        reinterpret_cast<const float*>(rg.x[STG]), of, qt * C::QN, x.wk0, x.lane);
 }
 
 // dk/dv item: the 128 keys of key block kb of head bh (loops over query tiles
 // from the diagonal down; rg.k / rg.v / rg.x hold Q / dO tiles and offsets).
-template <int D>
-__device__ __forceinline__ void dkdv_item(const BwdPtrs& pp, const Ring& rg, int bh, int kb) {
+template <int D, typename E>
+__device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, int bh, int kb) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     const int T = pp.T, BH = pp.BH;
     const f16* __restrict__ qr = pp.qr;
     const f16* __restrict__ kr = pp.kr;
-    const bf16* __restrict__ v = pp.v;
-    const bf16* __restrict__ dO = pp.dO;
+    const E* __restrict__ v = pp.v;
+    const E* __restrict__ dO = pp.dO;
     const float* __restrict__ ws = pp.ws;
     const float* __restrict__ cs = pp.cs;
     const float* __restrict__ sn = pp.sn;
-    bf16* __restrict__ dk = pp.dk;
-    bf16* __restrict__ dv = pp.dv;
+    E* __restrict__ dk = pp.dk;
+    E* __restrict__ dv = pp.dv;
     const float scale = kLn2;  // dK^r = s dS^T Q^r = ln 2 * dS^T (log2(e) s Q^r)
     const int k0 = kb * C::KM;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -396,7 +398,7 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs& pp, const Ring& rg, int
     const uint32_t hbytes = (uint32_t)T * D * 2;
     const int wk0 = k0 + wave * 32;
     const int tk = wk0 + c32;
-    const DkdvCtx<D> x = {qr + hoff, dO + hoff, ws + (size_t)(wave >> 1) * BH * T + (size_t)bh * T,
+    const DkdvCtx<D, E> x = {qr + hoff, dO + hoff, ws + (size_t)(wave >> 1) * BH * T + (size_t)bh * T,
                           T, wk0, lane, wave};
     const TileLoads<D, 64, 4> ld(wave, lane);
     const OperandOffs<D> of(lane);
@@ -412,12 +414,12 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs& pp, const Ring& rg, int
 
     const rsrc_t kbuf = make_rsrc(kr + hoff, hbytes), vbuf = make_rsrc(v + hoff, hbytes);
     f16x8 kf[C::DK];
-    bf16x8 vf[C::DK];
+    vec8<E> vf[C::DK];
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) {
         const uint32_t off = (uint32_t)(tk * D + 16 * c + 8 * hf) * 2;
         kf[c] = __builtin_bit_cast(f16x8, buf_load16(kbuf, off));
-        vf[c] = as_bf16x8(buf_load16(vbuf, off));
+        vf[c] = as_vec8<vec8<E>>(buf_load16(vbuf, off));
     }
     f32x16 dva[C::DB], dka[C::DB];
 #pragma unroll
@@ -427,32 +429,32 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs& pp, const Ring& rg, int
     int qt = qt0;
     for (; qt < min(qfull, nqt); ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 0) dkdv_step<D, 0, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if (stg == 1) dkdv_step<D, 1, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if constexpr (NS > 2) dkdv_step<D, 2, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        if (stg == 0) dkdv_step<D, E, 0, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if (stg == 1) dkdv_step<D, E, 1, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if constexpr (NS > 2) dkdv_step<D, E, 2, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
     // the full tiles, rotated so that the unrolled body starts on stage 0
     for (; qt < nqt && (qt - qt0) % NS != 0; ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        if (stg == 1) dkdv_step<D, E, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if constexpr (NS > 2) dkdv_step<D, E, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
     for (; qt + NS <= nqt; qt += NS) {
-        dkdv_step<D, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 1, nqt);
-        if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 2, nqt);
+        dkdv_step<D, E, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        dkdv_step<D, E, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 1, nqt);
+        if constexpr (NS > 2) dkdv_step<D, E, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 2, nqt);
     }
     for (; qt < nqt; ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 0) dkdv_step<D, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if (stg == 1) dkdv_step<D, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if constexpr (NS > 2) dkdv_step<D, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        if (stg == 0) dkdv_step<D, E, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if (stg == 1) dkdv_step<D, E, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if constexpr (NS > 2) dkdv_step<D, E, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
     wait_vmcnt<0>();
 
     if (tk < T) {
-        bf16* ko = dk + hoff + (size_t)tk * D;
-        bf16* vo = dv + hoff + (size_t)tk * D;
+        E* ko = dk + hoff + (size_t)tk * D;
+        E* vo = dv + hoff + (size_t)tk * D;
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
@@ -464,8 +466,8 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs& pp, const Ring& rg, int
                 for (int pr = 0; pr < 2; ++pr) {
                     const float x0 = dka[b][4 * g + 2 * pr] * scale;
                     const float x1 = dka[b][4 * g + 2 * pr + 1] * scale;
-                    wk[pr] = pack_bf16x2(x0 * c2[pr] + x1 * s2[pr], x1 * c2[pr] - x0 * s2[pr]);
-                    wv[pr] = pack_bf16x2(dva[b][4 * g + 2 * pr], dva[b][4 * g + 2 * pr + 1]);
+                    wk[pr] = pack2<E>(x0 * c2[pr] + x1 * s2[pr], x1 * c2[pr] - x0 * s2[pr]);
+                    wv[pr] = pack2<E>(dva[b][4 * g + 2 * pr], dva[b][4 * g + 2 * pr + 1]);
                 }
                 *reinterpret_cast<u32x2*>(ko + d) = wk;
                 *reinterpret_cast<u32x2*>(vo + d) = wv;
@@ -479,8 +481,8 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs& pp, const Ring& rg, int
 // Item classes alternate dk/dv key block r and dq q-block nqb-1-r
 // (r = 0, 1, ...), which is heaviest first up to the 4:3 ratio of their
 // products per tile; each class holds one item per head.
-template <int D>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_bf16_kernel(BwdPtrs pp, int nqb,
+template <int D, typename E>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd16_kernel(BwdPtrs<E> pp, int nqb,
                                                                          int nkb, int kinds,
                                                                          int ncu) {
     using C = BwdTile<D>;
@@ -500,30 +502,31 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_bf16_kernel(BwdPtrs 
     const int r = c / per;
     const bool is_dkdv = kinds == 2 || (kinds == 3 && (c % 2) == 0);
     if (is_dkdv) {
-        if (r < nkb) dkdv_item<D>(pp, rg, bh, r);
+        if (r < nkb) dkdv_item<D, E>(pp, rg, bh, r);
     } else {
-        if (r < nqb) dq_item<D>(pp, rg, bh, nqb - 1 - r);
+        if (r < nqb) dq_item<D, E>(pp, rg, bh, nqb - 1 - r);
     }
 }
 
-template <int D>
+template <int D, typename E>
 static hipError_t launch_grads(const BwdArgs& a, int kinds) {
     using C = BwdTile<D>;
     const size_t n = (size_t)a.B * a.H * a.T * a.D;
     const f16* rot = static_cast<const f16*>(a.rot);
-    const BwdPtrs pp = {rot, rot + n, (const bf16*)a.v, (const bf16*)a.dO, a.ws, a.cs, a.sn,
-                        (bf16*)a.dq, (bf16*)a.dk, (bf16*)a.dv, a.B * a.H, a.T};
+    const BwdPtrs<E> pp = {rot, rot + n, (const E*)a.v, (const E*)a.dO, a.ws, a.cs, a.sn,
+                           (E*)a.dq, (E*)a.dk, (E*)a.dv, a.B * a.H, a.T};
     const int nqb = (a.T + C::QM - 1) / C::QM;
     const int nkb = (a.T + C::KM - 1) / C::KM;
     const int per = kinds == 3 ? 2 : 1;
     const int items = per * (nqb > nkb ? nqb : nkb) * a.B * a.H;
-    hipLaunchKernelGGL(bwd_bf16_kernel<D>, dim3(items), dim3(C::NT), 0, a.stream, pp, nqb, nkb,
+    hipLaunchKernelGGL((bwd16_kernel<D, E>), dim3(items), dim3(C::NT), 0, a.stream, pp, nqb, nkb,
                        kinds, device_cu_count());
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_grads_bf16(const BwdArgs& a) {
-    return a.D == 64 ? launch_grads<64>(a, 3) : launch_grads<128>(a, 3);
+hipError_t launch_bwd_grads16(const BwdArgs& a, bool f16_storage) {
+    if (f16_storage) return a.D == 64 ? launch_grads<64, f16>(a, 3) : launch_grads<128, f16>(a, 3);
+    return a.D == 64 ? launch_grads<64, bf16>(a, 3) : launch_grads<128, bf16>(a, 3);
 }
 
 }  // namespace attn

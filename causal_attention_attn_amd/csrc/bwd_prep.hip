@@ -1,14 +1,14 @@
 // Backward pre-pass: the per-row quantities the gradient kernels need,
 // delta_t = sum_d dO[t,d] o[t,d] (the row sum of P * dP, since o_t = sum_u P v_u)
-// and, for the bf16 kernels, lse_t * log2(e). They depend only on rows of o, dO
+// and, for the 16-bit kernels, lse_t * log2(e). They depend only on rows of o, dO
 // and lse, so one memory-bound pass computes them before the gradient kernels,
 // which then have no dependency on each other.
 //
 // Layout written to the workspace:
-//   bf16 path: ws[r] = -lse_r * log2(e), ws[R + r] = -delta_r  (R = B*H*T rows;
+//   bf16/fp16: ws[r] = -lse_r * log2(e), ws[R + r] = -delta_r  (R = B*H*T rows;
 //              negated because they are the initial accumulators of the
 //              S*log2(e) and dP products)
-//   fp32 path: ws[r] = delta_r
+//   fp32:      ws[r] = delta_r
 #include "device_common.h"
 #include "launchers.h"
 
@@ -16,7 +16,7 @@ namespace attn {
 
 // LPR lanes share one row; each loads 16 consecutive bytes of o and of dO, so a
 // wave reads whole rows contiguously.
-template <typename E, int D, bool BF16_LAYOUT>
+template <typename E, int D, bool HALF_LAYOUT>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const E* __restrict__ o,
                                                        const E* __restrict__ dO,
                                                        const float* __restrict__ lse,
@@ -34,8 +34,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const E* __restrict__ o,
         const u32x4 b = *reinterpret_cast<const u32x4*>(dO + e0);
         if constexpr (sizeof(E) == 2) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc += bf16_lo(a[e]) * bf16_lo(b[e]) + bf16_hi(a[e]) * bf16_hi(b[e]);
+            for (int e = 0; e < 4; ++e) {
+                const f32x2 x = unpack2<E>(a[e]), y = unpack2<E>(b[e]);
+                acc += x[0] * y[0] + x[1] * y[1];
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc += __uint_as_float(a[e]) * __uint_as_float(b[e]);
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const E* __restrict__ o,
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (row < rows && part == 0) {
-        if constexpr (BF16_LAYOUT) {
+        if constexpr (HALF_LAYOUT) {
             ws[row] = -lse[row] * kLog2e;
             ws[rows + row] = -acc;
         } else {
@@ -54,17 +56,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const E* __restrict__ o,
     }
 }
 
-template <typename E, int D, bool BF16_LAYOUT>
+template <typename E, int D, bool HALF_LAYOUT>
 static hipError_t launch_prep_t(const BwdArgs& a) {
     constexpr int LPR = D / (16 / (int)sizeof(E));
     const long rows = (long)a.B * a.H * a.T;
     const long blocks = (rows * LPR + 255) / 256;
-    hipLaunchKernelGGL((bwd_prep_kernel<E, D, BF16_LAYOUT>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_prep_kernel<E, D, HALF_LAYOUT>), dim3((unsigned)blocks), dim3(256), 0,
                        a.stream, (const E*)a.o, (const E*)a.dO, a.lse, a.ws, rows);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_prep_bf16(const BwdArgs& a) {
+hipError_t launch_bwd_prep16(const BwdArgs& a, bool f16_storage) {
+    if (f16_storage)
+        return a.D == 64 ? launch_prep_t<f16, 64, true>(a) : launch_prep_t<f16, 128, true>(a);
     return a.D == 64 ? launch_prep_t<bf16, 64, true>(a) : launch_prep_t<bf16, 128, true>(a);
 }
 

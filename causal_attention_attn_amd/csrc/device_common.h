@@ -46,15 +46,6 @@ __device__ __forceinline__ f32x16 splat16(float x) {
     return r;
 }
 
-// acc + lo(w) + hi(w) for a packed bf16 pair w (v_dot2c_f32_bf16 against 1, 1):
-// two probabilities summed per instruction, exactly the rounded values that
-// feed the following MFMA.
-__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
-    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w),
-                                           __builtin_bit_cast(b2, 0x3f803f80u), acc, false);
-}
-
 // Work item of workgroup `bid` when items are numbered heaviest first and the
 // dispatcher hands workgroups to the ncu CUs in rounds (workgroup r*ncu + c
 // lands on CU c in round r). Odd rounds take their items in reverse, so a CU
@@ -84,6 +75,37 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, T2));
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) { return pack2<bf16>(lo, hi); }
+
+// 16-bit storage types of the fast path (bf16 or fp16): 8-wide vectors,
+// unpacking of a packed pair, and the sum of a packed pair.
+template <typename E>
+struct Vec8 {
+    typedef E type __attribute__((ext_vector_type(8)));
+};
+template <typename E>
+using vec8 = typename Vec8<E>::type;
+
+template <typename E>
+__device__ __forceinline__ f32x2 unpack2(uint32_t w) {
+    typedef E E2 __attribute__((ext_vector_type(2)));
+    return __builtin_convertvector(__builtin_bit_cast(E2, w), f32x2);
+}
+
+// acc + lo(w) + hi(w) for a packed pair w, one v_dot2c against (1, 1): two
+// probabilities summed per instruction, exactly the rounded values that feed
+// the following MFMA.
+template <typename E>
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+    if constexpr (__is_same(E, bf16)) {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w),
+                                               __builtin_bit_cast(b2, 0x3f803f80u), acc, false);
+    } else {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), __builtin_bit_cast(h2, 0x3c003c00u),
+                                      acc, false);
+    }
+}
 
 template <typename V>
 __device__ __forceinline__ V as_vec8(u32x4 w) { return __builtin_bit_cast(V, w); }

@@ -1,4 +1,5 @@
-// Forward pass of causal RoPE attention, bf16 storage / fp32 accumulation, gfx950.
+// Forward pass of causal RoPE attention, 16-bit storage (bf16 or fp16, type E)
+// with fp32 accumulation, gfx950.
 //
 // FlashAttention-style exact attention ("Show HN: NanoEuler", paragraph 2): the
 // score matrix is produced tile by tile in registers, a running row maximum and
@@ -13,14 +14,15 @@
 //     B operand of S^T = K Q^T (v_mfma_f32_32x32x16_f16, k = head dim). The
 //     rotated q and k are not bf16 values; fp16's 11-bit significand keeps the
 //     score error small where the softmax is sharp (bf16 operands give ~3e-2
-//     error on O for logits of standard deviation ~9). P and V stay bf16.
-//   * 64-key tiles of rotated K (fp16) and V (bf16) stream straight from
+//     error on O for logits of standard deviation ~9). P and V are of the
+//     storage type E (P is rounded to E before the PV product).
+//   * 64-key tiles of rotated K (fp16) and V (E) stream straight from
 //     global memory into an NS-stage LDS ring (buffer_load ... lds), issued
 //     NS-1 tiles ahead of use: no registers hold tiles in flight, and one
 //     barrier per tile both publishes a tile and frees the oldest stage;
 //   * S^T puts one query per lane column, so each lane owns one query's running
 //     max/sum; the running maximum enters as the MFMA's initial accumulator, so
-//     the per-element softmax work is exp2, bf16 rounding and a packed pair sum
+//     the per-element softmax work is exp2, rounding to E and a packed pair sum
 //     (the exact tile maximum is only taken when the probabilities would leave
 //     their bound, see fwd_tile);
 //   * the rounded probabilities of S^T are directly the B operand of
@@ -60,11 +62,11 @@ struct FwdState {
     float m, l;
 };
 
-// Probabilities p = 2^x of the tile's live 32-key blocks, rounded to bf16 and
+// Probabilities p = 2^x of the tile's live 32-key blocks, rounded to E and
 // packed as the B operand of O^T += V^T P^T; returns this lane's sum of the
 // rounded values.
-template <int D, bool DIAG>
-__device__ __forceinline__ float fwd_probs(const f32x16* x, bf16x8 (*pb)[2], int k0, int wq0) {
+template <int D, typename E, bool DIAG>
+__device__ __forceinline__ float fwd_probs(const f32x16* x, vec8<E> (*pb)[2], int k0, int wq0) {
     using C = FwdTile<D>;
     float part[C::NSB][2];
 #pragma unroll
@@ -76,11 +78,11 @@ __device__ __forceinline__ float fwd_probs(const f32x16* x, bf16x8 (*pb)[2], int
             float a = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                w[e] = pack_bf16x2(exp2_fast(x[sb][8 * j + 2 * e]),
-                                   exp2_fast(x[sb][8 * j + 2 * e + 1]));
-                a = add_bf16x2(w[e], a);
+                w[e] = pack2<E>(exp2_fast(x[sb][8 * j + 2 * e]),
+                                exp2_fast(x[sb][8 * j + 2 * e + 1]));
+                a = add_pair<E>(w[e], a);
             }
-            pb[sb][j] = as_bf16x8(w);
+            pb[sb][j] = as_vec8<vec8<E>>(w);
             part[sb][j] = a;
         }
     }
@@ -142,14 +144,14 @@ __device__ __forceinline__ void fwd_scores(f32x16* x, const FwdState<D>& st, con
 // (and on the wave's first tile, which sets m) the exact maximum is taken, O
 // and l are rescaled and the tile's probabilities are recomputed. The V^T
 // operands are read from LDS first, so their latency overlaps the softmax.
-template <int D, bool DIAG>
+template <int D, typename E, bool DIAG>
 __device__ __forceinline__ void fwd_softmax_pv(FwdState<D>& st, f32x16* x, const char* vs,
                                                const OperandOffs<D>& of, int k0, int wq0,
                                                bool first) {
     using C = FwdTile<D>;
     constexpr float kLimit = 256.f;
     constexpr int ROWB = 2 * D;
-    bf16x8 va[C::NSB][C::DB][2];
+    vec8<E> va[C::NSB][C::DB][2];
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
         if (DIAG && k0 + 32 * sb > wq0) break;
@@ -158,14 +160,14 @@ __device__ __forceinline__ void fwd_softmax_pv(FwdState<D>& st, f32x16* x, const
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const char* vb = vs + (32 * sb + 16 * j) * ROWB;
-                va[sb][b][j] = tr_pair<bf16x8>(vb + of.v[b][0], vb + of.v[b][1]);
+                va[sb][b][j] = tr_pair<vec8<E>>(vb + of.v[b][0], vb + of.v[b][1]);
             }
     }
-    bf16x8 pb[C::NSB][2];
+    vec8<E> pb[C::NSB][2];
     float ts = 0.f;
     bool slow = first;
     if (!first) {
-        ts = fwd_probs<D, DIAG>(x, pb, k0, wq0);
+        ts = fwd_probs<D, E, DIAG>(x, pb, k0, wq0);
         slow = wave_any(ts > kLimit);
     }
     if (slow) {
@@ -193,7 +195,7 @@ __device__ __forceinline__ void fwd_softmax_pv(FwdState<D>& st, f32x16* x, const
             if (DIAG && k0 + 32 * sb > wq0) break;
             x[sb] -= d;
         }
-        ts = fwd_probs<D, DIAG>(x, pb, k0, wq0);
+        ts = fwd_probs<D, E, DIAG>(x, pb, k0, wq0);
     }
     st.l += ts;
 #pragma unroll
@@ -207,10 +209,10 @@ __device__ __forceinline__ void fwd_softmax_pv(FwdState<D>& st, f32x16* x, const
 }
 
 // Shared state of one workgroup's pass over its key tiles.
-template <int D>
+template <int D, typename E>
 struct FwdCtx {
     const f16* kr;
-    const bf16* v;
+    const E* v;
     int T, wq0, lane, wave;
 };
 
@@ -220,10 +222,10 @@ struct FwdCtx {
 // last reads were made before it) and refill that stage with tile n+NS-1;
 // finish tile n (its V operands are read before the softmax, which hides their
 // latency) and read tile n+1's K operands while the PV products run.
-template <int D, int STG, bool DIAG>
+template <int D, typename E, int STG, bool DIAG>
 __device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, KOps<D>& kr,
                                          const Ring& rg, const TileLoads<D, 64, 4>& ld,
-                                         const OperandOffs<D>& of, const FwdCtx<D>& x, int n) {
+                                         const OperandOffs<D>& of, const FwdCtx<D, E>& x, int n) {
     using C = FwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int NXT = (STG + 1) % NS;
@@ -237,14 +239,14 @@ __device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, KOps<
     const int nx = n + NS - 1;
     ld.issue(x.kr, x.T, nx * C::BN, rg.k[FREE], x.wave);
     ld.issue(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave);
-    if (live) fwd_softmax_pv<D, DIAG>(st, s, rg.v[STG], of, k0, x.wq0, n == 0);
+    if (live) fwd_softmax_pv<D, E, DIAG>(st, s, rg.v[STG], of, k0, x.wq0, n == 0);
     read_k(kr, rg.k[NXT], of);
 }
 
-template <int D>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
-    const f16* __restrict__ qr, const f16* __restrict__ kr, const bf16* __restrict__ v,
-    bf16* __restrict__ o, float* __restrict__ lse, int BH, int T, int nqb, int ncu) {
+template <int D, typename E>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
+    const f16* __restrict__ qr, const f16* __restrict__ kr, const E* __restrict__ v,
+    E* __restrict__ o, float* __restrict__ lse, int BH, int T, int nqb, int ncu) {
     using C = FwdTile<D>;
     constexpr int NS = C::NS;
     // one __shared__ object per ring stage (see Ring); stages >= NS are stubs
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     const size_t hoff = (size_t)bh * T * D;
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
-    const FwdCtx<D> x = {kr + hoff, v + hoff, T, wq0, lane, wave};
+    const FwdCtx<D, E> x = {kr + hoff, v + hoff, T, wq0, lane, wave};
     const TileLoads<D, 64, 4> ld(wave, lane);
     const OperandOffs<D> of(lane);
 
@@ -303,12 +305,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     int n = 0;
     // full tiles: branch-free bodies, ring stages as compile-time constants
     for (; n + NS <= nfull; n += NS)
-        static_for<NS>([&](auto S) { fwd_step<D, S, false>(st, qf, kops, rg, ld, of, x, n + S); });
+        static_for<NS>([&](auto S) { fwd_step<D, E, S, false>(st, qf, kops, rg, ld, of, x, n + S); });
     // the rest (at most NS-1 full tiles, then the diagonal tiles)
     for (; n < ntiles; ++n) {
         const int stg = n % NS;
         static_for<NS>([&](auto S) {
-            if (stg == S) fwd_step<D, S, true>(st, qf, kops, rg, ld, of, x, n);
+            if (stg == S) fwd_step<D, E, S, true>(st, qf, kops, rg, ld, of, x, n);
         });
     }
     wait_vmcnt<0>();  // no LDS writes may land after this workgroup's LDS is released
@@ -316,14 +318,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     const float l_tot = sum_across_halves(st.l);
     if (tq < T) {
         const float inv = 1.f / l_tot;
-        bf16* orow = o + hoff + (size_t)tq * D;
+        E* orow = o + hoff + (size_t)tq * D;
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 u32x2 w;
-                w[0] = pack_bf16x2(st.o[b][4 * g] * inv, st.o[b][4 * g + 1] * inv);
-                w[1] = pack_bf16x2(st.o[b][4 * g + 2] * inv, st.o[b][4 * g + 3] * inv);
+                w[0] = pack2<E>(st.o[b][4 * g] * inv, st.o[b][4 * g + 1] * inv);
+                w[1] = pack2<E>(st.o[b][4 * g + 2] * inv, st.o[b][4 * g + 3] * inv);
                 *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * g + 4 * hf) = w;
             }
         }
@@ -331,21 +333,32 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_kernel(
     }
 }
 
-template <int D>
+// Explicit instantiations: the host pass does not always emit the launch stub of
+// a kernel template with a 16-bit element-type argument on its own.
+template __global__ void fwd16_kernel<64, bf16>(const f16*, const f16*, const bf16*, bf16*, float*,
+                                                int, int, int, int);
+template __global__ void fwd16_kernel<128, bf16>(const f16*, const f16*, const bf16*, bf16*,
+                                                 float*, int, int, int, int);
+template __global__ void fwd16_kernel<64, f16>(const f16*, const f16*, const f16*, f16*, float*,
+                                               int, int, int, int);
+template __global__ void fwd16_kernel<128, f16>(const f16*, const f16*, const f16*, f16*, float*,
+                                                int, int, int, int);
+
+template <int D, typename E>
 static hipError_t launch_fwd(const FwdArgs& a) {
     using C = FwdTile<D>;
     const int BH = a.B * a.H;
     const int nqb = (a.T + C::BM - 1) / C::BM;
     const size_t n = (size_t)a.B * a.H * a.T * a.D;
     const f16* rot = static_cast<const f16*>(a.rot);
-    hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(nqb * BH), dim3(C::NT), 0, a.stream, rot,
-                       rot + n, (const bf16*)a.v, (bf16*)a.o, a.lse, BH, a.T, nqb,
-                       device_cu_count());
+    hipLaunchKernelGGL((fwd16_kernel<D, E>), dim3(nqb * BH), dim3(C::NT), 0, a.stream, rot,
+                       rot + n, (const E*)a.v, (E*)a.o, a.lse, BH, a.T, nqb, device_cu_count());
     return hipGetLastError();
 }
 
-hipError_t launch_fwd_bf16(const FwdArgs& a) {
-    return a.D == 64 ? launch_fwd<64>(a) : launch_fwd<128>(a);
+hipError_t launch_fwd16(const FwdArgs& a, bool f16_storage) {
+    if (f16_storage) return a.D == 64 ? launch_fwd<64, f16>(a) : launch_fwd<128, f16>(a);
+    return a.D == 64 ? launch_fwd<64, bf16>(a) : launch_fwd<128, bf16>(a);
 }
 
 }  // namespace attn

@@ -10,7 +10,7 @@ namespace attn {
 struct FwdArgs {
     const void *q, *k, *v;
     const float *cs, *sn;
-    const void* rot;  // bf16 path: rotated q * log2(e)/sqrt(D), then rotated k, [B, H, T, D] fp16 each
+    const void* rot;  // 16-bit path: rotated q * log2(e)/sqrt(D), then rotated k, [B, H, T, D] fp16 each
     void* o;
     float* lse;
     int B, H, T, D;
@@ -20,9 +20,9 @@ struct FwdArgs {
 struct BwdArgs {
     const void *q, *k, *v, *o, *dO;
     const float *lse, *cs, *sn;
-    const void* rot;  // bf16 path: rotated q * log2(e)/sqrt(D), then rotated k, [B, H, T, D] fp16 each
+    const void* rot;  // 16-bit path: rotated q * log2(e)/sqrt(D), then rotated k, [B, H, T, D] fp16 each
     void *dq, *dk, *dv;
-    float* ws;  // workspace (written by the pre-pass): bf16 path [B, H, T] -lse*log2(e),
+    float* ws;  // workspace (written by the pre-pass): 16-bit path [B, H, T] -lse*log2(e),
                 // then [B, H, T] -delta; fp32 path [B, H, T] delta
     int B, H, T, D;
     hipStream_t stream;
@@ -32,12 +32,13 @@ struct BwdArgs {
 int device_cu_count();
 
 hipError_t launch_rope_tables(float* cs, float* sn, int T, int D, double base, hipStream_t s);
+// The 16-bit path (bf16 or, with f16_storage, fp16 tensors).
 hipError_t launch_rotate_qk(const void* q, const void* k, const float* cs, const float* sn,
-                            void* out, int B, int H, int T, int D, hipStream_t s);
-
-hipError_t launch_fwd_bf16(const FwdArgs& a);
-hipError_t launch_bwd_prep_bf16(const BwdArgs& a);   // workspace entries (bf16 layout)
-hipError_t launch_bwd_grads_bf16(const BwdArgs& a);  // dq, dk, dv in one launch
+                            void* out, int B, int H, int T, int D, bool f16_storage,
+                            hipStream_t s);
+hipError_t launch_fwd16(const FwdArgs& a, bool f16_storage);
+hipError_t launch_bwd_prep16(const BwdArgs& a, bool f16_storage);   // workspace entries
+hipError_t launch_bwd_grads16(const BwdArgs& a, bool f16_storage);  // dq, dk, dv in one launch
 
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_prep_f32(const BwdArgs& a);    // workspace entries (delta)

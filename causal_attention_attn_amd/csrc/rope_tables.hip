@@ -35,12 +35,12 @@ hipError_t launch_rope_tables(float* cs, float* sn, int T, int D, double base, h
 // Rotate q and k once: out[0] = qs * R q, out[1] = R k, both [B, H, T, D] fp16
 // (rounded once from the fp32 rotation). qs = log2(e)/sqrt(D) folds the score
 // scale and the change to base-2 exponentials into the query, so a score
-// product comes out of the MFMA directly as S * log2(e). The bf16 kernels read
+// product comes out of the MFMA directly as S * log2(e). The 16-bit kernels read
 // these instead of applying RoPE per tile. One thread per 8 consecutive
 // features of one row, for q and k together (one cos/sin read serves both).
-template <int D>
-__global__ __launch_bounds__(256) void rotate_qk_kernel(const bf16* __restrict__ q,
-                                                        const bf16* __restrict__ k,
+template <int D, typename E>
+__global__ __launch_bounds__(256) void rotate_qk_kernel(const E* __restrict__ q,
+                                                        const E* __restrict__ k,
                                                         const float* __restrict__ cs,
                                                         const float* __restrict__ sn,
                                                         f16* __restrict__ out, int T,
@@ -58,8 +58,8 @@ __global__ __launch_bounds__(256) void rotate_qk_kernel(const bf16* __restrict__
     u32x4 rq, rk;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const float q0 = bf16_lo(wq[p]), q1 = bf16_hi(wq[p]);
-        const float k0 = bf16_lo(wk[p]), k1 = bf16_hi(wk[p]);
+        const f32x2 qp = unpack2<E>(wq[p]), kp = unpack2<E>(wk[p]);
+        const float q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
         rq[p] = pack2<f16>((q0 * cv[p] - q1 * sv[p]) * qs, (q0 * sv[p] + q1 * cv[p]) * qs);
         rk[p] = pack2<f16>(k0 * cv[p] - k1 * sv[p], k0 * sv[p] + k1 * cv[p]);
     }
@@ -67,18 +67,26 @@ __global__ __launch_bounds__(256) void rotate_qk_kernel(const bf16* __restrict__
     *reinterpret_cast<u32x4*>(out + (size_t)chunks * 8 + e0) = rk;
 }
 
-hipError_t launch_rotate_qk(const void* q, const void* k, const float* cs, const float* sn,
-                            void* out, int B, int H, int T, int D, hipStream_t st) {
+template <typename E>
+static hipError_t launch_rotate_t(const void* q, const void* k, const float* cs, const float* sn,
+                                  void* out, int B, int H, int T, int D, hipStream_t st) {
     const int chunks = (int)((long)B * H * T * D / 8);
     const int blocks = (chunks + 255) / 256;
     const float qs = kLog2e / sqrtf((float)D);
     if (D == 64)
-        hipLaunchKernelGGL(rotate_qk_kernel<64>, dim3(blocks), dim3(256), 0, st, (const bf16*)q,
-                           (const bf16*)k, cs, sn, (f16*)out, T, chunks, qs);
+        hipLaunchKernelGGL((rotate_qk_kernel<64, E>), dim3(blocks), dim3(256), 0, st, (const E*)q,
+                           (const E*)k, cs, sn, (f16*)out, T, chunks, qs);
     else
-        hipLaunchKernelGGL(rotate_qk_kernel<128>, dim3(blocks), dim3(256), 0, st, (const bf16*)q,
-                           (const bf16*)k, cs, sn, (f16*)out, T, chunks, qs);
+        hipLaunchKernelGGL((rotate_qk_kernel<128, E>), dim3(blocks), dim3(256), 0, st, (const E*)q,
+                           (const E*)k, cs, sn, (f16*)out, T, chunks, qs);
     return hipGetLastError();
+}
+
+hipError_t launch_rotate_qk(const void* q, const void* k, const float* cs, const float* sn,
+                            void* out, int B, int H, int T, int D, bool f16_storage,
+                            hipStream_t st) {
+    return f16_storage ? launch_rotate_t<f16>(q, k, cs, sn, out, B, H, T, D, st)
+                       : launch_rotate_t<bf16>(q, k, cs, sn, out, B, H, T, D, st);
 }
 
 }  // namespace attn

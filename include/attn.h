@@ -27,8 +27,10 @@
  *     contiguous row-major [B, H, T, D] with D innermost; lse and the backward
  *     workspace hold [B, H, T] fp32; cos/sin tables are [T, D/2] fp32.
  *   - dtype is ATTN_BF16 (bf16 storage, fp32 accumulation; rotated q/k and dS
- *     are carried in fp16 inside the kernels) or ATTN_F32 (fp32 everywhere); it
- *     applies to q, k, v, o, dO, dq, dk and dv.
+ *     are carried in fp16 inside the kernels), ATTN_F16 (the same kernels with
+ *     fp16 storage, so P, V and dO are fp16 operands too) or ATTN_F32 (fp32
+ *     everywhere); it applies to q, k, v, o, dO, dq, dk and dv. "The 16-bit
+ *     path" below means ATTN_BF16 and ATTN_F16.
  *   - D in {64, 128}; T >= 1; B*H >= 1; B*H*T*D < 2^31. The scale is fixed at
  *     1/sqrt(D). There is no dropout, bias, padding mask or grouped-query sharing.
  *   - The caller owns all memory. The library never allocates, frees or
@@ -49,7 +51,7 @@
 extern "C" {
 #endif
 
-enum attn_dtype { ATTN_BF16 = 0, ATTN_F32 = 1 };
+enum attn_dtype { ATTN_BF16 = 0, ATTN_F32 = 1, ATTN_F16 = 2 };
 
 enum attn_status {
     ATTN_OK = 0,
@@ -78,7 +80,7 @@ int attn_rope_tables(float* cos_tab, float* sin_tab, int T, int D, double base,
 
 /*
  * attn_saved_bytes - size of the "saved" buffer that attn_fwd fills and the
- * backward reads: for ATTN_BF16 the RoPE-rotated q (times log2(e)/sqrt(D)) and
+ * backward reads: for the 16-bit path the RoPE-rotated q (times log2(e)/sqrt(D)) and
  * the RoPE-rotated k, each [B,H,T,D] fp16 (4*B*H*T*D bytes, rounded up to 256);
  * 0 for ATTN_F32, whose kernels rotate on load. Returns 0 for arguments the
  * other calls would reject.
@@ -108,10 +110,10 @@ int attn_rotate_qk(const void* q, const void* k, const float* cos_tab, const flo
  *   cos_tab, sin_tab  [T,D/2] fp32 from attn_rope_tables (or equal values)
  *   o         [B,H,T,D] dtype, output
  *   lse       [B,H,T] fp32, output
- *   saved     ATTN_BF16: device buffer of attn_saved_bytes(); receives the
+ *   saved     16-bit path: device buffer of attn_saved_bytes(); receives the
  *             rotated q and k (attn_rotate_qk) and must be handed to the
  *             backward. ATTN_F32: ignored, may be NULL.
- * ATTN_BF16 enqueues attn_rotate_qk then attn_fwd_rotated.
+ * The 16-bit path enqueues attn_rotate_qk then attn_fwd_rotated.
  */
 int attn_fwd(const void* q, const void* k, const void* v,
              const float* cos_tab, const float* sin_tab,
@@ -119,7 +121,7 @@ int attn_fwd(const void* q, const void* k, const void* v,
              int B, int H, int T, int D, int dtype, void* stream);
 
 /*
- * attn_fwd_rotated - the forward kernel alone (ATTN_BF16 only; ATTN_F32 gets
+ * attn_fwd_rotated - the forward kernel alone (16-bit path only; ATTN_F32 gets
  * ATTN_ERR_DTYPE): o and lse from the rotated q and k already in `saved`
  * (attn_rotate_qk) and from v.
  */
@@ -128,7 +130,7 @@ int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void*
 
 /*
  * attn_bwd_workspace_bytes - device workspace the backward needs: for
- * ATTN_BF16 -lse_t * log2 e of every row ([B,H,T] fp32) followed by -delta_t
+ * the 16-bit path -lse_t * log2 e of every row ([B,H,T] fp32) followed by -delta_t
  * of every row ([B,H,T] fp32), 8*B*H*T bytes; for ATTN_F32 delta_t alone
  * (4*B*H*T bytes); rounded up to 256, where delta_t = sum_d dO[t,d] o[t,d].
  * Returns 0 for arguments attn_bwd would reject.
@@ -142,13 +144,13 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype);
  * Recompute-based: P is rebuilt from q, k and lse; nothing of size T x T is
  * stored. Enqueues attn_bwd_prep then attn_bwd_grads on `stream`.
  *   q, k, v, o, dO  [B,H,T,D] dtype, inputs (o and lse from attn_fwd); the
- *                   ATTN_BF16 kernels take the rotated q and k from `saved`
+ *                   16-bit kernels take the rotated q and k from `saved`
  *   lse             [B,H,T] fp32, input
- *   saved           ATTN_BF16: the buffer attn_fwd filled for these q and k
+ *   saved           16-bit path: the buffer attn_fwd filled for these q and k
  *                   (or attn_rotate_qk); ATTN_F32: ignored, may be NULL
  *   dq, dk, dv      [B,H,T,D] dtype, outputs (overwritten)
  *   workspace       device buffer of at least attn_bwd_workspace_bytes()
- * ATTN_BF16 rounds dS = P (dP - delta) to fp16 for the dq/dk products, so
+ * The 16-bit path rounds dS = P (dP - delta) to fp16 for the dq/dk products, so
  * |dS| must stay below 65504 (true whenever |dO_t|*|v_u| < 32752 in L2 norm).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -162,7 +164,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
 /*
  * attn_bwd_prep - first stage of attn_bwd, the per-row pre-pass of the
  * recompute-based backward: delta_t = sum_d dO[t,d] o[t,d] (equal to
- * sum_u P[t,u] dP[t,u], the softmax Jacobian term) and, for ATTN_BF16,
+ * sum_u P[t,u] dP[t,u], the softmax Jacobian term) and, for the 16-bit path,
  * lse_t * log2 e, written to the workspace in the layout of
  * attn_bwd_workspace_bytes. o, dO [B,H,T,D] dtype and lse [B,H,T] fp32 are
  * inputs; the workspace must not alias them.
@@ -175,7 +177,7 @@ int attn_bwd_prep(const void* o, const void* dO, const float* lse,
  * attn_bwd_grads - second stage of attn_bwd: writes dq, dk (w.r.t. the pre-RoPE
  * q and k) and dv. Reads the workspace entries of attn_bwd_prep, which must
  * have been enqueued before it on the same stream (or completed) for the same
- * o, dO and lse. Same arguments and rules as attn_bwd, minus o; for ATTN_BF16
+ * o, dO and lse. Same arguments and rules as attn_bwd, minus o; on the 16-bit path
  * dq and dk/dv come from one launch.
  */
 int attn_bwd_grads(const void* q, const void* k, const void* v,

@@ -90,7 +90,7 @@ def test_fwd_rejects_bad_arguments(lib):
     assert f(T=0) == 2
     assert f(B=0) == 2
     assert f(B=1 << 16, H=1 << 10, T=1 << 10) == 2      # 2^42 elements
-    assert f(dtype=2) == 3
+    assert f(dtype=3) == 3
     assert f(k=MIS) == 4
     assert f(o=FAKE) == 7                                 # o aliases q
     assert f(lse=FAKE + 32) == 7                          # lse aliases v

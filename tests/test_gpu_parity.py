@@ -32,12 +32,16 @@ SMALL = [(1, 1, 1), (1, 1, 3), (1, 2, 63), (1, 1, 64), (2, 1, 65), (1, 3, 127), 
          (1, 2, 200), (1, 1, 257), (2, 2, 333)]
 
 
+HALF = {"bf16": workloads.HEADLINE, "f16": "gpt2s_f16_b8h12t1024d64"}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("B,H,T", SMALL)
-def test_bf16_small_shapes(B, H, T, D):
-    w = workloads.WORKLOADS[workloads.HEADLINE]
+def test_16bit_small_shapes(B, H, T, D, dtype):
+    w = workloads.WORKLOADS[HALF[dtype]]
     x = workloads.make(w, seed=T + D, shape=(B, H, T, D))
-    assert_close(gpu_run(x), oracle_run(x), "bf16", f"bf16 B{B} H{H} T{T} D{D}")
+    assert_close(gpu_run(x), oracle_run(x), dtype, f"{dtype} B{B} H{H} T{T} D{D}")
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -56,6 +60,7 @@ def test_peaky_logits_small():
 
 FULL = [
     ("gpt2s_bf16_b8h12t1024d64", [(0, 0), (3, 7), (7, 11)]),
+    ("gpt2s_f16_b8h12t1024d64", [(0, 0), (7, 11)]),
     ("longctx_bf16_b2h12t4096d64", [(0, 0), (1, 11)]),
     ("peaky_bf16_b16h12t2048d64", [(0, 0), (15, 11)]),
     ("wide_bf16_b1h6t8192d128", [(0, 5)]),
@@ -69,7 +74,7 @@ def test_full_size_workloads_on_sampled_heads(name, heads):
     w = workloads.WORKLOADS[name]
     x = workloads.make(w)
     got = gpu_run(x)
-    assert_close(select_heads(got, heads), oracle_run(x, heads=heads), "bf16", name)
+    assert_close(select_heads(got, heads), oracle_run(x, heads=heads), w.dtype, name)
 
 
 def test_row_zero_is_v_zero_bitwise():

@@ -27,7 +27,7 @@ class Workload:
     H: int
     T: int
     D: int
-    dtype: str                 # "bf16" or "f32"
+    dtype: str                 # "bf16", "f16" or "f32"
     qk: tuple = ("normal", 1.0)
     v: tuple = ("normal", 1.0)
     do: tuple = ("normal", 0.1)
@@ -46,6 +46,8 @@ WORKLOADS = {
                  do=("normal", 1.0)),
         # one attention layer of the 12-head, 768-wide model at T = 1024
         Workload("gpt2s_bf16_b8h12t1024d64", 8, 12, 1024, 64, "bf16"),
+        # the same layer with fp16 tensors
+        Workload("gpt2s_f16_b8h12t1024d64", 8, 12, 1024, 64, "f16"),
         # byte-level long context, most key tiles above the diagonal skipped
         Workload("longctx_bf16_b2h12t4096d64", 2, 12, 4096, 64, "bf16"),
         # peaky logits (q, k with std 3) and bounded values
@@ -82,7 +84,7 @@ def draw(shape, qk=("normal", 1.0), v=("normal", 1.0), do=("normal", 0.1), seed=
 
 def torch_dtype(dtype):
     import torch
-    return {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
 
 
 def make(workload, seed=0, shape=None):
@@ -100,6 +102,6 @@ def make(workload, seed=0, shape=None):
 
 
 def as_float64(t):
-    """Exact float64 copy of a (bf16 or fp32) CPU tensor, as a numpy array."""
+    """Exact float64 copy of a (bf16, fp16 or fp32) CPU tensor, as a numpy array."""
     import torch
     return t.detach().to("cpu", torch.float64).numpy()
