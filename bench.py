@@ -11,9 +11,9 @@ uses the causal FLOP convention: forward 2*B*H*T^2*D, backward 2.5x forward.
 
 Prints ONE JSON line. The headline value is the whole step's rate over K
 steps launched back to back between two HIP events. Besides it the line carries
-  kernels       each kernel's average duration, from R back-to-back launches of
-                that kernel alone between two HIP events on the kernels' stream
-                (five rounds);
+  kernels       each kernel's average duration inside a step, from further
+                steps with a HIP event on the kernels' stream between kernels
+                (five rounds of R steps; min/max over the rounds);
   roofline      for the kernel with the longest average duration;
   cpu_baseline  the float64 oracle timed on this host's cores on a bounded
                 sample of the same workload (and a parity check of the GPU
@@ -52,6 +52,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96,
                     help="heads of the workload the CPU oracle runs on")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU oracle's passes until this much time has gone by")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes three times (the "
                          "reference point that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -136,23 +138,28 @@ def main():
     ms_step = start.elapsed_time(end) / K
     print(f"# timed {K} steps in {wall:.3f} s wall", file=sys.stderr, flush=True)
 
-    # per-kernel durations: each kernel launched R times back to back between two HIP
-    # events on the kernels' stream, repeated in rounds (an event between every launch
-    # would add its own gap to each interval); inputs are those of the timed steps
+    # per-kernel durations: R more whole steps with a HIP event on the kernels' stream
+    # before and after every kernel, in five rounds; each interval is one kernel's share
+    # of a step as it runs inside the step (its launch included), which is also what a
+    # kernel trace reports as that dispatch's duration
     R = max(1, min(K, 50))
-    per = {}
-    for n, f in (("rotate_kernel", rotate), ("fwd_kernel", fwd), ("bwd_prep_kernel", bwd_prep),
-                 ("bwd_grads_kernel", bwd_grads)):
-        samples = []
-        for _ in range(5):
-            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a_ev.record(stream)
-            for _ in range(R):
+    order = (("rotate_kernel", rotate), ("fwd_kernel", fwd), ("bwd_prep_kernel", bwd_prep),
+             ("bwd_grads_kernel", bwd_grads))
+    per = {n: [] for n, _ in order}
+    for _ in range(5):
+        evs = []
+        for _ in range(R):
+            row = [torch.cuda.Event(enable_timing=True)]
+            row[0].record(stream)
+            for _, f in order:
                 f()
-            b_ev.record(stream)
-            torch.cuda.synchronize()
-            samples.append(a_ev.elapsed_time(b_ev) / R)
-        per[n] = np.array(samples)
+                row.append(torch.cuda.Event(enable_timing=True))
+                row[-1].record(stream)
+            evs.append(row)
+        torch.cuda.synchronize()
+        for i, (n, _) in enumerate(order):
+            per[n].append(np.mean([row[i].elapsed_time(row[i + 1]) for row in evs]))
+    per = {n: np.array(v) for n, v in per.items()}
     # leave every output as one full step writes it (for the parity check below)
     rotate(); fwd(); bwd_prep(); bwd_grads()
     torch.cuda.synchronize()
@@ -182,7 +189,8 @@ def main():
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
-        cpu, parity = cpu_baseline(w, x, dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv), args.cpu_heads)
+        cpu, parity = cpu_baseline(w, x, dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv), args.cpu_heads,
+                                   args.cpu_seconds)
 
     line = {
         "metric": METRIC,
@@ -244,9 +252,10 @@ def measured_traffic(kernel, workload):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(w, x, gpu_out, heads):
+def cpu_baseline(w, x, gpu_out, heads, min_seconds):
     """Time the float64 oracle (as it stands) on the first `heads` heads of the
-    same inputs and compare the GPU outputs on those heads."""
+    same inputs, repeating whole forward + backward passes until at least
+    `min_seconds` have gone by, and compare the GPU outputs on those heads."""
     import numpy as np
 
     import oracle
@@ -261,23 +270,33 @@ def cpu_baseline(w, x, gpu_out, heads):
     B, H, T, D = w.shape
     heads = max(1, min(heads, B * H))
     sel = [(i // H, i % H) for i in range(heads)]
-    f = {n: np.stack([workloads.as_float64(t)[b, h] for b, h in sel])[None]
-         for n, t in x.items()}
-    t0 = time.perf_counter()
-    ro, rl = oracle.attention_forward(f["q"], f["k"], f["v"], base=w.base)
-    t1 = time.perf_counter()
-    rg = oracle.attention_backward(f["q"], f["k"], f["v"], f["do"], base=w.base)
-    t2 = time.perf_counter()
+    def pick(t):  # the selected heads as one (1, heads, T, D) float64 array
+        a = workloads.as_float64(t)
+        return np.stack([a[b, h] for b, h in sel])[None]
+
+    f = {n: pick(t) for n, t in x.items()}
+    t_fwd = t_bwd = 0.0
+    passes = 0
+    while passes == 0 or t_fwd + t_bwd < min_seconds:
+        t0 = time.perf_counter()
+        ro, rl = oracle.attention_forward(f["q"], f["k"], f["v"], base=w.base)
+        t1 = time.perf_counter()
+        rg = oracle.attention_backward(f["q"], f["k"], f["v"], f["do"], base=w.base)
+        t2 = time.perf_counter()
+        t_fwd += t1 - t0
+        t_bwd += t2 - t1
+        passes += 1
     fl = causal_flops(1, heads, T, D)
-    secs = t2 - t0
-    cpu = {"value": round((fl["fwd"] + fl["bwd"]) / secs / 1e12, 6), "unit": "TFLOP/s",
+    secs = t_fwd + t_bwd
+    cpu = {"value": round(passes * (fl["fwd"] + fl["bwd"]) / secs / 1e12, 6), "unit": "TFLOP/s",
            "cores": blas_threads, "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-           "sample": f"{heads} of {B * H} heads (all T={T} rows), fwd {t1 - t0:.2f} s + "
-                     f"bwd {t2 - t1:.2f} s, numpy float64 full T x T matrices, causal FLOP count"}
+           "sample": f"{heads} of {B * H} heads (all T={T} rows), {passes} passes of fwd + bwd "
+                     f"({t_fwd:.2f} s + {t_bwd:.2f} s), numpy float64 full T x T matrices, "
+                     f"causal FLOP count"}
     worst = {}
     ref = dict(o=ro, dq=rg[0], dk=rg[1], dv=rg[2])
     for n, r in ref.items():
-        gg = np.stack([workloads.as_float64(gpu_out[n])[b, h] for b, h in sel])[None]
+        gg = pick(gpu_out[n])
         d = gg - r
         worst[n] = {"max_abs": float(np.max(np.abs(d))),
                     "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(r))}
