@@ -54,6 +54,10 @@ def main():
                     help="heads of the workload the CPU oracle runs on")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle's passes until this much time has gone by")
+    ap.add_argument("--layout", choices=["bhtd", "packed"], default="bhtd",
+                    help="packed: compare the model-native entry points (q, k, v from a packed "
+                         "[B, T, 3, H, D] tensor, o and dO as [B, T, H, D]) with the "
+                         "[B, H, T, D] entry points plus the permute copies a model would need")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes three times (the "
                          "reference point that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -85,6 +89,8 @@ def main():
     attn.load()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.layout == "packed":
+        return bench_packed(args, dev)
 
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
@@ -214,6 +220,88 @@ def main():
         "parity": parity,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_packed(args, dev):
+    """One JSON line: whole fwd+bwd steps through the packed entry points, against
+    the same steps through the [B, H, T, D] entry points with the permute copies
+    a model holding a packed QKV projection output needs around them."""
+    import torch
+
+    import causal_attention_attn_amd as attn
+    import workloads
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    B, H, T, D = w.shape
+    dt = {"bf16": attn.ATTN_BF16, "f16": attn.ATTN_F16}[w.dtype]
+    x = workloads.make(w, seed=0)
+    qkv = torch.stack([x["q"], x["k"], x["v"]], 0).permute(1, 3, 0, 2, 4).contiguous().to(dev)
+    do_t = x["do"].permute(0, 2, 1, 3).contiguous().to(dev)     # [B, T, H, D]
+    cs, sn = attn.rope_tables(T, D, w.base, dev)
+    nsv = attn.attn_saved_bytes(B, H, T, D, dt)
+    nws = attn.attn_bwd_workspace_bytes(B, H, T, D, dt)
+    saved = torch.empty(nsv, dtype=torch.uint8, device=dev)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    o_t = torch.empty((B, T, H, D), dtype=qkv.dtype, device=dev)
+    dqkv = torch.empty_like(qkv)
+    sh = torch.cuda.current_stream(dev).cuda_stream
+
+    def packed():
+        attn.attn_fwd_packed(qkv, cs, sn, o_t, lse, saved, nsv, B, H, T, D, dt, sh)
+        attn.attn_bwd_packed(qkv, o_t, do_t, lse, cs, sn, saved, nsv, dqkv, ws, nws, B, H, T, D,
+                             dt, sh)
+
+    q, k, v = (torch.empty((B, H, T, D), dtype=qkv.dtype, device=dev) for _ in range(3))
+    o, do = torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    o_t2, dqkv2 = torch.empty_like(o_t), torch.empty_like(qkv)
+
+    def permuted():
+        for i, t in enumerate((q, k, v)):
+            t.copy_(qkv[:, :, i].permute(0, 2, 1, 3))
+        attn.attn_fwd(q, k, v, cs, sn, o, lse, saved, nsv, B, H, T, D, dt, sh)
+        o_t2.copy_(o.permute(0, 2, 1, 3))
+        do.copy_(do_t.permute(0, 2, 1, 3))
+        attn.attn_bwd(q, k, v, o, do, lse, cs, sn, saved, nsv, dq, dk, dv, ws, nws, B, H, T, D,
+                      dt, sh)
+        for i, t in enumerate((dq, dk, dv)):
+            dqkv2[:, :, i].copy_(t.permute(0, 2, 1, 3))
+
+    def plain():
+        attn.attn_fwd(q, k, v, cs, sn, o, lse, saved, nsv, B, H, T, D, dt, sh)
+        attn.attn_bwd(q, k, v, o, do, lse, cs, sn, saved, nsv, dq, dk, dv, ws, nws, B, H, T, D,
+                      dt, sh)
+
+    def timed(f):
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    res = {}
+    for _ in range(3):  # interleaved rounds; the minimum of each
+        for n, f in (("packed", packed), ("bhtd_with_permutes", permuted), ("bhtd", plain)):
+            res[n] = min(res.get(n, 1e30), timed(f))
+    packed()
+    permuted()
+    torch.cuda.synchronize()
+    fl = causal_flops(B, H, T, D)
+    total = fl["fwd"] + fl["bwd"]
+    print(json.dumps({
+        "metric": "causal attn fwd+bwd step, model-native layouts", "unit": "ms",
+        "workload": name, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": {n: round(t, 5) for n, t in res.items()},
+        "tflops": {n: round(total / (t * 1e-3) / 1e12, 2) for n, t in res.items()},
+        "packed_equals_bhtd_bitwise": bool(torch.equal(dqkv, dqkv2) and torch.equal(o_t, o_t2)),
+    }), flush=True)
 
 
 # kernel -> the sources that define it; a traffic figure is valid only for these exact sources

@@ -13,9 +13,11 @@ from ._lib import (  # noqa: F401
     AttnError,
     attn_bwd,
     attn_bwd_grads,
+    attn_bwd_packed,
     attn_bwd_prep,
     attn_bwd_workspace_bytes,
     attn_fwd,
+    attn_fwd_packed,
     attn_fwd_rotated,
     attn_last_hip_error,
     attn_rope_tables,
@@ -24,4 +26,4 @@ from ._lib import (  # noqa: F401
     attn_status_string,
     load,
 )
-from .api import backward, forward, rope_tables  # noqa: F401
+from .api import backward, backward_packed, forward, forward_packed, rope_tables  # noqa: F401

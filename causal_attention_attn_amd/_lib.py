@@ -38,6 +38,9 @@ _SIGS = {
     "attn_bwd_prep": (_I, [_P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
     "attn_bwd_grads": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _P, _Z,
                             _I, _I, _I, _I, _I, _P]),
+    "attn_fwd_packed": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_packed": (_I, [_P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _Z, _I, _I, _I, _I, _I,
+                             _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
 }
@@ -143,6 +146,19 @@ def attn_bwd_grads(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, d
     _call("attn_bwd_grads", _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(cos_tab),
           _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dq), _ptr(dk), _ptr(dv),
           _ptr(workspace), int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
+
+
+def attn_fwd_packed(qkv, cos_tab, sin_tab, o, lse, saved, saved_bytes, B, H, T, D, dtype,
+                    stream=None):
+    _call("attn_fwd_packed", _ptr(qkv), _ptr(cos_tab), _ptr(sin_tab), _ptr(o), _ptr(lse),
+          _ptr(saved), int(saved_bytes), B, H, T, D, dtype, _stream(stream))
+
+
+def attn_bwd_packed(qkv, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dqkv, workspace,
+                    workspace_bytes, B, H, T, D, dtype, stream=None):
+    _call("attn_bwd_packed", _ptr(qkv), _ptr(o), _ptr(dO), _ptr(lse), _ptr(cos_tab),
+          _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dqkv), _ptr(workspace),
+          int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
 
 
 def attn_status_string(status):

@@ -74,3 +74,45 @@ def backward(q, k, v, o, do, lse, saved, base=10000.0):
     _lib.attn_bwd(q, k, v, o, do, lse, cs, sn, saved if nsaved else None, nsaved, dq, dk, dv,
                   ws, nbytes, B, H, T, D, dt)
     return dq, dk, dv
+
+
+def _packed_shape(qkv):
+    if qkv.dim() != 5 or qkv.shape[2] != 3:
+        raise ValueError("expected a packed [B, T, 3, H, D] tensor")
+    if not qkv.is_cuda or not qkv.is_contiguous():
+        raise ValueError("the packed tensor must be a contiguous GPU tensor")
+    B, T, _, H, D = qkv.shape
+    return B, H, T, D
+
+
+def forward_packed(qkv, base=10000.0):
+    """Forward from the QKV projection's packed [B, T, 3, H, D] output; returns
+    (o, lse, saved) with o as [B, T, H, D] (= [B, T, H*D], the out-projection's
+    input). 16-bit dtypes only."""
+    B, H, T, D = _packed_shape(qkv)
+    dt = _dtype_code(qkv)
+    cs, sn = rope_tables(T, D, base, qkv.device)
+    o = torch.empty((B, T, H, D), dtype=qkv.dtype, device=qkv.device)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=qkv.device)
+    nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
+    saved = torch.empty(max(nsaved, 1), dtype=torch.uint8, device=qkv.device)
+    _lib.attn_fwd_packed(qkv, cs, sn, o, lse, saved, nsaved, B, H, T, D, dt)
+    return o, lse, saved
+
+
+def backward_packed(qkv, o, do, lse, saved, base=10000.0):
+    """Gradients of sum(o * do) w.r.t. the pre-RoPE q, k and v of a packed
+    [B, T, 3, H, D] tensor, returned in that layout (o and do are [B, T, H, D])."""
+    B, H, T, D = _packed_shape(qkv)
+    for t in (o, do):
+        if tuple(t.shape) != (B, T, H, D) or t.dtype != qkv.dtype or not t.is_contiguous():
+            raise ValueError("o and do must be contiguous [B, T, H, D] of the packed dtype")
+    dt = _dtype_code(qkv)
+    cs, sn = rope_tables(T, D, base, qkv.device)
+    dqkv = torch.empty_like(qkv)
+    nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
+    nbytes = _lib.attn_bwd_workspace_bytes(B, H, T, D, dt)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=qkv.device)
+    _lib.attn_bwd_packed(qkv, o, do, lse, cs, sn, saved, nsaved, dqkv, ws, nbytes, B, H, T, D,
+                         dt)
+    return dqkv

@@ -94,9 +94,28 @@ attn::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* 
     a.lse = lse; a.cs = cs; a.sn = sn; a.rot = saved;
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.ws = static_cast<float*>(const_cast<void*>(ws));
+    a.lqkv = a.lo = attn::layout_bhtd(H, T, D);
     a.B = B; a.H = H; a.T = T; a.D = D;
     a.stream = static_cast<hipStream_t>(stream);
     return a;
+}
+
+// the packed entry points: the 16-bit path only; the packed [B, T, 3, H, D]
+// tensor must hold fewer than 2^31 elements (all in-head byte offsets fit 32
+// bits) and a token row fewer than 2^23 (the strided tile loads form a row's
+// extra offset with a 24-bit multiply)
+int check_packed(int B, int H, int T, int D, int dtype) {
+    const int st = check_shape(B, H, T, D, dtype);
+    if (st) return st;
+    if (dtype == ATTN_F32) return ATTN_ERR_DTYPE;
+    if ((long long)3 * B * H * T * D >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    if ((long long)3 * H * D >= (1ll << 23)) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+// the q, k and v slices of a packed [B, T, 3, H, D] tensor (16-bit elements)
+const void* packed_slot(const void* qkv, int slot, int H, int D) {
+    return static_cast<const char*>(qkv) + (size_t)slot * H * D * 2;
 }
 
 }  // namespace
@@ -145,8 +164,9 @@ int attn_rotate_qk(const void* q, const void* k, const float* cos_tab, const flo
     st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
     if (st) return st;
     if (any_alias({saved}, {q, k, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
-    return hip_status(attn::launch_rotate_qk(q, k, cos_tab, sin_tab, saved, B, H, T, D,
-                                             dtype == ATTN_F16, static_cast<hipStream_t>(stream)));
+    return hip_status(attn::launch_rotate_qk(q, k, attn::layout_bhtd(H, T, D), cos_tab, sin_tab,
+                                             saved, B, H, T, D, dtype == ATTN_F16,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void* o, float* lse,
@@ -161,6 +181,7 @@ int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void*
     if (any_alias({o, lse}, {v, saved})) return ATTN_ERR_ALIAS;
     attn::FwdArgs a = {};
     a.v = v; a.rot = saved; a.o = o; a.lse = lse;
+    a.lqkv = a.lo = attn::layout_bhtd(H, T, D);
     a.B = B; a.H = H; a.T = T; a.D = D;
     a.stream = static_cast<hipStream_t>(stream);
     return hip_status(attn::launch_fwd16(a, dtype == ATTN_F16));
@@ -185,6 +206,7 @@ int attn_fwd(const void* q, const void* k, const void* v, const float* cos_tab,
     }
     attn::FwdArgs a = {};
     a.q = q; a.k = k; a.v = v; a.cs = cos_tab; a.sn = sin_tab; a.o = o; a.lse = lse;
+    a.lqkv = a.lo = attn::layout_bhtd(H, T, D);
     a.B = B; a.H = H; a.T = T; a.D = D;
     a.stream = static_cast<hipStream_t>(stream);
     return hip_status(attn::launch_fwd_f32(a));
@@ -247,6 +269,57 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     if (st) return st;
     return attn_bwd_grads(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, dk, dv,
                           workspace, workspace_bytes, B, H, T, D, dtype, stream);
+}
+
+int attn_fwd_packed(const void* qkv, const float* cos_tab, const float* sin_tab, void* o,
+                    float* lse, void* saved, size_t saved_bytes, int B, int H, int T, int D,
+                    int dtype, void* stream) {
+    int st = check_packed(B, H, T, D, dtype);
+    if (st) return st;
+    st = check_ptrs({qkv, cos_tab, sin_tab, o, lse});
+    if (st) return st;
+    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+    if (st) return st;
+    if (any_alias({o, lse, saved}, {qkv, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const attn::Layout lqkv = attn::layout_bthd(H, T, D, 3);
+    st = hip_status(attn::launch_rotate_qk(packed_slot(qkv, 0, H, D), packed_slot(qkv, 1, H, D),
+                                           lqkv, cos_tab, sin_tab, saved, B, H, T, D,
+                                           dtype == ATTN_F16, s));
+    if (st) return st;
+    attn::FwdArgs a = {};
+    a.v = packed_slot(qkv, 2, H, D); a.rot = saved; a.o = o; a.lse = lse;
+    a.lqkv = lqkv;
+    a.lo = attn::layout_bthd(H, T, D, 1);
+    a.B = B; a.H = H; a.T = T; a.D = D;
+    a.stream = s;
+    return hip_status(attn::launch_fwd16(a, dtype == ATTN_F16));
+}
+
+int attn_bwd_packed(const void* qkv, const void* o, const void* dO, const float* lse,
+                    const float* cos_tab, const float* sin_tab, const void* saved,
+                    size_t saved_bytes, void* dqkv, void* workspace, size_t workspace_bytes,
+                    int B, int H, int T, int D, int dtype, void* stream) {
+    int st = check_packed(B, H, T, D, dtype);
+    if (st) return st;
+    st = check_ptrs({qkv, o, dO, lse, cos_tab, sin_tab, dqkv});
+    if (st) return st;
+    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+    if (st) return st;
+    if (workspace == nullptr || workspace_bytes < workspace_need(B, H, T, dtype))
+        return ATTN_ERR_WORKSPACE;
+    if (misaligned(workspace)) return ATTN_ERR_ALIGN;
+    if (any_alias({dqkv, workspace}, {qkv, o, dO, lse, cos_tab, sin_tab, saved}))
+        return ATTN_ERR_ALIAS;
+    char* g = static_cast<char*>(dqkv);
+    attn::BwdArgs a = bwd_args(nullptr, nullptr, packed_slot(qkv, 2, H, D), o, dO, lse, cos_tab,
+                               sin_tab, saved, g, g + (size_t)H * D * 2, g + (size_t)2 * H * D * 2,
+                               workspace, B, H, T, D, stream);
+    a.lqkv = attn::layout_bthd(H, T, D, 3);
+    a.lo = attn::layout_bthd(H, T, D, 1);
+    st = hip_status(attn::launch_bwd_prep16(a, dtype == ATTN_F16));
+    if (st) return st;
+    return hip_status(attn::launch_bwd_grads16(a, dtype == ATTN_F16));
 }
 
 const char* attn_status_string(int status) {

@@ -127,11 +127,12 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const vec8
 }
 
 // Step n of the dq kernel's key-tile loop on ring stage STG (= n % NS).
-template <int D, typename E, int STG, bool DIAG>
+template <int D, typename E, int STG, bool DIAG, bool STRIDED>
 __device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const vec8<E>* df,
                                         const Ring& rg,
                                         const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
-                                        const f16* kr, const E* v, int T, int n, int ntiles,
+                                        const f16* kr, const E* v, int vst, int T, int n,
+                                        int ntiles,
                                         int wq0, int lane, int wave, const f32x16& nl,
                                         const f32x16& nd) {
     using C = BwdTile<D>;
@@ -145,7 +146,8 @@ __device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const vec8
     const int nx = n + NS - 1;
     if (nx < ntiles) {
         ld.issue(kr, T, nx * C::KN, rg.k[NXT], wave);
-        ld.issue(v, T, nx * C::KN, rg.v[NXT], wave);
+        if constexpr (STRIDED) ld.issue_strided(v, T, nx * C::KN, rg.v[NXT], wave, vst);
+        else ld.issue(v, T, nx * C::KN, rg.v[NXT], wave);
     }
     dq_tile<D, E, DIAG>(acc, qf, df, rg.k[STG], rg.v[STG], of, n * C::KN, wq0, lane, nl, nd);
 }
@@ -161,12 +163,14 @@ struct BwdPtrs {
     const float* cs;
     const float* sn;
     E *dq, *dk, *dv;
-    int BH, T;
+    Layout lv;         // v, dq, dk and dv
+    Layout lo;         // dO
+    int H, BH, T;
 };
 
 // dq item: the 128 queries of q-block qb of head bh (loops over key tiles up
 // to the diagonal; rg.k / rg.v hold K / V tiles).
-template <int D, typename E>
+template <int D, typename E, bool STRIDED>
 __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, int bh, int qb) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
@@ -185,8 +189,14 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
     const size_t hoff = (size_t)bh * T * D;
     const uint32_t hbytes = (uint32_t)T * D * 2;
     const f16* kh = pp.kr + hoff;
-    const E* vh = pp.v + hoff;
-    const rsrc_t qbuf = make_rsrc(qr + hoff, hbytes), gbuf = make_rsrc(dO + hoff, hbytes);
+    // v, dO and dq: [B, H, T, D] unless STRIDED (then where their layouts put them)
+    const int vst = STRIDED ? pp.lv.st : D, gst = STRIDED ? pp.lo.st : D;
+    const long long vhead = STRIDED ? pp.lv.head(bh, pp.H) : (long long)hoff;
+    const E* vh = pp.v + vhead;
+    const rsrc_t qbuf = make_rsrc(qr + hoff, hbytes);
+    const rsrc_t gbuf =
+        STRIDED ? make_rsrc(dO + pp.lo.head(bh, pp.H), pp.lo.head_bytes(T, D))
+                : make_rsrc(dO + hoff, hbytes);
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
     const TileLoads<D, 64, 4> ld(wave, lane);
@@ -201,7 +211,8 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
     for (int s = 0; s < NS - 1; ++s) {
         if (s < ntiles) {
             ld.issue(kh, T, s * C::KN, rg.k[s], wave);
-            ld.issue(vh, T, s * C::KN, rg.v[s], wave);
+            if constexpr (STRIDED) ld.issue_strided(vh, T, s * C::KN, rg.v[s], wave, vst);
+            else ld.issue(vh, T, s * C::KN, rg.v[s], wave);
         }
     }
 
@@ -210,9 +221,9 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
     vec8<E> df[C::DK];
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) {
-        const uint32_t off = (uint32_t)(tq * D + 16 * c + 8 * hf) * 2;
-        qf[c] = __builtin_bit_cast(f16x8, buf_load16(qbuf, off));
-        df[c] = as_vec8<vec8<E>>(buf_load16(gbuf, off));
+        const uint32_t col = (uint32_t)(16 * c + 8 * hf) * 2;
+        qf[c] = __builtin_bit_cast(f16x8, buf_load16(qbuf, (uint32_t)tq * D * 2 + col));
+        df[c] = as_vec8<vec8<E>>(buf_load16(gbuf, (uint32_t)tq * gst * 2 + col));
     }
     const float nlt = tq < T ? ws[(size_t)bh * T + tq] : 0.f;
     const float ndl = tq < T ? ws[(size_t)BH * T + (size_t)bh * T + tq] : 0.f;
@@ -224,24 +235,24 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
 
     int n = 0;
     for (; n + NS <= nfull; n += NS) {
-        dq_step<D, E, 0, false>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
-        dq_step<D, E, 1, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 1, ntiles, wq0, lane, wave, nl, nd);
+        dq_step<D, E, 0, false, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
+        dq_step<D, E, 1, false, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n + 1, ntiles, wq0, lane, wave, nl, nd);
         if constexpr (NS > 2)
-            dq_step<D, E, 2, false>(acc, qf, df, rg, ld, of, kh, vh, T, n + 2, ntiles, wq0, lane, wave, nl, nd);
+            dq_step<D, E, 2, false, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n + 2, ntiles, wq0, lane, wave, nl, nd);
     }
     for (; n < ntiles; ++n) {
         const int stg = n % NS;
         if (stg == 0)
-            dq_step<D, E, 0, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
+            dq_step<D, E, 0, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
         else if (stg == 1)
-            dq_step<D, E, 1, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
+            dq_step<D, E, 1, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
         else if constexpr (NS > 2)
-            dq_step<D, E, 2, true>(acc, qf, df, rg, ld, of, kh, vh, T, n, ntiles, wq0, lane, wave, nl, nd);
+            dq_step<D, E, 2, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
     }
     wait_vmcnt<0>();
 
     if (tq < T) {
-        E* out = dq + hoff + (size_t)tq * D;
+        E* out = STRIDED ? row_ptr(dq + vhead, tq, vst) : dq + hoff + (size_t)tq * D;
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
@@ -334,11 +345,12 @@ __device__ __forceinline__ void dkdv_tile(f32x16* dva, f32x16* dka, const f16x8*
     }
 }
 
-template <int D, typename E>
+template <int D, typename E, bool STRIDED>
 struct DkdvCtx {
     const f16* qh;
     const E* gh;
     const float* oh;  // this wave's per-row offsets: -lse*log2(e) (waves 0, 1) or -delta (2, 3)
+    int gst;          // elements between consecutive rows of dO
     int T, wk0, lane, wave;
 
     // query tile qt -> LDS stage: rotated Q and dO tiles, then 32 of the 128
@@ -347,7 +359,8 @@ struct DkdvCtx {
                                           char* gs, char* ls) const {
         constexpr int QN = BwdTile<D>::QN;
         ld.issue(qh, T, qt * QN, qs, wave);
-        ld.issue(gh, T, qt * QN, gs, wave);
+        if constexpr (STRIDED) ld.issue_strided(gh, T, qt * QN, gs, wave, gst);
+        else ld.issue(gh, T, qt * QN, gs, wave);
         if (lane < 32)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 make_rsrc(oh, (uint32_t)T * 4), LDS_PTR(ls + 128 * wave), 4,
@@ -356,11 +369,11 @@ struct DkdvCtx {
 };
 
 // Step of the dk/dv kernel's query-tile loop on ring stage STG.
-template <int D, typename E, int STG, bool DIAG>
+template <int D, typename E, int STG, bool DIAG, bool STRIDED>
 __device__ __forceinline__ void dkdv_step(f32x16* dva, f32x16* dka, const f16x8* kf,
                                           const vec8<E>* vf, const Ring& rg,
                                           const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
-                                          const DkdvCtx<D, E>& x, int qt, int nqt) {
+                                          const DkdvCtx<D, E, STRIDED>& x, int qt, int nqt) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int NXT = (STG + NS - 1) % NS;
@@ -375,7 +388,7 @@ __device__ __forceinline__ void dkdv_step(f32x16* dva, f32x16* dka, const f16x8*
 
 // dk/dv item: the 128 keys of key block kb of head bh (loops over query tiles
 // from the diagonal down; rg.k / rg.v / rg.x hold Q / dO tiles and offsets).
-template <int D, typename E>
+template <int D, typename E, bool STRIDED>
 __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, int bh, int kb) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
@@ -398,8 +411,12 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
     const uint32_t hbytes = (uint32_t)T * D * 2;
     const int wk0 = k0 + wave * 32;
     const int tk = wk0 + c32;
-    const DkdvCtx<D, E> x = {qr + hoff, dO + hoff, ws + (size_t)(wave >> 1) * BH * T + (size_t)bh * T,
-                          T, wk0, lane, wave};
+    // v, dO, dk and dv: [B, H, T, D] unless STRIDED (then where their layouts put them)
+    const int vst = STRIDED ? pp.lv.st : D;
+    const long long vhead = STRIDED ? pp.lv.head(bh, pp.H) : (long long)hoff;
+    const DkdvCtx<D, E, STRIDED> x = {qr + hoff, dO + (STRIDED ? pp.lo.head(bh, pp.H) : (long long)hoff),
+                             ws + (size_t)(wave >> 1) * BH * T + (size_t)bh * T,
+                             STRIDED ? pp.lo.st : D, T, wk0, lane, wave};
     const TileLoads<D, 64, 4> ld(wave, lane);
     const OperandOffs<D> of(lane);
 
@@ -412,14 +429,15 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
     for (int s = 0; s < NS - 1; ++s)
         if (qt0 + s < nqt) x.issue(ld, qt0 + s, rg.k[s], rg.v[s], rg.x[s]);
 
-    const rsrc_t kbuf = make_rsrc(kr + hoff, hbytes), vbuf = make_rsrc(v + hoff, hbytes);
+    const rsrc_t kbuf = make_rsrc(kr + hoff, hbytes);
+    const rsrc_t vbuf = make_rsrc(v + vhead, STRIDED ? pp.lv.head_bytes(T, D) : hbytes);
     f16x8 kf[C::DK];
     vec8<E> vf[C::DK];
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) {
-        const uint32_t off = (uint32_t)(tk * D + 16 * c + 8 * hf) * 2;
-        kf[c] = __builtin_bit_cast(f16x8, buf_load16(kbuf, off));
-        vf[c] = as_vec8<vec8<E>>(buf_load16(vbuf, off));
+        const uint32_t col = (uint32_t)(16 * c + 8 * hf) * 2;
+        kf[c] = __builtin_bit_cast(f16x8, buf_load16(kbuf, (uint32_t)tk * D * 2 + col));
+        vf[c] = as_vec8<vec8<E>>(buf_load16(vbuf, (uint32_t)tk * vst * 2 + col));
     }
     f32x16 dva[C::DB], dka[C::DB];
 #pragma unroll
@@ -429,32 +447,32 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
     int qt = qt0;
     for (; qt < min(qfull, nqt); ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 0) dkdv_step<D, E, 0, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if (stg == 1) dkdv_step<D, E, 1, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if constexpr (NS > 2) dkdv_step<D, E, 2, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        if (stg == 0) dkdv_step<D, E, 0, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if (stg == 1) dkdv_step<D, E, 1, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if constexpr (NS > 2) dkdv_step<D, E, 2, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
     // the full tiles, rotated so that the unrolled body starts on stage 0
     for (; qt < nqt && (qt - qt0) % NS != 0; ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 1) dkdv_step<D, E, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if constexpr (NS > 2) dkdv_step<D, E, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        if (stg == 1) dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if constexpr (NS > 2) dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
     for (; qt + NS <= nqt; qt += NS) {
-        dkdv_step<D, E, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        dkdv_step<D, E, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 1, nqt);
-        if constexpr (NS > 2) dkdv_step<D, E, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt + 2, nqt);
+        dkdv_step<D, E, 0, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt + 1, nqt);
+        if constexpr (NS > 2) dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt + 2, nqt);
     }
     for (; qt < nqt; ++qt) {
         const int stg = (qt - qt0) % NS;
-        if (stg == 0) dkdv_step<D, E, 0, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if (stg == 1) dkdv_step<D, E, 1, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if constexpr (NS > 2) dkdv_step<D, E, 2, false>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        if (stg == 0) dkdv_step<D, E, 0, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if (stg == 1) dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        else if constexpr (NS > 2) dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
     wait_vmcnt<0>();
 
     if (tk < T) {
-        E* ko = dk + hoff + (size_t)tk * D;
-        E* vo = dv + hoff + (size_t)tk * D;
+        E* ko = STRIDED ? row_ptr(dk + vhead, tk, vst) : dk + hoff + (size_t)tk * D;
+        E* vo = STRIDED ? row_ptr(dv + vhead, tk, vst) : dv + hoff + (size_t)tk * D;
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
@@ -481,7 +499,7 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
 // Item classes alternate dk/dv key block r and dq q-block nqb-1-r
 // (r = 0, 1, ...), which is heaviest first up to the 4:3 ratio of their
 // products per tile; each class holds one item per head.
-template <int D, typename E>
+template <int D, typename E, bool STRIDED>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd16_kernel(BwdPtrs<E> pp, int nqb,
                                                                          int nkb, int kinds,
                                                                          int ncu) {
@@ -502,9 +520,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd16_kernel(BwdPtrs<E> 
     const int r = c / per;
     const bool is_dkdv = kinds == 2 || (kinds == 3 && (c % 2) == 0);
     if (is_dkdv) {
-        if (r < nkb) dkdv_item<D, E>(pp, rg, bh, r);
+        if (r < nkb) dkdv_item<D, E, STRIDED>(pp, rg, bh, r);
     } else {
-        if (r < nqb) dq_item<D, E>(pp, rg, bh, nqb - 1 - r);
+        if (r < nqb) dq_item<D, E, STRIDED>(pp, rg, bh, nqb - 1 - r);
     }
 }
 
@@ -513,14 +531,20 @@ static hipError_t launch_grads(const BwdArgs& a, int kinds) {
     using C = BwdTile<D>;
     const size_t n = (size_t)a.B * a.H * a.T * a.D;
     const f16* rot = static_cast<const f16*>(a.rot);
-    const BwdPtrs<E> pp = {rot, rot + n, (const E*)a.v, (const E*)a.dO, a.ws, a.cs, a.sn,
-                           (E*)a.dq, (E*)a.dk, (E*)a.dv, a.B * a.H, a.T};
+    const BwdPtrs<E> pp = {rot,        rot + n,    (const E*)a.v, (const E*)a.dO, a.ws,
+                           a.cs,       a.sn,       (E*)a.dq,      (E*)a.dk,       (E*)a.dv,
+                           a.lqkv,     a.lo,       a.H,           a.B * a.H,      a.T};
     const int nqb = (a.T + C::QM - 1) / C::QM;
     const int nkb = (a.T + C::KM - 1) / C::KM;
     const int per = kinds == 3 ? 2 : 1;
     const int items = per * (nqb > nkb ? nqb : nkb) * a.B * a.H;
-    hipLaunchKernelGGL((bwd16_kernel<D, E>), dim3(items), dim3(C::NT), 0, a.stream, pp, nqb, nkb,
-                       kinds, device_cu_count());
+    // row pitch D for both means plain [B, H, T, D] (see Layout)
+    if (a.lqkv.st != a.D || a.lo.st != a.D)
+        hipLaunchKernelGGL((bwd16_kernel<D, E, true>), dim3(items), dim3(C::NT), 0, a.stream, pp,
+                           nqb, nkb, kinds, device_cu_count());
+    else
+        hipLaunchKernelGGL((bwd16_kernel<D, E, false>), dim3(items), dim3(C::NT), 0, a.stream, pp,
+                           nqb, nkb, kinds, device_cu_count());
     return hipGetLastError();
 }
 

@@ -15,21 +15,38 @@
 namespace attn {
 
 // LPR lanes share one row; each loads 16 consecutive bytes of o and of dO, so a
-// wave reads whole rows contiguously.
-template <typename E, int D, bool HALF_LAYOUT>
+// wave reads whole rows contiguously. Plain [B, H, T, D] tensors are walked as
+// one flat array of rows; STRIDED ones (rows where the Layout puts them) give
+// each head `bph` consecutive workgroups.
+template <typename E, int D, bool HALF_LAYOUT, bool STRIDED>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const E* __restrict__ o,
-                                                       const E* __restrict__ dO,
+                                                       const E* __restrict__ dO, Layout lo,
                                                        const float* __restrict__ lse,
-                                                       float* __restrict__ ws, long rows) {
+                                                       float* __restrict__ ws, int H, int T,
+                                                       int bph, long long rows) {
     constexpr int EPL = 16 / (int)sizeof(E);  // elements per 16-byte load
     constexpr int LPR = D / EPL;              // lanes per row (8 .. 32)
     static_assert(LPR >= 2 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "lanes per row");
-    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-    const long row = gid / LPR;
-    const int part = (int)(gid % LPR);
+    long long row, e0;
+    int part;
+    bool valid;
+    if constexpr (STRIDED) {
+        const int bh = blockIdx.x / bph;
+        const int i = (blockIdx.x - bh * bph) * 256 + threadIdx.x;
+        const int t = i / LPR;
+        part = i % LPR;
+        valid = t < T;
+        row = (long long)bh * T + t;
+        e0 = lo.head(bh, H) + (long long)t * lo.st + part * EPL;
+    } else {
+        const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+        row = gid / LPR;
+        part = (int)(gid % LPR);
+        valid = row < rows;
+        e0 = row * D + part * EPL;
+    }
     float acc = 0.f;
-    if (row < rows) {
-        const size_t e0 = (size_t)row * D + (size_t)part * EPL;
+    if (valid) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(o + e0);
         const u32x4 b = *reinterpret_cast<const u32x4*>(dO + e0);
         if constexpr (sizeof(E) == 2) {
@@ -46,7 +63,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const E* __restrict__ o,
     // the LPR lanes of a row are consecutive and LPR divides the wave
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (row < rows && part == 0) {
+    if (valid && part == 0) {
         if constexpr (HALF_LAYOUT) {
             ws[row] = -lse[row] * kLog2e;
             ws[rows + row] = -acc;
@@ -59,10 +76,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const E* __restrict__ o,
 template <typename E, int D, bool HALF_LAYOUT>
 static hipError_t launch_prep_t(const BwdArgs& a) {
     constexpr int LPR = D / (16 / (int)sizeof(E));
-    const long rows = (long)a.B * a.H * a.T;
-    const long blocks = (rows * LPR + 255) / 256;
-    hipLaunchKernelGGL((bwd_prep_kernel<E, D, HALF_LAYOUT>), dim3((unsigned)blocks), dim3(256), 0,
-                       a.stream, (const E*)a.o, (const E*)a.dO, a.lse, a.ws, rows);
+    const long long rows = (long long)a.B * a.H * a.T;
+    if (a.lo.st != D) {  // rows not D apart: a strided layout (see Layout)
+        const int bph = (a.T * LPR + 255) / 256;
+        const unsigned blocks = (unsigned)((long long)a.B * a.H * bph);
+        hipLaunchKernelGGL((bwd_prep_kernel<E, D, HALF_LAYOUT, true>), dim3(blocks), dim3(256),
+                           0, a.stream, (const E*)a.o, (const E*)a.dO, a.lo, a.lse, a.ws, a.H,
+                           a.T, bph, rows);
+    } else {
+        const unsigned blocks = (unsigned)((rows * LPR + 255) / 256);
+        hipLaunchKernelGGL((bwd_prep_kernel<E, D, HALF_LAYOUT, false>), dim3(blocks), dim3(256),
+                           0, a.stream, (const E*)a.o, (const E*)a.dO, a.lo, a.lse, a.ws, a.H,
+                           a.T, 0, rows);
+    }
     return hipGetLastError();
 }
 

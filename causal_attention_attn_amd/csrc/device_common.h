@@ -62,6 +62,14 @@ __device__ __forceinline__ int snake_item(int bid, int ncu, int n_items) {
     return r * ncu + (((ncu >> 3) - 1 - (c >> 3)) << 3) + (c & 7);
 }
 
+// Row t of a head whose 16-bit rows are st elements apart. The in-head byte
+// offset fits 32 bits (the entry points check it), so a lane needs one 32-bit
+// offset register rather than a 64-bit address.
+template <typename E>
+__device__ __forceinline__ E* row_ptr(E* head, int t, int st) {
+    return reinterpret_cast<E*>(reinterpret_cast<char*>(head) + (uint32_t)t * (uint32_t)st * 2u);
+}
+
 // True on every lane when the predicate holds on any active lane of the wave.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
@@ -217,15 +225,18 @@ __device__ __forceinline__ int tile_off(int r, int col) {
 // the tile, each issuing IPW 1 KB instructions; instruction i of this wave
 // fills LDS bytes [1024 (wave IPW + i), +1024) of the tile and takes its
 // global chunk at voff[i] from the tile's first row. Each tile gets its own
-// buffer resource starting at that row and ending at row T, so rows past the
-// end of the sequence read as zeros (the range check covers the per-lane
-// offset, not a scalar one).
+// buffer resource starting at that row and ending just after the last element
+// of row T-1, so rows past the end of the sequence read as zeros (the range
+// check covers the per-lane offset, not a scalar one) and nothing beyond the
+// head's last element is touched.
 template <int D, int ROWS, int NW>
 struct TileLoads {
     static constexpr int NC = D / 8;                 // 16-byte chunks per row
     static constexpr int INSTR = ROWS * NC / 64;     // 1 KB instructions per tile
     static_assert(INSTR % NW == 0, "tile instructions must divide among waves");
     static constexpr int IPW = INSTR / NW;
+    static constexpr int ROW_SHIFT = D == 64 ? 7 : 8;  // log2 of a row's 2*D bytes
+    static_assert((2 * D) == (1 << ROW_SHIFT), "row bytes");
     uint32_t voff[IPW];
     __device__ __forceinline__ TileLoads(int wave, int lane) {
 #pragma unroll
@@ -235,7 +246,7 @@ struct TileLoads {
             voff[i] = (uint32_t)(r * D + 8 * swz<D>(r, pos)) * 2;
         }
     }
-    // rows r0 .. r0+ROWS-1 of a [T, D] 16-bit head -> LDS `tile`
+    // rows r0 .. r0+ROWS-1 of a [T, D] head -> LDS `tile`
     __device__ __forceinline__ void issue(const void* head, int T, int r0, char* tile,
                                           int wave) const {
         const int rows = T > r0 ? T - r0 : 0;
@@ -245,6 +256,29 @@ struct TileLoads {
         for (int i = 0; i < IPW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(src, LDS_PTR(tile + (wave * IPW + i) * 1024),
                                                      16, voff[i], 0, 0, 0);
+    }
+    // The same for a head whose rows are `pitch` elements apart (its rows sit
+    // inside token rows that hold other heads or tensors). The row of a chunk is
+    // voff >> ROW_SHIFT (the swizzled column stays below one row), so its offset
+    // gains row * (pitch - D) * 2 bytes; that is formed right before each load
+    // (asm, so the compiler does not keep a second offset array live across the
+    // tile loop).
+    __device__ __forceinline__ void issue_strided(const void* head, int T, int r0, char* tile,
+                                                  int wave, int pitch) const {
+        const int rows = T > r0 ? T - r0 : 0;
+        const uint32_t bytes = rows > 0 ? (uint32_t)((rows - 1) * pitch + D) * 2 : 0u;
+        const rsrc_t src =
+            make_rsrc(static_cast<const char*>(head) + (size_t)r0 * pitch * 2, bytes);
+        const uint32_t extra = (uint32_t)(pitch - D) * 2;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            uint32_t off;
+            asm volatile("v_lshrrev_b32 %0, %2, %1\n\tv_mad_u32_u24 %0, %0, %3, %1"
+                         : "=&v"(off)
+                         : "v"(voff[i]), "i"(ROW_SHIFT), "s"(extra));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src, LDS_PTR(tile + (wave * IPW + i) * 1024),
+                                                     16, off, 0, 0, 0);
+        }
     }
 };
 

@@ -213,6 +213,7 @@ template <int D, typename E>
 struct FwdCtx {
     const f16* kr;
     const E* v;
+    int vst;  // elements between consecutive rows of v
     int T, wq0, lane, wave;
 };
 
@@ -222,7 +223,7 @@ struct FwdCtx {
 // last reads were made before it) and refill that stage with tile n+NS-1;
 // finish tile n (its V operands are read before the softmax, which hides their
 // latency) and read tile n+1's K operands while the PV products run.
-template <int D, typename E, int STG, bool DIAG>
+template <int D, typename E, int STG, bool DIAG, bool STRIDED>
 __device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, KOps<D>& kr,
                                          const Ring& rg, const TileLoads<D, 64, 4>& ld,
                                          const OperandOffs<D>& of, const FwdCtx<D, E>& x, int n) {
@@ -238,15 +239,17 @@ __device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, KOps<
     ring_barrier();
     const int nx = n + NS - 1;
     ld.issue(x.kr, x.T, nx * C::BN, rg.k[FREE], x.wave);
-    ld.issue(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave);
+    if constexpr (STRIDED) ld.issue_strided(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave, x.vst);
+    else ld.issue(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave);
     if (live) fwd_softmax_pv<D, E, DIAG>(st, s, rg.v[STG], of, k0, x.wq0, n == 0);
     read_k(kr, rg.k[NXT], of);
 }
 
-template <int D, typename E>
+template <int D, typename E, bool STRIDED>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
     const f16* __restrict__ qr, const f16* __restrict__ kr, const E* __restrict__ v,
-    E* __restrict__ o, float* __restrict__ lse, int BH, int T, int nqb, int ncu) {
+    E* __restrict__ o, float* __restrict__ lse, Layout lv, Layout lo, int H, int BH, int T,
+    int nqb, int ncu) {
     using C = FwdTile<D>;
     constexpr int NS = C::NS;
     // one __shared__ object per ring stage (see Ring); stages >= NS are stubs
@@ -268,7 +271,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
     const size_t hoff = (size_t)bh * T * D;
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
-    const FwdCtx<D, E> x = {kr + hoff, v + hoff, T, wq0, lane, wave};
+    // v and o: [B, H, T, D] unless STRIDED (then where their layouts put them)
+    const FwdCtx<D, E> x = {kr + hoff, v + (STRIDED ? lv.head(bh, H) : (long long)hoff),
+                            STRIDED ? lv.st : D, T, wq0, lane, wave};
     const TileLoads<D, 64, 4> ld(wave, lane);
     const OperandOffs<D> of(lane);
 
@@ -280,7 +285,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) {
         ld.issue(x.kr, T, s * C::BN, rg.k[s], wave);
-        ld.issue(x.v, T, s * C::BN, rg.v[s], wave);
+        if constexpr (STRIDED) ld.issue_strided(x.v, T, s * C::BN, rg.v[s], wave, x.vst);
+        else ld.issue(x.v, T, s * C::BN, rg.v[s], wave);
     }
 
     const rsrc_t qh = make_rsrc(qr + hoff, (uint32_t)T * D * 2);
@@ -305,12 +311,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
     int n = 0;
     // full tiles: branch-free bodies, ring stages as compile-time constants
     for (; n + NS <= nfull; n += NS)
-        static_for<NS>([&](auto S) { fwd_step<D, E, S, false>(st, qf, kops, rg, ld, of, x, n + S); });
+        static_for<NS>([&](auto S) {
+            fwd_step<D, E, S, false, STRIDED>(st, qf, kops, rg, ld, of, x, n + S);
+        });
     // the rest (at most NS-1 full tiles, then the diagonal tiles)
     for (; n < ntiles; ++n) {
         const int stg = n % NS;
         static_for<NS>([&](auto S) {
-            if (stg == S) fwd_step<D, E, S, true>(st, qf, kops, rg, ld, of, x, n);
+            if (stg == S) fwd_step<D, E, S, true, STRIDED>(st, qf, kops, rg, ld, of, x, n);
         });
     }
     wait_vmcnt<0>();  // no LDS writes may land after this workgroup's LDS is released
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
     const float l_tot = sum_across_halves(st.l);
     if (tq < T) {
         const float inv = 1.f / l_tot;
-        E* orow = o + hoff + (size_t)tq * D;
+        E* orow = STRIDED ? row_ptr(o + lo.head(bh, H), tq, lo.st) : o + hoff + (size_t)tq * D;
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
@@ -335,14 +343,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
 
 // Explicit instantiations: the host pass does not always emit the launch stub of
 // a kernel template with a 16-bit element-type argument on its own.
-template __global__ void fwd16_kernel<64, bf16>(const f16*, const f16*, const bf16*, bf16*, float*,
-                                                int, int, int, int);
-template __global__ void fwd16_kernel<128, bf16>(const f16*, const f16*, const bf16*, bf16*,
-                                                 float*, int, int, int, int);
-template __global__ void fwd16_kernel<64, f16>(const f16*, const f16*, const f16*, f16*, float*,
-                                               int, int, int, int);
-template __global__ void fwd16_kernel<128, f16>(const f16*, const f16*, const f16*, f16*, float*,
-                                                int, int, int, int);
+#define ATTN_FWD_INST(D_, E_, S_)                                                            \
+    template __global__ void fwd16_kernel<D_, E_, S_>(const f16*, const f16*, const E_*, E_*, \
+                                                      float*, Layout, Layout, int, int, int,  \
+                                                      int, int);
+ATTN_FWD_INST(64, bf16, false) ATTN_FWD_INST(128, bf16, false)
+ATTN_FWD_INST(64, f16, false) ATTN_FWD_INST(128, f16, false)
+ATTN_FWD_INST(64, bf16, true) ATTN_FWD_INST(128, bf16, true)
+ATTN_FWD_INST(64, f16, true) ATTN_FWD_INST(128, f16, true)
+#undef ATTN_FWD_INST
 
 template <int D, typename E>
 static hipError_t launch_fwd(const FwdArgs& a) {
@@ -351,8 +360,16 @@ static hipError_t launch_fwd(const FwdArgs& a) {
     const int nqb = (a.T + C::BM - 1) / C::BM;
     const size_t n = (size_t)a.B * a.H * a.T * a.D;
     const f16* rot = static_cast<const f16*>(a.rot);
-    hipLaunchKernelGGL((fwd16_kernel<D, E>), dim3(nqb * BH), dim3(C::NT), 0, a.stream, rot,
-                       rot + n, (const E*)a.v, (E*)a.o, a.lse, BH, a.T, nqb, device_cu_count());
+    // row pitch D for both means plain [B, H, T, D] (see Layout)
+    const bool strided = a.lqkv.st != a.D || a.lo.st != a.D;
+    if (strided)
+        hipLaunchKernelGGL((fwd16_kernel<D, E, true>), dim3(nqb * BH), dim3(C::NT), 0, a.stream,
+                           rot, rot + n, (const E*)a.v, (E*)a.o, a.lse, a.lqkv, a.lo, a.H, BH,
+                           a.T, nqb, device_cu_count());
+    else
+        hipLaunchKernelGGL((fwd16_kernel<D, E, false>), dim3(nqb * BH), dim3(C::NT), 0, a.stream,
+                           rot, rot + n, (const E*)a.v, (E*)a.o, a.lse, a.lqkv, a.lo, a.H, BH,
+                           a.T, nqb, device_cu_count());
     return hipGetLastError();
 }
 

@@ -7,12 +7,38 @@
 
 namespace attn {
 
+// Where element (b, h, t, d) of a [B, H, T, D]-indexed tensor sits, in elements
+// from the tensor's base: b*sb + h*sh + t*st + d (the D features of a row are
+// contiguous). Contiguous [B, H, T, D] has (H*T*D, T*D, D); a head's slice of
+// token-major [B, T, H, D] has (T*H*D, D, H*D); a q, k or v slice of the packed
+// [B, T, 3, H, D] projection output has (3*T*H*D, D, 3*H*D).
+struct Layout {
+    long long sb, sh;
+    int st;
+    __host__ __device__ long long head(int bh, int H) const {
+        return (long long)(bh / H) * sb + (long long)(bh % H) * sh;
+    }
+    // bytes from a head's first element to the end of its row T-1
+    __host__ __device__ unsigned int head_bytes(int T, int D) const {
+        return (unsigned int)(((long long)(T - 1) * st + D) * 2);
+    }
+};
+
+inline Layout layout_bhtd(int H, int T, int D) {
+    return {(long long)H * T * D, (long long)T * D, D};
+}
+inline Layout layout_bthd(int H, int T, int D, int slots) {
+    return {(long long)slots * T * H * D, D, slots * H * D};
+}
+
 struct FwdArgs {
     const void *q, *k, *v;
     const float *cs, *sn;
     const void* rot;  // 16-bit path: rotated q * log2(e)/sqrt(D), then rotated k, [B, H, T, D] fp16 each
     void* o;
     float* lse;
+    Layout lqkv;  // q, k, v (the 16-bit path; fp32 takes [B, H, T, D] only)
+    Layout lo;    // o
     int B, H, T, D;
     hipStream_t stream;
 };
@@ -24,6 +50,8 @@ struct BwdArgs {
     void *dq, *dk, *dv;
     float* ws;  // workspace (written by the pre-pass): 16-bit path [B, H, T] -lse*log2(e),
                 // then [B, H, T] -delta; fp32 path [B, H, T] delta
+    Layout lqkv;  // v, dq, dk, dv (q and k too, for fp32, which takes [B, H, T, D] only)
+    Layout lo;    // o, dO
     int B, H, T, D;
     hipStream_t stream;
 };
@@ -33,9 +61,9 @@ int device_cu_count();
 
 hipError_t launch_rope_tables(float* cs, float* sn, int T, int D, double base, hipStream_t s);
 // The 16-bit path (bf16 or, with f16_storage, fp16 tensors).
-hipError_t launch_rotate_qk(const void* q, const void* k, const float* cs, const float* sn,
-                            void* out, int B, int H, int T, int D, bool f16_storage,
-                            hipStream_t s);
+hipError_t launch_rotate_qk(const void* q, const void* k, Layout lqk, const float* cs,
+                            const float* sn, void* out, int B, int H, int T, int D,
+                            bool f16_storage, hipStream_t s);
 hipError_t launch_fwd16(const FwdArgs& a, bool f16_storage);
 hipError_t launch_bwd_prep16(const BwdArgs& a, bool f16_storage);   // workspace entries
 hipError_t launch_bwd_grads16(const BwdArgs& a, bool f16_storage);  // dq, dk, dv in one launch

@@ -38,21 +38,35 @@ hipError_t launch_rope_tables(float* cs, float* sn, int T, int D, double base, h
 // product comes out of the MFMA directly as S * log2(e). The 16-bit kernels read
 // these instead of applying RoPE per tile. One thread per 8 consecutive
 // features of one row, for q and k together (one cos/sin read serves both).
-template <int D, typename E>
+// Plain [B, H, T, D] inputs are walked as one flat array; STRIDED inputs (rows
+// where the Layout puts them) give each head `bph` consecutive workgroups.
+template <int D, typename E, bool STRIDED>
 __global__ __launch_bounds__(256) void rotate_qk_kernel(const E* __restrict__ q,
-                                                        const E* __restrict__ k,
+                                                        const E* __restrict__ k, Layout lqk,
                                                         const float* __restrict__ cs,
                                                         const float* __restrict__ sn,
-                                                        f16* __restrict__ out, int T,
-                                                        int chunks, float qs) {
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= chunks) return;
+                                                        f16* __restrict__ out, int H, int T,
+                                                        int bph, long long n, float qs) {
     constexpr int NC = D / 8;
-    const int c = idx % NC;
-    const int t = (idx / NC) % T;
-    const size_t e0 = (size_t)idx * 8;
-    const u32x4 wq = *reinterpret_cast<const u32x4*>(q + e0);
-    const u32x4 wk = *reinterpret_cast<const u32x4*>(k + e0);
+    long long src, dst;
+    int t, c;
+    if constexpr (STRIDED) {
+        const int bh = blockIdx.x / bph;
+        const int i = (blockIdx.x - bh * bph) * 256 + threadIdx.x;
+        if (i >= T * NC) return;
+        t = i / NC;
+        c = i % NC;
+        src = lqk.head(bh, H) + (long long)t * lqk.st + 8 * c;
+        dst = ((long long)bh * T + t) * D + 8 * c;
+    } else {
+        const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+        if ((long long)idx * 8 >= n) return;
+        c = idx % NC;
+        t = (idx / NC) % T;
+        src = dst = (long long)idx * 8;
+    }
+    const u32x4 wq = *reinterpret_cast<const u32x4*>(q + src);
+    const u32x4 wk = *reinterpret_cast<const u32x4*>(k + src);
     const f32x4 cv = *reinterpret_cast<const f32x4*>(cs + t * (D / 2) + 4 * c);
     const f32x4 sv = *reinterpret_cast<const f32x4*>(sn + t * (D / 2) + 4 * c);
     u32x4 rq, rk;
@@ -63,30 +77,37 @@ __global__ __launch_bounds__(256) void rotate_qk_kernel(const E* __restrict__ q,
         rq[p] = pack2<f16>((q0 * cv[p] - q1 * sv[p]) * qs, (q0 * sv[p] + q1 * cv[p]) * qs);
         rk[p] = pack2<f16>(k0 * cv[p] - k1 * sv[p], k0 * sv[p] + k1 * cv[p]);
     }
-    *reinterpret_cast<u32x4*>(out + e0) = rq;
-    *reinterpret_cast<u32x4*>(out + (size_t)chunks * 8 + e0) = rk;
+    *reinterpret_cast<u32x4*>(out + dst) = rq;
+    *reinterpret_cast<u32x4*>(out + n + dst) = rk;
 }
 
-template <typename E>
-static hipError_t launch_rotate_t(const void* q, const void* k, const float* cs, const float* sn,
-                                  void* out, int B, int H, int T, int D, hipStream_t st) {
-    const int chunks = (int)((long)B * H * T * D / 8);
-    const int blocks = (chunks + 255) / 256;
+template <int D, typename E>
+static hipError_t launch_rotate_d(const void* q, const void* k, Layout lqk, const float* cs,
+                                  const float* sn, void* out, int B, int H, int T,
+                                  hipStream_t st) {
+    const long long n = (long long)B * H * T * D;
     const float qs = kLog2e / sqrtf((float)D);
-    if (D == 64)
-        hipLaunchKernelGGL((rotate_qk_kernel<64, E>), dim3(blocks), dim3(256), 0, st, (const E*)q,
-                           (const E*)k, cs, sn, (f16*)out, T, chunks, qs);
-    else
-        hipLaunchKernelGGL((rotate_qk_kernel<128, E>), dim3(blocks), dim3(256), 0, st, (const E*)q,
-                           (const E*)k, cs, sn, (f16*)out, T, chunks, qs);
+    if (lqk.st != D) {  // rows not D apart: a strided layout (see Layout)
+        const int bph = (T * (D / 8) + 255) / 256;
+        const unsigned blocks = (unsigned)((long long)B * H * bph);
+        hipLaunchKernelGGL((rotate_qk_kernel<D, E, true>), dim3(blocks), dim3(256), 0, st,
+                           (const E*)q, (const E*)k, lqk, cs, sn, (f16*)out, H, T, bph, n, qs);
+    } else {
+        const unsigned blocks = (unsigned)((n / 8 + 255) / 256);
+        hipLaunchKernelGGL((rotate_qk_kernel<D, E, false>), dim3(blocks), dim3(256), 0, st,
+                           (const E*)q, (const E*)k, lqk, cs, sn, (f16*)out, H, T, 0, n, qs);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_rotate_qk(const void* q, const void* k, const float* cs, const float* sn,
-                            void* out, int B, int H, int T, int D, bool f16_storage,
-                            hipStream_t st) {
-    return f16_storage ? launch_rotate_t<f16>(q, k, cs, sn, out, B, H, T, D, st)
-                       : launch_rotate_t<bf16>(q, k, cs, sn, out, B, H, T, D, st);
+hipError_t launch_rotate_qk(const void* q, const void* k, Layout lqk, const float* cs,
+                            const float* sn, void* out, int B, int H, int T, int D,
+                            bool f16_storage, hipStream_t st) {
+    if (f16_storage)
+        return D == 64 ? launch_rotate_d<64, f16>(q, k, lqk, cs, sn, out, B, H, T, st)
+                       : launch_rotate_d<128, f16>(q, k, lqk, cs, sn, out, B, H, T, st);
+    return D == 64 ? launch_rotate_d<64, bf16>(q, k, lqk, cs, sn, out, B, H, T, st)
+                   : launch_rotate_d<128, bf16>(q, k, lqk, cs, sn, out, B, H, T, st);
 }
 
 }  // namespace attn

@@ -24,8 +24,9 @@
  *
  * Conventions common to all calls:
  *   - Every tensor pointer is a DEVICE pointer, 16-byte aligned; tensors are
- *     contiguous row-major [B, H, T, D] with D innermost; lse and the backward
- *     workspace hold [B, H, T] fp32; cos/sin tables are [T, D/2] fp32.
+ *     contiguous row-major [B, H, T, D] with D innermost (the *_packed entry
+ *     points take the model-native layouts they describe instead); lse and the
+ *     backward workspace hold [B, H, T] fp32; cos/sin tables are [T, D/2] fp32.
  *   - dtype is ATTN_BF16 (bf16 storage, fp32 accumulation; rotated q/k and dS
  *     are carried in fp16 inside the kernels), ATTN_F16 (the same kernels with
  *     fp16 storage, so P, V and dO are fp16 operands too) or ATTN_F32 (fp32
@@ -187,6 +188,59 @@ int attn_bwd_grads(const void* q, const void* k, const void* v,
                    void* dq, void* dk, void* dv,
                    const void* workspace, size_t workspace_bytes,
                    int B, int H, int T, int D, int dtype, void* stream);
+
+/*
+ * Model-native layouts. In the model the pages describe, attention sits between
+ * two projections: the query, key and value projections (RoPE is applied to the
+ * first two) feed it, and its output feeds the output projection ("Tiny Hackable
+ * CUDA", section 3, causal attention paragraph; the engine runs those
+ * projections as cuBLAS matrix products, "Show HN: NanoEuler", paragraph 2). A
+ * fused QKV projection of a [B*T, C] activation, C = H*D, produces one
+ * [B, T, 3, H, D] tensor (q, k, v slots of each token's row), and the output
+ * projection consumes o as [B, T, H*D]. These two entry points read and write
+ * those layouts directly, so no permute copies are needed on either side; the
+ * arithmetic, kernels and results are those of attn_fwd / attn_bwd (bitwise
+ * equal for the same values).
+ *
+ * 16-bit path only (ATTN_BF16, ATTN_F16; ATTN_F32 gets ATTN_ERR_DTYPE); the
+ * packed tensor must hold fewer than 2^31 elements (3*B*H*T*D < 2^31) and a
+ * token row of it fewer than 2^23 (3*H*D < 2^23); otherwise ATTN_ERR_SHAPE.
+ * lse, the saved buffer and the workspace keep their [B, H, T] / [2][B, H, T, D]
+ * layouts and sizes (attn_saved_bytes, attn_bwd_workspace_bytes).
+ */
+
+/*
+ * attn_fwd_packed - forward pass from the packed projection output.
+ *   qkv       [B, T, 3, H, D] dtype, input: qkv[b,t,0,h,:] is q of head h at
+ *             position t, [.., 1, ..] is k, [.., 2, ..] is v (pre-RoPE)
+ *   cos_tab, sin_tab  [T, D/2] fp32 from attn_rope_tables
+ *   o         [B, T, H, D] dtype (= [B, T, H*D]), output
+ *   lse       [B, H, T] fp32, output
+ *   saved     device buffer of attn_saved_bytes(); receives the rotated q and k
+ * Enqueues the rotation pass and the forward kernel.
+ */
+int attn_fwd_packed(const void* qkv, const float* cos_tab, const float* sin_tab,
+                    void* o, float* lse, void* saved, size_t saved_bytes,
+                    int B, int H, int T, int D, int dtype, void* stream);
+
+/*
+ * attn_bwd_packed - backward pass in the same layouts: gradients of
+ * L = sum(o * dO) with respect to the pre-RoPE q, k and v, written into one
+ * [B, T, 3, H, D] tensor, ready for the QKV projection's backward.
+ *   qkv       [B, T, 3, H, D] dtype, the forward's input (v is read from it)
+ *   o, dO     [B, T, H, D] dtype, inputs (o and lse from attn_fwd_packed)
+ *   lse       [B, H, T] fp32, input
+ *   saved     the buffer attn_fwd_packed filled
+ *   dqkv      [B, T, 3, H, D] dtype, output (overwritten): dq, dk, dv slots
+ *   workspace device buffer of at least attn_bwd_workspace_bytes()
+ * Enqueues the pre-pass and the gradient kernel; the |dS| bound of attn_bwd
+ * applies.
+ */
+int attn_bwd_packed(const void* qkv, const void* o, const void* dO, const float* lse,
+                    const float* cos_tab, const float* sin_tab,
+                    const void* saved, size_t saved_bytes, void* dqkv,
+                    void* workspace, size_t workspace_bytes,
+                    int B, int H, int T, int D, int dtype, void* stream);
 
 /* attn_status_string - static, human-readable name of a status code. */
 const char* attn_status_string(int status);

@@ -68,3 +68,23 @@ def assert_close(got, ref, dtype, label=""):
     lse_tol = 1e-2 + 1e-3 * big if dtype != "f32" else 1e-5
     assert mx <= lse_tol, f"{label} lse max-abs {mx:.3e} > {lse_tol:.3e}"
     print(label, "; ".join(report), flush=True)
+
+
+def to_packed(x, dev):
+    """q, k, v [B, H, T, D] -> the packed [B, T, 3, H, D] projection output, and
+    do [B, H, T, D] -> [B, T, H, D], on `dev`."""
+    qkv = torch.stack([x["q"], x["k"], x["v"]], dim=0).permute(1, 3, 0, 2, 4).contiguous()
+    return qkv.to(dev), x["do"].permute(0, 2, 1, 3).contiguous().to(dev)
+
+
+def gpu_run_packed(x, base=10000.0):
+    """The packed entry points on the same values as gpu_run; outputs come back
+    in [B, H, T, D] (lse [B, H, T]) as CPU tensors."""
+    dev = torch.device("cuda", 0)
+    qkv, do = to_packed(x, dev)
+    o, lse, saved = attn.forward_packed(qkv, base=base)
+    dqkv = attn.backward_packed(qkv, o, do, lse, saved, base=base)
+    torch.cuda.synchronize()
+    bhtd = lambda t: t.permute(0, 2, 1, 3).contiguous().cpu()
+    return dict(o=bhtd(o), lse=lse.cpu(), dq=bhtd(dqkv[:, :, 0]), dk=bhtd(dqkv[:, :, 1]),
+                dv=bhtd(dqkv[:, :, 2]))

@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_rotated", "attn_rotate_qk", "attn_saved_bytes", "attn_bwd",
               "attn_bwd_prep", "attn_bwd_grads", "attn_rope_tables", "attn_bwd_workspace_bytes",
-              "attn_status_string", "attn_last_hip_error"):
+              "attn_fwd_packed", "attn_bwd_packed", "attn_status_string", "attn_last_hip_error"):
         assert n in names
 
 
@@ -162,6 +162,39 @@ def test_bwd_stages_reject_bad_arguments(lib):
     assert g(dv=FAKE + 32) == 7                           # dv aliases v
     assert g(dk=FAKE + 128) == 7                          # dk aliases dq
     assert g(dq=FAKE + 176) == 7                          # dq aliases the workspace
+
+
+def test_packed_entry_points_reject_bad_arguments(lib):
+    fb = dict(qkv=FAKE, cos_tab=FAKE + 16, sin_tab=FAKE + 32, o=FAKE + 48, lse=FAKE + 64,
+              saved=FAKE + 80, saved_bytes=4 * 8 * 64, B=1, H=1, T=8, D=64, dtype=0, stream=0)
+    f = lambda **o: status_of(lambda: attn.attn_fwd_packed(**{**fb, **o}))
+    assert f(qkv=0) == 1
+    assert f(saved=0) == 1
+    assert f(D=96) == 2
+    assert f(dtype=1) == 3                                # fp32 has no packed path
+    assert f(dtype=7) == 3
+    assert f(o=MIS) == 4
+    assert f(saved_bytes=16) == 9
+    assert f(o=FAKE) == 7                                 # o aliases qkv
+    assert f(saved=FAKE + 32) == 7                        # saved aliases a table
+    # the packed tensor (3*B*H*T*D elements) must stay below 2^31 elements
+    assert f(B=1, H=16, T=1 << 19, D=128, saved_bytes=1 << 40) == 2   # 3 * 2^30 elements
+    assert f(B=1, H=1 << 16, T=1, D=64, saved_bytes=1 << 40) == 2     # a token row of 3 * 2^22
+    bb = dict(qkv=FAKE, o=FAKE + 16, dO=FAKE + 32, lse=FAKE + 48, cos_tab=FAKE + 64,
+              sin_tab=FAKE + 80, saved=FAKE + 96, saved_bytes=4 * 8 * 64, dqkv=FAKE + 112,
+              workspace=FAKE + 128, workspace_bytes=256, B=1, H=1, T=8, D=64, dtype=0, stream=0)
+    g = lambda **o: status_of(lambda: attn.attn_bwd_packed(**{**bb, **o}))
+    assert g(dqkv=0) == 1
+    assert g(dO=0) == 1
+    assert g(dtype=1) == 3
+    assert g(T=0) == 2
+    assert g(dqkv=MIS) == 4
+    assert g(workspace=0) == 5
+    assert g(workspace_bytes=255) == 5
+    assert g(saved_bytes=8) == 9
+    assert g(dqkv=FAKE) == 7                              # dqkv aliases qkv
+    assert g(workspace=FAKE + 112) == 7                   # workspace aliases dqkv
+    assert g(dqkv=FAKE + 96) == 7                         # dqkv aliases saved
 
 
 def test_rope_tables_reject_bad_arguments(lib):
