@@ -10,6 +10,7 @@ differences, brute force and a library routine); see the test suite.
 from .attention import (  # noqa: F401
     DEFAULT_BASE,
     attention_backward,
+    attention_decode,
     attention_forward,
     attention_probabilities,
     rope,

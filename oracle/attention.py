@@ -29,6 +29,10 @@ What is computed, per (batch, head) and entirely in float64:
   dK^r = s dS^T Q^r, and the gradients with respect to the un-rotated inputs
   are dq = R_t^T dQ^r, dk = R_u^T dK^r (multiplication by exp(-j*t*theta_i)).
 
+* Decode. One generation step at position pos: the new query, rotated by its
+  own position, against cached keys and values of positions 0 .. pos; by
+  definition row pos of the causal forward over those positions.
+
 FlashAttention is exact attention evaluated in tiles; the oracle is the plain
 full-matrix definition instead, with no tiling. For long sequences the rows are
 processed in groups (each row's softmax always spans all T keys), which changes
@@ -48,18 +52,22 @@ def rope_frequencies(D, base=DEFAULT_BASE):
     return np.power(float(base), -2.0 * i / D)
 
 
-def rope(x, base=DEFAULT_BASE, inverse=False):
+def rope(x, base=DEFAULT_BASE, inverse=False, positions=None):
     """Rotate each adjacent feature pair of x[..., T, D] by its position's angle.
 
     The pair (x[2i], x[2i+1]) at position t is read as the complex number
     x[2i] + j*x[2i+1] and multiplied by exp(+j*t*theta_i); inverse=True
     multiplies by exp(-j*t*theta_i), which is the transpose of the rotation
-    and therefore carries a gradient back through RoPE.
+    and therefore carries a gradient back through RoPE. Row r of x sits at
+    position r, or at positions[r] when positions (T integers) is given.
     """
     x = np.asarray(x, dtype=np.float64)
     T, D = x.shape[-2], x.shape[-1]
     theta = rope_frequencies(D, base)
-    angle = np.arange(T, dtype=np.float64)[:, None] * theta[None, :]
+    pos = np.arange(T) if positions is None else np.asarray(positions)
+    if pos.shape != (T,):
+        raise ValueError("one position per row")
+    angle = pos.astype(np.float64)[:, None] * theta[None, :]
     phase = np.exp((-1j if inverse else 1j) * angle)          # [T, D/2]
     z = (x[..., 0::2] + 1j * x[..., 1::2]) * phase
     out = np.empty_like(x)
@@ -171,3 +179,39 @@ def attention_backward(q, k, v, do, base=DEFAULT_BASE, row_chunk=1024,
         return dq, dk, dv, delta
     return dq, dk, dv
 
+
+
+def attention_decode(q, k_cache, v_cache, pos, base=DEFAULT_BASE):
+    """One generation step over a key/value cache.
+
+    The pages' model generates text one token at a time, and each new position
+    may attend only to itself and earlier positions ("Tiny Hackable CUDA",
+    section 3, causal attention paragraph). At position `pos` the new query q
+    ([B, H, D], pre-RoPE) is rotated by its own position and scored against the
+    cached keys of positions 0 .. pos (k_cache [B, H, L, D], pre-RoPE, L > pos,
+    each rotated by its own position); v_cache [B, H, L, D] holds the values.
+    Rows of the cache past `pos` are not read. Returns (o [B, H, D],
+    lse [B, H]) in float64: softmax(S) v and the natural log-sum-exp of the
+    scaled scores S_u = (1/sqrt(D)) <R_pos q, R_u k_u>, u = 0 .. pos.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_cache = np.asarray(k_cache, dtype=np.float64)
+    v_cache = np.asarray(v_cache, dtype=np.float64)
+    if q.ndim != 3 or k_cache.ndim != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B, H, D] and k_cache, v_cache [B, H, L, D]")
+    B, H, L, D = k_cache.shape
+    if q.shape != (B, H, D) or not 0 <= pos < L:
+        raise ValueError("q must be [B, H, D] and 0 <= pos < L")
+    scale = 1.0 / np.sqrt(D)
+    o = np.empty((B, H, D))
+    lse = np.empty((B, H))
+    for b in range(B):
+        for h in range(H):
+            qr = rope(q[b, h][None, :], base, positions=[pos])[0]
+            kr = rope(k_cache[b, h, :pos + 1], base)
+            S = scale * (kr @ qr)                     # [pos + 1]
+            m = S.max()
+            w = np.exp(S - m)
+            o[b, h] = (w @ v_cache[b, h, :pos + 1]) / w.sum()
+            lse[b, h] = m + np.log(w.sum())
+    return o, lse

@@ -247,6 +247,51 @@ def test_torch_sdpa_float64_cross_check():
     np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
+# ---------------------------------------------------------------- decode ---------
+
+@pytest.mark.parametrize("pos,L,D", [(0, 1, 8), (5, 9, 8), (33, 34, 16), (63, 100, 64)])
+def test_decode_is_a_row_of_the_forward(pos, L, D):
+    """A generation step at position pos sees exactly what row pos of the causal
+    forward over positions 0 .. pos sees (the other query rows are arbitrary)."""
+    B, H = 2, 3
+    q = rand((B, H, D), 300 + pos)
+    k, v = rand((B, H, L, D), 301 + pos), rand((B, H, L, D), 302 + pos)
+    o, lse = oracle.attention_decode(q, k, v, pos)
+    qf = rand((B, H, pos + 1, D), 303)
+    qf[:, :, pos] = q
+    of, lf = oracle.attention_forward(qf, k[:, :, :pos + 1], v[:, :, :pos + 1])
+    np.testing.assert_allclose(o, of[:, :, pos], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lf[:, :, pos], rtol=1e-13, atol=1e-13)
+
+
+def test_decode_closed_forms():
+    B, H, L, D = 2, 2, 40, 16
+    k, v = rand((B, H, L, D), 310), rand((B, H, L, D), 311)
+    q = rand((B, H, D), 312)
+    # position 0: the only key is the query's own position and R_0 = I
+    o, lse = oracle.attention_decode(q, k, v, 0)
+    np.testing.assert_array_equal(o, v[:, :, 0])
+    np.testing.assert_allclose(lse, (q * k[:, :, 0]).sum(-1) / 4.0, rtol=1e-14)
+    # an all-zero query weighs positions 0 .. pos equally
+    for pos in (1, 17, 39):
+        o, lse = oracle.attention_decode(np.zeros((B, H, D)), k, v, pos)
+        np.testing.assert_allclose(o, v[:, :, :pos + 1].mean(axis=2), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse, math.log(pos + 1), rtol=1e-14)
+
+
+def test_decode_reads_nothing_past_pos():
+    B, H, L, D = 1, 2, 30, 8
+    q, k, v = rand((B, H, D), 320), rand((B, H, L, D), 321), rand((B, H, L, D), 322)
+    pos = 11
+    o, lse = oracle.attention_decode(q, k, v, pos)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, pos + 1:] = rand((B, H, L - pos - 1, D), 323)
+    v2[:, :, pos + 1:] = np.nan
+    o2, lse2 = oracle.attention_decode(q, k2, v2, pos)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
 # ------------------------------------------------------ planted mistakes ---------
 
 def test_pins_catch_planted_mistakes(monkeypatch):
@@ -288,3 +333,12 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(A, "rope", lambda x, base=10000.0, inverse=False:
                         np.asarray(x, float).copy() if inverse else real_rope(x, base))
     assert fwd_ok() and not bwd_ok()
+    monkeypatch.setattr(A, "rope", real_rope)
+    # a decode query rotated at position 0 instead of its own position
+    qd, kd, vd = rand((1, 1, 4), 95), rand((1, 1, 6, 4), 96), rand((1, 1, 6, 4), 97)
+    bo = brute_force.head_forward(L(np.concatenate([kd[:, :, :5], qd[:, :, None]], 2)),
+                                  L(kd), L(vd))[0]
+    assert np.allclose(A.attention_decode(qd, kd, vd, 5)[0][0, 0], bo[5], rtol=1e-10)
+    monkeypatch.setattr(A, "rope", lambda x, base=10000.0, inverse=False, positions=None:
+                        real_rope(x, base, inverse, None if positions is None else [0]))
+    assert not np.allclose(A.attention_decode(qd, kd, vd, 5)[0][0, 0], bo[5], rtol=1e-6)
