@@ -16,9 +16,13 @@ from ._lib import (  # noqa: F401
     attn_bwd_packed,
     attn_bwd_prep,
     attn_bwd_workspace_bytes,
+    attn_decode,
+    attn_decode_workspace_bytes,
     attn_fwd,
     attn_fwd_packed,
     attn_fwd_rotated,
+    attn_kv_append,
+    attn_kv_cache_bytes,
     attn_last_hip_error,
     attn_rope_tables,
     attn_rotate_qk,
@@ -26,4 +30,11 @@ from ._lib import (  # noqa: F401
     attn_status_string,
     load,
 )
-from .api import backward, backward_packed, forward, forward_packed, rope_tables  # noqa: F401
+from .api import (  # noqa: F401
+    KVCache,
+    backward,
+    backward_packed,
+    forward,
+    forward_packed,
+    rope_tables,
+)

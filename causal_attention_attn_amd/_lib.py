@@ -41,6 +41,10 @@ _SIGS = {
     "attn_fwd_packed": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
     "attn_bwd_packed": (_I, [_P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _Z, _I, _I, _I, _I, _I,
                              _P]),
+    "attn_kv_cache_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "attn_kv_append": (_I, [_P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "attn_decode": (_I, [_P, _P, _Z, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
 }
@@ -159,6 +163,27 @@ def attn_bwd_packed(qkv, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dqkv,
     _call("attn_bwd_packed", _ptr(qkv), _ptr(o), _ptr(dO), _ptr(lse), _ptr(cos_tab),
           _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dqkv), _ptr(workspace),
           int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
+
+
+def attn_kv_cache_bytes(B, H, Tmax, D, dtype):
+    return int(load().attn_kv_cache_bytes(B, H, Tmax, D, dtype))
+
+
+def attn_kv_append(k, v, cos_tab, sin_tab, cache, cache_bytes, pos0, n, B, H, Tmax, D, dtype,
+                   stream=None):
+    _call("attn_kv_append", _ptr(k), _ptr(v), _ptr(cos_tab), _ptr(sin_tab), _ptr(cache),
+          int(cache_bytes), pos0, n, B, H, Tmax, D, dtype, _stream(stream))
+
+
+def attn_decode_workspace_bytes(B, H, Tmax, D, dtype):
+    return int(load().attn_decode_workspace_bytes(B, H, Tmax, D, dtype))
+
+
+def attn_decode(q, cache, cache_bytes, cos_tab, sin_tab, o, lse, workspace, workspace_bytes,
+                pos, B, H, Tmax, D, dtype, stream=None):
+    _call("attn_decode", _ptr(q), _ptr(cache), int(cache_bytes), _ptr(cos_tab), _ptr(sin_tab),
+          _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes), pos, B, H, Tmax, D, dtype,
+          _stream(stream))
 
 
 def attn_status_string(status):

@@ -116,3 +116,43 @@ def backward_packed(qkv, o, do, lse, saved, base=10000.0):
     _lib.attn_bwd_packed(qkv, o, do, lse, cs, sn, saved, nsaved, dqkv, ws, nbytes, B, H, T, D,
                          dt)
     return dqkv
+
+
+class KVCache:
+    """A key/value cache for generation: B sequences, H heads, up to Tmax
+    positions, head dimension D, 16-bit dtype. append() writes pre-RoPE keys and
+    values of new positions; decode() runs one generation step."""
+
+    def __init__(self, B, H, Tmax, D, dtype=torch.bfloat16, device=None, base=10000.0):
+        self.B, self.H, self.Tmax, self.D, self.base = B, H, Tmax, D, base
+        self.dtype = dtype
+        self.code = _DTYPES[dtype]
+        self.device = torch.device(device if device is not None else "cuda")
+        self.nbytes = _lib.attn_kv_cache_bytes(B, H, Tmax, D, self.code)
+        if self.nbytes == 0:
+            raise ValueError("unsupported cache shape or dtype")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=self.device)
+        self.ws_bytes = _lib.attn_decode_workspace_bytes(B, H, Tmax, D, self.code)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.cs, self.sn = rope_tables(Tmax, D, base, self.device)
+
+    def append(self, k, v, pos0):
+        """k, v: [B, H, n, D] pre-RoPE keys and values of positions pos0 .. pos0+n-1."""
+        B, H, n, D = k.shape
+        if v.shape != k.shape or (B, H, D) != (self.B, self.H, self.D):
+            raise ValueError("k and v must be [B, H, n, D] of the cache's B, H and D")
+        if k.dtype != self.dtype or v.dtype != self.dtype:
+            raise ValueError("k and v must have the cache's dtype")
+        _lib.attn_kv_append(k.contiguous(), v.contiguous(), self.cs, self.sn, self.buf,
+                            self.nbytes, pos0, n, B, H, self.Tmax, D, self.code)
+
+    def decode(self, q, pos):
+        """q: [B, H, D] pre-RoPE query at position pos; returns (o [B, H, D], lse [B, H])."""
+        if tuple(q.shape) != (self.B, self.H, self.D) or q.dtype != self.dtype:
+            raise ValueError("q must be [B, H, D] of the cache's dtype")
+        o = torch.empty_like(q)
+        lse = torch.empty((self.B, self.H), dtype=torch.float32, device=q.device)
+        _lib.attn_decode(q.contiguous(), self.buf, self.nbytes, self.cs, self.sn, o, lse,
+                         self.ws, self.ws_bytes, pos, self.B, self.H, self.Tmax, self.D,
+                         self.code)
+        return o, lse

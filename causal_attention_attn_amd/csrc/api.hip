@@ -341,3 +341,70 @@ const char* attn_status_string(int status) {
 int attn_last_hip_error(void) { return g_last_hip_error; }
 
 }  // extern "C"
+
+// ---- decode over a key/value cache (16-bit path) ----
+
+namespace {
+
+int check_cache_shape(int B, int H, int Tmax, int D, int dtype) {
+    const int st = check_shape(B, H, Tmax, D, dtype);
+    if (st) return st;
+    if (dtype == ATTN_F32) return ATTN_ERR_DTYPE;
+    return ATTN_OK;
+}
+
+size_t cache_need(int B, int H, int Tmax, int D) { return round256((size_t)4 * B * H * Tmax * D); }
+
+size_t decode_ws_need(int B, int H, int Tmax, int D) {
+    return round256(attn::decode_workspace_floats(B, H, Tmax, D) * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_kv_cache_bytes(int B, int H, int Tmax, int D, int dtype) {
+    if (check_cache_shape(B, H, Tmax, D, dtype) != ATTN_OK) return 0;
+    return cache_need(B, H, Tmax, D);
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int Tmax, int D, int dtype) {
+    if (check_cache_shape(B, H, Tmax, D, dtype) != ATTN_OK) return 0;
+    return decode_ws_need(B, H, Tmax, D);
+}
+
+int attn_kv_append(const void* k, const void* v, const float* cos_tab, const float* sin_tab,
+                   void* cache, size_t cache_bytes, int pos0, int n, int B, int H, int Tmax,
+                   int D, int dtype, void* stream) {
+    int st = check_cache_shape(B, H, Tmax, D, dtype);
+    if (st) return st;
+    if (n < 1 || pos0 < 0 || (long long)pos0 + n > Tmax) return ATTN_ERR_SHAPE;
+    st = check_ptrs({k, v, cos_tab, sin_tab, cache});
+    if (st) return st;
+    if (cache_bytes < cache_need(B, H, Tmax, D)) return ATTN_ERR_WORKSPACE;
+    if (any_alias({cache}, {k, v, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
+    return hip_status(attn::launch_kv_append(k, v, cos_tab, sin_tab, cache, pos0, n, B, H, Tmax,
+                                             D, dtype == ATTN_F16,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int attn_decode(const void* q, const void* cache, size_t cache_bytes, const float* cos_tab,
+                const float* sin_tab, void* o, float* lse, void* workspace,
+                size_t workspace_bytes, int pos, int B, int H, int Tmax, int D, int dtype,
+                void* stream) {
+    int st = check_cache_shape(B, H, Tmax, D, dtype);
+    if (st) return st;
+    if (pos < 0 || pos >= Tmax) return ATTN_ERR_SHAPE;
+    st = check_ptrs({q, cache, cos_tab, sin_tab, o, lse});
+    if (st) return st;
+    if (cache_bytes < cache_need(B, H, Tmax, D)) return ATTN_ERR_WORKSPACE;
+    if (workspace == nullptr || workspace_bytes < decode_ws_need(B, H, Tmax, D))
+        return ATTN_ERR_WORKSPACE;
+    if (misaligned(workspace)) return ATTN_ERR_ALIGN;
+    if (any_alias({o, lse, workspace}, {q, cache, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
+    return hip_status(attn::launch_decode(q, cache, cos_tab, sin_tab, o, lse,
+                                          static_cast<float*>(workspace), pos, B, H, Tmax, D,
+                                          dtype == ATTN_F16, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

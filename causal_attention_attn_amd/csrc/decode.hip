@@ -1,0 +1,259 @@
+// Decode: one generation step of causal RoPE attention over a key/value cache,
+// 16-bit storage (bf16 or fp16, type E), gfx950.
+//
+// The pages' model generates one token at a time and a position may attend only
+// to itself and earlier positions, with RoPE on the query and key projections
+// encoding relative position ("Tiny Hackable CUDA", section 3, causal attention
+// paragraph). At generation step `pos` the new query is rotated by its own
+// position and scored against the cached keys of positions 0 .. pos, each
+// rotated once, by its own position, when it entered the cache.
+//
+// Cache (one caller buffer): K' = R_u k_u for every head and position, fp16
+// [B, H, Tmax, D] (rotated in fp32 and rounded once, like the forward's rotated
+// keys), followed by V, E [B, H, Tmax, D].
+//
+// A step reads (pos + 1) K' and V rows per head and does O(D) arithmetic per
+// row: it is bound by memory, not by MFMA (one query row is no contraction
+// worth a matrix core). The keys of a head are split into 64-key slices, one
+// slice per wave, so that even a handful of heads fills the chip:
+//   partial kernel  a wave loads its slice's K' and V rows with coalesced
+//                   16-byte loads (a row's 16-byte chunks on consecutive lanes),
+//                   forms the scores with fp16 dot products against the
+//                   rotated, log2(e)/sqrt(D)-scaled query, and keeps
+//                   (max m, sum l, unnormalised o) of its slice;
+//   combine kernel  per head, merges the slices: M = max m_i,
+//                   o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, and
+//                   lse = (M + log2 L) ln 2.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace attn {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kSlice = 64;  // keys per wave (one partial result each)
+
+template <int D>
+constexpr int partial_stride() { return D + 4; }  // o[D], m, l, 2 pad: 16-byte rows
+
+// Append n tokens to the cache: K' rows R_u k_u (u = pos0 + i) rounded once to
+// fp16, V rows copied. k and v are [B, H, n, D]. One thread per 8 features.
+template <int D, typename E>
+__global__ __launch_bounds__(256) void kv_append_kernel(const E* __restrict__ k,
+                                                        const E* __restrict__ v,
+                                                        const float* __restrict__ cs,
+                                                        const float* __restrict__ sn,
+                                                        f16* __restrict__ kc, E* __restrict__ vc,
+                                                        int n, int pos0, int Tmax,
+                                                        long long chunks) {
+    constexpr int NC = D / 8;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= chunks) return;
+    const int c = (int)(idx % NC);
+    const long long row = idx / NC;  // over B*H*n source rows
+    const int i = (int)(row % n);
+    const long long bh = row / n;
+    const int u = pos0 + i;
+    const long long src = row * D + 8 * c;
+    const long long dst = (bh * Tmax + u) * D + 8 * c;
+    const u32x4 wk = *reinterpret_cast<const u32x4*>(k + src);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(v + src);
+    const f32x4 cv = *reinterpret_cast<const f32x4*>(cs + (long long)u * (D / 2) + 4 * c);
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(sn + (long long)u * (D / 2) + 4 * c);
+    u32x4 rk;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f32x2 kp = unpack2<E>(wk[p]);
+        const float k0 = kp[0], k1 = kp[1];
+        rk[p] = pack2<f16>(k0 * cv[p] - k1 * sv[p], k0 * sv[p] + k1 * cv[p]);
+    }
+    *reinterpret_cast<u32x4*>(kc + dst) = rk;
+    *reinterpret_cast<u32x4*>(vc + dst) = wv;
+}
+
+// One wave per (head, 64-key slice). Lane l holds 16-byte chunk l % NC of rows
+// l / NC, l / NC + RPI, ... of the slice, for K' and for V.
+template <int D, typename E>
+__global__ __launch_bounds__(256) void decode_partial_kernel(
+    const E* __restrict__ q, const f16* __restrict__ kc, const E* __restrict__ vc,
+    const float* __restrict__ cs, const float* __restrict__ sn, float* __restrict__ part,
+    int Tmax, int pos, int nsplit, int nwaves, float qs) {
+    constexpr int NC = D / 8;          // 16-byte chunks per row
+    constexpr int RPI = 64 / NC;       // rows per load instruction
+    constexpr int NI = kSlice / RPI;   // load instructions per operand
+    const int lane = threadIdx.x & 63;
+    // = bh * nsplit + slice, uniform over the wave (its loads use scalar descriptors)
+    const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (gw >= nwaves) return;                             // no barriers below
+    const int bh = gw / nsplit, u0 = (gw % nsplit) * kSlice;
+    const int cc = lane % NC, rl = lane / NC;
+
+    // cache rows 0 .. pos of this head; rows past pos read as zeros
+    const uint32_t bytes = (uint32_t)(pos + 1) * D * 2;
+    const rsrc_t kb = make_rsrc(kc + (size_t)bh * Tmax * D, bytes);
+    const rsrc_t vb = make_rsrc(vc + (size_t)bh * Tmax * D, bytes);
+    u32x4 kr[NI], vr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const uint32_t off = (uint32_t)((u0 + i * RPI + rl) * D + 8 * cc) * 2;
+        kr[i] = buf_load16(kb, off);
+        vr[i] = buf_load16(vb, off);
+    }
+
+    // this lane's chunk of the query: R_pos q scaled by log2(e)/sqrt(D), fp16
+    const u32x4 wq = *reinterpret_cast<const u32x4*>(q + (size_t)bh * D + 8 * cc);
+    const f32x4 c4 = *reinterpret_cast<const f32x4*>(cs + (size_t)pos * (D / 2) + 4 * cc);
+    const f32x4 s4 = *reinterpret_cast<const f32x4*>(sn + (size_t)pos * (D / 2) + 4 * cc);
+    f16x2 qh[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f32x2 x = unpack2<E>(wq[p]);
+        qh[p] = __builtin_bit_cast(f16x2, pack2<f16>((x[0] * c4[p] - x[1] * s4[p]) * qs,
+                                                     (x[0] * s4[p] + x[1] * c4[p]) * qs));
+    }
+
+    // scores in log2 units; the NC lanes of a row add their chunks' dot products
+    float s[NI];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t kw = kr[i][p];  // a plain value: bit_cast of a vector element reads element 0
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, kw), qh[p], acc, false);
+        }
+#pragma unroll
+        for (int x = 1; x < NC; x <<= 1) acc += __shfl_xor(acc, x);
+        s[i] = u0 + i * RPI + rl <= pos ? acc : -INFINITY;
+        m = fmaxf(m, s[i]);
+    }
+#pragma unroll
+    for (int x = NC; x < 64; x <<= 1) m = fmaxf(m, __shfl_xor(m, x));
+
+    // p = 2^(s - m) (0 for rows past pos); l and o over this lane's rows
+    float l = 0.f;
+    float o[8] = {};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const float p = exp2_fast(s[i] - m);
+        l += p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f32x2 x = unpack2<E>(vr[i][e]);
+            o[2 * e] += p * x[0];
+            o[2 * e + 1] += p * x[1];
+        }
+    }
+    // sum over the rows: the lanes that share chunk cc
+#pragma unroll
+    for (int x = NC; x < 64; x <<= 1) {
+        l += __shfl_xor(l, x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] += __shfl_xor(o[j], x);
+    }
+    float* dst = part + (size_t)gw * partial_stride<D>();
+    if (rl == 0) {
+        *reinterpret_cast<f32x4*>(dst + 8 * cc) = f32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<f32x4*>(dst + 8 * cc + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    }
+    if (lane == 0) {
+        dst[D] = m;
+        dst[D + 1] = l;
+    }
+}
+
+// Merge a head's slices; one thread per feature.
+template <int D, typename E>
+__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part,
+                                                           E* __restrict__ o,
+                                                           float* __restrict__ lse, int nsplit) {
+    constexpr int PS = partial_stride<D>();
+    const int bh = blockIdx.x, d = threadIdx.x;
+    const float* P = part + (size_t)bh * nsplit * PS;
+    float M = -INFINITY;
+    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, P[i * PS + D]);
+    float L = 0.f, O = 0.f;
+    for (int i = 0; i < nsplit; ++i) {
+        const float w = exp2_fast(P[i * PS + D] - M);
+        L += w * P[i * PS + D + 1];
+        O += w * P[i * PS + d];
+    }
+    o[(size_t)bh * D + d] = static_cast<E>(O / L);
+    if (d == 0) lse[bh] = (M + log2f(L)) * kLn2;
+}
+
+// Explicit instantiations: the host pass does not always emit the launch stub of
+// a kernel template with a 16-bit element-type argument on its own.
+#define ATTN_DEC_INST(D_, E_)                                                                \
+    template __global__ void kv_append_kernel<D_, E_>(const E_*, const E_*, const float*,      \
+                                                      const float*, f16*, E_*, int, int, int,  \
+                                                      long long);                              \
+    template __global__ void decode_partial_kernel<D_, E_>(const E_*, const f16*, const E_*,   \
+                                                           const float*, const float*, float*, \
+                                                           int, int, int, int, float);         \
+    template __global__ void decode_combine_kernel<D_, E_>(const float*, E_*, float*, int);
+ATTN_DEC_INST(64, bf16) ATTN_DEC_INST(128, bf16) ATTN_DEC_INST(64, f16) ATTN_DEC_INST(128, f16)
+#undef ATTN_DEC_INST
+
+int decode_slices(int pos) { return (pos + kSlice) / kSlice; }
+
+size_t decode_workspace_floats(int B, int H, int Tmax, int D) {
+    return (size_t)B * H * decode_slices(Tmax - 1) * (D + 4);
+}
+
+template <int D, typename E>
+static hipError_t launch_append_t(const void* k, const void* v, const float* cs,
+                                  const float* sn, void* cache, int pos0, int n, int B, int H,
+                                  int Tmax, hipStream_t st) {
+    const long long chunks = (long long)B * H * n * (D / 8);
+    const size_t kbytes = (size_t)B * H * Tmax * D * 2;
+    f16* kc = static_cast<f16*>(cache);
+    E* vc = reinterpret_cast<E*>(static_cast<char*>(cache) + kbytes);
+    hipLaunchKernelGGL((kv_append_kernel<D, E>), dim3((unsigned)((chunks + 255) / 256)),
+                       dim3(256), 0, st, (const E*)k, (const E*)v, cs, sn, kc, vc, n, pos0, Tmax,
+                       chunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const void* k, const void* v, const float* cs, const float* sn,
+                            void* cache, int pos0, int n, int B, int H, int Tmax, int D,
+                            bool f16_storage, hipStream_t st) {
+    if (f16_storage)
+        return D == 64 ? launch_append_t<64, f16>(k, v, cs, sn, cache, pos0, n, B, H, Tmax, st)
+                       : launch_append_t<128, f16>(k, v, cs, sn, cache, pos0, n, B, H, Tmax, st);
+    return D == 64 ? launch_append_t<64, bf16>(k, v, cs, sn, cache, pos0, n, B, H, Tmax, st)
+                   : launch_append_t<128, bf16>(k, v, cs, sn, cache, pos0, n, B, H, Tmax, st);
+}
+
+template <int D, typename E>
+static hipError_t launch_decode_t(const void* q, const void* cache, const float* cs,
+                                  const float* sn, void* o, float* lse, float* ws, int pos,
+                                  int B, int H, int Tmax, hipStream_t st) {
+    const int nsplit = decode_slices(pos);
+    const int nwaves = B * H * nsplit;
+    const size_t kbytes = (size_t)B * H * Tmax * D * 2;
+    const f16* kc = static_cast<const f16*>(cache);
+    const E* vc = reinterpret_cast<const E*>(static_cast<const char*>(cache) + kbytes);
+    const float qs = kLog2e / sqrtf((float)D);
+    hipLaunchKernelGGL((decode_partial_kernel<D, E>), dim3((unsigned)((nwaves + 3) / 4)),
+                       dim3(256), 0, st, (const E*)q, kc, vc, cs, sn, ws, Tmax, pos, nsplit,
+                       nwaves, qs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<D, E>), dim3((unsigned)(B * H)), dim3(D), 0, st,
+                       ws, (E*)o, lse, nsplit);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const void* q, const void* cache, const float* cs, const float* sn,
+                         void* o, float* lse, float* ws, int pos, int B, int H, int Tmax, int D,
+                         bool f16_storage, hipStream_t st) {
+    if (f16_storage)
+        return D == 64 ? launch_decode_t<64, f16>(q, cache, cs, sn, o, lse, ws, pos, B, H, Tmax, st)
+                       : launch_decode_t<128, f16>(q, cache, cs, sn, o, lse, ws, pos, B, H, Tmax, st);
+    return D == 64 ? launch_decode_t<64, bf16>(q, cache, cs, sn, o, lse, ws, pos, B, H, Tmax, st)
+                   : launch_decode_t<128, bf16>(q, cache, cs, sn, o, lse, ws, pos, B, H, Tmax, st);
+}
+
+}  // namespace attn

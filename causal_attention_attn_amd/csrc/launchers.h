@@ -68,6 +68,17 @@ hipError_t launch_fwd16(const FwdArgs& a, bool f16_storage);
 hipError_t launch_bwd_prep16(const BwdArgs& a, bool f16_storage);   // workspace entries
 hipError_t launch_bwd_grads16(const BwdArgs& a, bool f16_storage);  // dq, dk, dv in one launch
 
+// Decode over a key/value cache (16-bit path): the cache is [B, H, Tmax, D] fp16
+// rotated keys followed by [B, H, Tmax, D] values of the storage type.
+int decode_slices(int pos);                                        // 64-key slices of 0..pos
+size_t decode_workspace_floats(int B, int H, int Tmax, int D);     // partials for pos = Tmax-1
+hipError_t launch_kv_append(const void* k, const void* v, const float* cs, const float* sn,
+                            void* cache, int pos0, int n, int B, int H, int Tmax, int D,
+                            bool f16_storage, hipStream_t s);
+hipError_t launch_decode(const void* q, const void* cache, const float* cs, const float* sn,
+                         void* o, float* lse, float* ws, int pos, int B, int H, int Tmax, int D,
+                         bool f16_storage, hipStream_t s);
+
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_prep_f32(const BwdArgs& a);    // workspace entries (delta)
 hipError_t launch_bwd_dq_f32(const BwdArgs& a);

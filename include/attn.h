@@ -242,6 +242,63 @@ int attn_bwd_packed(const void* qkv, const void* o, const void* dO, const float*
                     void* workspace, size_t workspace_bytes,
                     int B, int H, int T, int D, int dtype, void* stream);
 
+/*
+ * Decode over a key/value cache. The pages' model generates text one token at
+ * a time, and the token at position pos may attend only to positions
+ * 0 .. pos ("Tiny Hackable CUDA", section 3, causal attention paragraph). A
+ * generation step therefore scores one new query against the keys of all
+ * earlier tokens; keeping those keys (already rotated by their own positions)
+ * and values in a cache makes a step cost O(pos) instead of a full forward.
+ * The result of attn_decode at position pos is, by definition, row pos of
+ * attn_fwd over positions 0 .. pos.
+ *
+ * 16-bit path only (ATTN_BF16, ATTN_F16; ATTN_F32 gets ATTN_ERR_DTYPE). Every
+ * sequence of the batch is at the same position. The RoPE tables passed to
+ * these calls must hold at least Tmax rows (attn_rope_tables with T = Tmax).
+ *
+ * Cache layout (one device buffer of attn_kv_cache_bytes()): the rotated keys
+ * R_u k_u as fp16 [B, H, Tmax, D] (rotated in fp32, rounded once; the same
+ * values the forward's rotation pass produces for k), then the values as
+ * [B, H, Tmax, D] dtype. Rows at positions not yet appended are not read.
+ */
+
+/* attn_kv_cache_bytes - 4*B*H*Tmax*D rounded up to 256 (0 for rejected arguments). */
+size_t attn_kv_cache_bytes(int B, int H, int Tmax, int D, int dtype);
+
+/*
+ * attn_kv_append - write n tokens into the cache at positions pos0 .. pos0+n-1
+ * (n = 1 for a generation step, n = prompt length for a prefill).
+ *   k, v      [B, H, n, D] dtype, the pre-RoPE key and value projections of
+ *             those tokens
+ *   cache     the cache buffer (cache_bytes >= attn_kv_cache_bytes(), else
+ *             ATTN_ERR_WORKSPACE); 0 <= pos0, pos0 + n <= Tmax (ATTN_ERR_SHAPE)
+ */
+int attn_kv_append(const void* k, const void* v, const float* cos_tab, const float* sin_tab,
+                   void* cache, size_t cache_bytes, int pos0, int n,
+                   int B, int H, int Tmax, int D, int dtype, void* stream);
+
+/*
+ * attn_decode_workspace_bytes - partial results of attn_decode for any
+ * pos < Tmax: B*H*ceil(Tmax/64)*(D+4) fp32, rounded up to 256.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int Tmax, int D, int dtype);
+
+/*
+ * attn_decode - one generation step at position pos (0 <= pos < Tmax, else
+ * ATTN_ERR_SHAPE), over cache rows 0 .. pos (appended before, on this stream
+ * or completed).
+ *   q         [B, H, D] dtype, the pre-RoPE query of the new token (rotated
+ *             here by position pos)
+ *   o         [B, H, D] dtype, output: softmax over u <= pos of
+ *             (1/sqrt(D)) <R_pos q, R_u k_u>, applied to v
+ *   lse       [B, H] fp32, output: natural log-sum-exp of those scores
+ *   workspace at least attn_decode_workspace_bytes()
+ */
+int attn_decode(const void* q, const void* cache, size_t cache_bytes,
+                const float* cos_tab, const float* sin_tab, void* o, float* lse,
+                void* workspace, size_t workspace_bytes, int pos,
+                int B, int H, int Tmax, int D, int dtype, void* stream);
+
 /* attn_status_string - static, human-readable name of a status code. */
 const char* attn_status_string(int status);
 

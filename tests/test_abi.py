@@ -37,7 +37,9 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_rotated", "attn_rotate_qk", "attn_saved_bytes", "attn_bwd",
               "attn_bwd_prep", "attn_bwd_grads", "attn_rope_tables", "attn_bwd_workspace_bytes",
-              "attn_fwd_packed", "attn_bwd_packed", "attn_status_string", "attn_last_hip_error"):
+              "attn_fwd_packed", "attn_bwd_packed", "attn_kv_cache_bytes", "attn_kv_append",
+              "attn_decode_workspace_bytes", "attn_decode", "attn_status_string",
+              "attn_last_hip_error"):
         assert n in names
 
 
@@ -195,6 +197,48 @@ def test_packed_entry_points_reject_bad_arguments(lib):
     assert g(dqkv=FAKE) == 7                              # dqkv aliases qkv
     assert g(workspace=FAKE + 112) == 7                   # workspace aliases dqkv
     assert g(dqkv=FAKE + 96) == 7                         # dqkv aliases saved
+
+
+def test_decode_sizes(lib):
+    assert attn.attn_kv_cache_bytes(8, 12, 1024, 64, 0) == 4 * 8 * 12 * 1024 * 64
+    assert attn.attn_kv_cache_bytes(8, 12, 1024, 64, 1) == 0             # fp32: no cache path
+    assert attn.attn_kv_cache_bytes(1, 1, 1, 96, 0) == 0                 # unsupported D
+    # one partial (D + 4 floats) per 64-key slice of Tmax, per head
+    assert attn.attn_decode_workspace_bytes(8, 12, 1024, 64, 0) == 8 * 12 * 16 * 68 * 4
+    assert attn.attn_decode_workspace_bytes(1, 2, 65, 128, 2) == ((2 * 2 * 132 * 4 + 255) // 256) * 256
+
+
+def test_decode_entry_points_reject_bad_arguments(lib):
+    cb = 4 * 1 * 1 * 8 * 64
+    ab = dict(k=FAKE, v=FAKE + 16, cos_tab=FAKE + 32, sin_tab=FAKE + 48, cache=FAKE + 64,
+              cache_bytes=cb, pos0=0, n=1, B=1, H=1, Tmax=8, D=64, dtype=0, stream=0)
+    f = lambda **o: status_of(lambda: attn.attn_kv_append(**{**ab, **o}))
+    assert f(k=0) == 1
+    assert f(D=32) == 2
+    assert f(n=0) == 2
+    assert f(pos0=-1) == 2
+    assert f(pos0=7, n=2) == 2                            # past Tmax
+    assert f(dtype=1) == 3
+    assert f(cache=MIS) == 4
+    assert f(cache_bytes=cb - 1) == 5
+    assert f(cache=FAKE) == 7                             # cache aliases k
+    db = dict(q=FAKE, cache=FAKE + 16, cache_bytes=cb, cos_tab=FAKE + 32, sin_tab=FAKE + 48,
+              o=FAKE + 64, lse=FAKE + 80, workspace=FAKE + 96, workspace_bytes=512, pos=3, B=1,
+              H=1, Tmax=8, D=64, dtype=0, stream=0)
+    g = lambda **o: status_of(lambda: attn.attn_decode(**{**db, **o}))
+    assert g(q=0) == 1
+    assert g(lse=0) == 1
+    assert g(pos=8) == 2
+    assert g(pos=-1) == 2
+    assert g(Tmax=0) == 2
+    assert g(dtype=1) == 3
+    assert g(o=MIS) == 4
+    assert g(cache_bytes=8) == 5
+    assert g(workspace=0) == 5
+    assert g(workspace_bytes=255) == 5
+    assert g(workspace=MIS) == 4
+    assert g(o=FAKE) == 7                                 # o aliases q
+    assert g(workspace=FAKE + 16) == 7                    # workspace aliases the cache
 
 
 def test_rope_tables_reject_bad_arguments(lib):

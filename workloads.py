@@ -55,6 +55,9 @@ WORKLOADS = {
                  qk=("normal", 3.0), v=("uniform", 1.0)),
         # wide heads (6 x 128 = 768) at T = 8192
         Workload("wide_bf16_b1h6t8192d128", 1, 6, 8192, 128, "bf16"),
+        # generation over a key/value cache: 8 sequences of the 12-head layer with
+        # 1024 cached positions; the step's query is q at the last position
+        Workload("decode_bf16_b8h12t1024d64", 8, 12, 1024, 64, "bf16"),
     )
 }
 
