@@ -91,6 +91,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.layout == "packed":
         return bench_packed(args, dev)
+    if (args.workload or "").startswith("decode_"):
+        return bench_decode(args, dev)
 
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
@@ -301,6 +303,72 @@ def bench_packed(args, dev):
         "ms_per_step": {n: round(t, 5) for n, t in res.items()},
         "tflops": {n: round(total / (t * 1e-3) / 1e12, 2) for n, t in res.items()},
         "packed_equals_bhtd_bitwise": bool(torch.equal(dqkv, dqkv2) and torch.equal(o_t, o_t2)),
+    }), flush=True)
+
+
+def bench_decode(args, dev):
+    """One JSON line for a decode workload: one generation step (attn_decode at
+    the cache's last position, its partial and combine kernels) and one step with
+    the new token's append (attn_kv_append of one position + attn_decode), each
+    timed over K back-to-back launches between two HIP events; the roofline is
+    HBM: the step must read every cached K' and V row of positions 0 .. pos."""
+    import torch
+
+    import causal_attention_attn_amd as attn
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    B, H, T, D = w.shape
+    dt = {"bf16": attn.ATTN_BF16, "f16": attn.ATTN_F16}[w.dtype]
+    x = workloads.make(w, seed=0)
+    pos = T - 1
+    cache = attn.KVCache(B, H, T, D, workloads.torch_dtype(w.dtype), dev, w.base)
+    cache.append(x["k"].to(dev), x["v"].to(dev), 0)
+    q = x["q"][:, :, pos].contiguous().to(dev)
+    k1 = x["k"][:, :, pos:pos + 1].contiguous().to(dev)
+    v1 = x["v"][:, :, pos:pos + 1].contiguous().to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    sh = torch.cuda.current_stream(dev).cuda_stream
+
+    def decode():
+        attn.attn_decode(q, cache.buf, cache.nbytes, cache.cs, cache.sn, o, lse, cache.ws,
+                         cache.ws_bytes, pos, B, H, T, D, dt, sh)
+
+    def step():
+        attn.attn_kv_append(k1, v1, cache.cs, cache.sn, cache.buf, cache.nbytes, pos, 1, B, H,
+                            T, D, dt, sh)
+        decode()
+
+    def timed(f):
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(torch.cuda.current_stream(dev))
+        for _ in range(args.steps):
+            f()
+        b.record(torch.cuda.current_stream(dev))
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps * 1e3       # us
+
+    t_dec = min(timed(decode) for _ in range(3))
+    t_step = min(timed(step) for _ in range(3))
+    # algorithmic bytes of one step: K' (fp16) and V rows 0 .. pos of every head,
+    # the query and the output row, and lse
+    alg = B * H * ((pos + 1) * D * 2 * 2 + 2 * D * 2 + 4)
+    gbs = alg / (t_dec * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "decode step over a KV cache (B sequences, one new token each), GB/s of "
+                  "algorithmic cache traffic", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "cache_positions": T, "pos": pos, "D": D},
+        "us_per_decode": round(t_dec, 3), "us_per_append_and_decode": round(t_step, 3),
+        "roofline": {"kernel": "decode (partial + combine)", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": alg},
     }), flush=True)
 
 

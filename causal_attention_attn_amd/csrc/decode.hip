@@ -163,21 +163,44 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     }
 }
 
-// Merge a head's slices; one thread per feature.
+// Merge a head's slices; one thread per feature. Slices are taken CH at a time
+// with all their loads issued together (one memory round trip per group; a
+// loop with one dependent load per slice would pay the latency nsplit times),
+// and merged online: the running sums are rescaled when the maximum grows.
 template <int D, typename E>
 __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part,
                                                            E* __restrict__ o,
                                                            float* __restrict__ lse, int nsplit) {
     constexpr int PS = partial_stride<D>();
+    constexpr int CH = 32;
     const int bh = blockIdx.x, d = threadIdx.x;
     const float* P = part + (size_t)bh * nsplit * PS;
-    float M = -INFINITY;
-    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, P[i * PS + D]);
-    float L = 0.f, O = 0.f;
-    for (int i = 0; i < nsplit; ++i) {
-        const float w = exp2_fast(P[i * PS + D] - M);
-        L += w * P[i * PS + D + 1];
-        O += w * P[i * PS + d];
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int c0 = 0; c0 < nsplit; c0 += CH) {
+        float mi[CH], li[CH], oi[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int i = min(c0 + j, nsplit - 1);  // past the end: a repeat, skipped below
+            mi[j] = P[i * PS + D];
+            li[j] = P[i * PS + D + 1];
+            oi[j] = P[i * PS + d];
+        }
+        float cm = M;
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            if (c0 + j < nsplit) cm = fmaxf(cm, mi[j]);
+        const float r = exp2_fast(M - cm);  // 0 on the first group (M = -inf, cm finite)
+        L *= r;
+        O *= r;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            if (c0 + j < nsplit) {
+                const float w = exp2_fast(mi[j] - cm);
+                L += w * li[j];
+                O += w * oi[j];
+            }
+        }
+        M = cm;
     }
     o[(size_t)bh * D + d] = static_cast<E>(O / L);
     if (d == 0) lse[bh] = (M + log2f(L)) * kLn2;
