@@ -147,3 +147,21 @@ def test_append_writes_rotated_keys_and_values():
     untouched = torch.cat([cache.buf[:2 * nk].view(B, H, Tmax, 2 * D)[:, :, :pos0].flatten(),
                            cache.buf[:2 * nk].view(B, H, Tmax, 2 * D)[:, :, pos0 + n:].flatten()])
     assert torch.all(untouched == 0x7E)
+
+
+def test_steps_at_different_positions_share_a_workspace():
+    """Decode steps at different positions reuse one workspace; repeating a
+    step reproduces it exactly."""
+    B, H, Tmax, D = 2, 3, 300, 64
+    q, k, v = inputs(B, H, Tmax, D, "bf16", seed=41)
+    cache = attn.KVCache(B, H, Tmax, D, torch.bfloat16, DEV)
+    cache.append(k.to(DEV), v.to(DEV), 0)
+    first = {}
+    for pos in (299, 5, 64, 299, 130, 5):
+        o, lse = cache.decode(q[:, :, pos].contiguous().to(DEV), pos)
+        torch.cuda.synchronize()
+        if pos in first:
+            assert torch.equal(o, first[pos][0]) and torch.equal(lse, first[pos][1])
+        else:
+            first[pos] = (o.clone(), lse.clone())
+            check(o.cpu(), lse.cpu(), q, k, v, pos, "bf16", f"shared workspace pos {pos}")
