@@ -16,3 +16,10 @@ from .attention import (  # noqa: F401
     rope,
     rope_frequencies,
 )
+from .layers import (  # noqa: F401
+    DEFAULT_EPS,
+    rmsnorm_backward,
+    rmsnorm_forward,
+    swiglu_backward,
+    swiglu_forward,
+)
