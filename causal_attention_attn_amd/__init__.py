@@ -24,10 +24,15 @@ from ._lib import (  # noqa: F401
     attn_kv_append,
     attn_kv_cache_bytes,
     attn_last_hip_error,
+    attn_rmsnorm_bwd,
+    attn_rmsnorm_bwd_workspace_bytes,
+    attn_rmsnorm_fwd,
     attn_rope_tables,
     attn_rotate_qk,
     attn_saved_bytes,
     attn_status_string,
+    attn_swiglu_bwd,
+    attn_swiglu_fwd,
     load,
 )
 from .api import (  # noqa: F401

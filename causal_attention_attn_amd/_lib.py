@@ -45,6 +45,11 @@ _SIGS = {
     "attn_kv_append": (_I, [_P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _I, _P]),
     "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _Z, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _P]),
+    "attn_rmsnorm_fwd": (_I, [_P, _P, _P, ctypes.c_float, _P, _P, _P, _I, _I, _I, _P]),
+    "attn_rmsnorm_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
+    "attn_rmsnorm_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _P]),
+    "attn_swiglu_fwd": (_I, [_P, _P, _I, _I, _I, _P]),
+    "attn_swiglu_bwd": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
 }
@@ -184,6 +189,29 @@ def attn_decode(q, cache, cache_bytes, cos_tab, sin_tab, o, lse, workspace, work
     _call("attn_decode", _ptr(q), _ptr(cache), int(cache_bytes), _ptr(cos_tab), _ptr(sin_tab),
           _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes), pos, B, H, Tmax, D, dtype,
           _stream(stream))
+
+
+def attn_rmsnorm_fwd(x, res, g, eps, h, y, rstd, N, C, dtype, stream=None):
+    _call("attn_rmsnorm_fwd", _ptr(x), _ptr(res), _ptr(g), float(eps), _ptr(h), _ptr(y),
+          _ptr(rstd), N, C, dtype, _stream(stream))
+
+
+def attn_rmsnorm_bwd_workspace_bytes(N, C, dtype):
+    return int(load().attn_rmsnorm_bwd_workspace_bytes(N, C, dtype))
+
+
+def attn_rmsnorm_bwd(h, g, rstd, dy, dres, dh, dg, workspace, workspace_bytes, N, C, dtype,
+                     stream=None):
+    _call("attn_rmsnorm_bwd", _ptr(h), _ptr(g), _ptr(rstd), _ptr(dy), _ptr(dres), _ptr(dh),
+          _ptr(dg), _ptr(workspace), int(workspace_bytes), N, C, dtype, _stream(stream))
+
+
+def attn_swiglu_fwd(u, out, N, F, dtype, stream=None):
+    _call("attn_swiglu_fwd", _ptr(u), _ptr(out), N, F, dtype, _stream(stream))
+
+
+def attn_swiglu_bwd(u, dout, du, N, F, dtype, stream=None):
+    _call("attn_swiglu_bwd", _ptr(u), _ptr(dout), _ptr(du), N, F, dtype, _stream(stream))
 
 
 def attn_status_string(status):

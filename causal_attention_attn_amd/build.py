@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["api.hip", "rope_tables.hip", "fwd_16bit.hip", "bwd_prep.hip", "bwd_16bit.hip",
-           "attn_f32.hip", "decode.hip"]
+           "attn_f32.hip", "decode.hip", "layers.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are switched off for every device pass; hipcc's host

@@ -408,3 +408,96 @@ int attn_decode(const void* q, const void* cache, size_t cache_bytes, const floa
 }
 
 }  // extern "C"
+
+// ---- residual add + RMSNorm, SwiGLU (16-bit path) ----
+
+namespace {
+
+// 16-bit tensors of N rows; the largest holds `elems` elements (< 2^31)
+int check_rows(int N, long long elems, int dtype) {
+    if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_DTYPE;
+    if (N < 1 || elems < 1 || elems >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+int check_norm(int N, int C, int dtype) {
+    if (C < 256 || C > 4096 || C % 256 != 0) return dtype == ATTN_BF16 || dtype == ATTN_F16
+                                                          ? ATTN_ERR_SHAPE : ATTN_ERR_DTYPE;
+    return check_rows(N, (long long)N * C, dtype);
+}
+
+int check_swiglu(int N, int F, int dtype) {
+    if (F < 8 || F % 8 != 0) return dtype == ATTN_BF16 || dtype == ATTN_F16 ? ATTN_ERR_SHAPE
+                                                                            : ATTN_ERR_DTYPE;
+    return check_rows(N, 2ll * N * F, dtype);
+}
+
+size_t norm_ws_need(int N, int C) {
+    return round256((size_t)attn::rmsnorm_bwd_parts(N) * C * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_rmsnorm_fwd(const void* x, const void* res, const void* g, float eps, void* h, void* y,
+                     float* rstd, int N, int C, int dtype, void* stream) {
+    int st = check_norm(N, C, dtype);
+    if (st) return st;
+    if (!(eps > 0.f) || eps != eps || eps > 1e30f) return ATTN_ERR_VALUE;
+    st = check_ptrs({x, g, y, rstd});
+    if (st) return st;
+    if ((res != nullptr && misaligned(res)) || (h != nullptr && misaligned(h))) return ATTN_ERR_ALIGN;
+    if (any_alias({y, rstd}, {x, g}) || (res != nullptr && any_alias({y, rstd}, {res})) ||
+        (h != nullptr && any_alias({h}, {x, g, y, rstd})) ||
+        (h != nullptr && res != nullptr && h == res))
+        return ATTN_ERR_ALIAS;
+    return hip_status(attn::launch_rmsnorm_fwd(x, res, g, eps, h, y, rstd, N, C,
+                                               dtype == ATTN_F16, static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_rmsnorm_bwd_workspace_bytes(int N, int C, int dtype) {
+    if (check_norm(N, C, dtype) != ATTN_OK) return 0;
+    return norm_ws_need(N, C);
+}
+
+int attn_rmsnorm_bwd(const void* h, const void* g, const float* rstd, const void* dy,
+                     const void* dres, void* dh, float* dg, void* workspace,
+                     size_t workspace_bytes, int N, int C, int dtype, void* stream) {
+    int st = check_norm(N, C, dtype);
+    if (st) return st;
+    st = check_ptrs({h, g, rstd, dy, dh, dg});
+    if (st) return st;
+    if (dres != nullptr && misaligned(dres)) return ATTN_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < norm_ws_need(N, C)) return ATTN_ERR_WORKSPACE;
+    if (misaligned(workspace)) return ATTN_ERR_ALIGN;
+    if (any_alias({dh, dg, workspace}, {h, g, rstd, dy}) ||
+        (dres != nullptr && any_alias({dh, dg, workspace}, {dres})))
+        return ATTN_ERR_ALIAS;
+    return hip_status(attn::launch_rmsnorm_bwd(h, g, rstd, dy, dres, dh, dg,
+                                               static_cast<float*>(workspace), N, C,
+                                               dtype == ATTN_F16, static_cast<hipStream_t>(stream)));
+}
+
+int attn_swiglu_fwd(const void* u, void* out, int N, int F, int dtype, void* stream) {
+    int st = check_swiglu(N, F, dtype);
+    if (st) return st;
+    st = check_ptrs({u, out});
+    if (st) return st;
+    if (any_alias({out}, {u})) return ATTN_ERR_ALIAS;
+    return hip_status(attn::launch_swiglu(u, nullptr, out, N, F, false, dtype == ATTN_F16,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int attn_swiglu_bwd(const void* u, const void* dout, void* du, int N, int F, int dtype,
+                    void* stream) {
+    int st = check_swiglu(N, F, dtype);
+    if (st) return st;
+    st = check_ptrs({u, dout, du});
+    if (st) return st;
+    if (any_alias({du}, {u, dout})) return ATTN_ERR_ALIAS;
+    return hip_status(attn::launch_swiglu(u, dout, du, N, F, true, dtype == ATTN_F16,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

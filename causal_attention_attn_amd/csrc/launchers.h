@@ -79,6 +79,18 @@ hipError_t launch_decode(const void* q, const void* cache, const float* cs, cons
                          void* o, float* lse, float* ws, int pos, int B, int H, int Tmax, int D,
                          bool f16_storage, hipStream_t s);
 
+// The per-layer kernels next to attention (16-bit path): residual add +
+// RMSNorm and SwiGLU.
+int rmsnorm_bwd_parts(int N);  // workgroups of the backward = rows of its fp32 partial sums
+hipError_t launch_rmsnorm_fwd(const void* x, const void* r, const void* g, float eps, void* h,
+                              void* y, float* rstd, int N, int C, bool f16_storage,
+                              hipStream_t s);
+hipError_t launch_rmsnorm_bwd(const void* h, const void* g, const float* rstd, const void* dy,
+                              const void* dres, void* dh, float* dg, float* part, int N, int C,
+                              bool f16_storage, hipStream_t s);
+hipError_t launch_swiglu(const void* u, const void* dout, void* out, int N, int F, bool backward,
+                         bool f16_storage, hipStream_t s);
+
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_prep_f32(const BwdArgs& a);    // workspace entries (delta)
 hipError_t launch_bwd_dq_f32(const BwdArgs& a);

@@ -1,0 +1,293 @@
+// The per-layer kernels next to attention, 16-bit storage (bf16 or fp16, type
+// E) with fp32 arithmetic, gfx950: residual add + RMSNorm, and SwiGLU.
+//
+// The pages list RMSNorm and SwiGLU among the engine's hand-written CUDA kernels
+// ("Show HN: NanoEuler", paragraph 2); each layer is causal attention plus a
+// feed-forward network of two linear transforms with a Swish activation, both
+// wrapped in residual connections ("Tiny Hackable CUDA", section 3). Readings:
+//   h = x + r (the residual stream, stored as E), y = h * rstd * g,
+//   rstd = 1 / sqrt(mean(h^2) + eps);  backward dh = rstd (g dy - h^ mean(h^ g dy))
+//   + dres, dg = sum over rows of dy h^ (h^ = h rstd);
+//   SwiGLU on the fused gate/up output u = [a | b]: out = silu(a) b,
+//   da = dout b s (1 + a (1 - s)), db = dout silu(a), s = sigmoid(a).
+//
+// All of it is elementwise or a per-row reduction over C: bound by HBM. Rows
+// are read with coalesced 8- or 16-byte loads, each row once (the RMSNorm row
+// stays in registers between its two passes), and every output is written once.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace attn {
+
+constexpr int kNormMaxChunks = 16;  // C <= 16 * 256 = 4096; kernels take NCH = C / 256
+
+template <typename E>
+__device__ __forceinline__ f32x4 load4(const E* p) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    const f32x2 lo = unpack2<E>(w[0]), hi = unpack2<E>(w[1]);
+    return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+template <typename E>
+__device__ __forceinline__ void store4(E* p, f32x4 v) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack2<E>(v[0], v[1]), pack2<E>(v[2], v[3])};
+}
+
+// Round each value to E and back (the stored residual stream is what the norm sees).
+template <typename E>
+__device__ __forceinline__ f32x4 round4(f32x4 v) {
+    const f32x2 lo = unpack2<E>(pack2<E>(v[0], v[1])), hi = unpack2<E>(pack2<E>(v[2], v[3]));
+    return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+// One wave per row; lane l holds features 4l + 256j, j < NCH = C/256.
+template <typename E, int NCH>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const E* __restrict__ x,
+                                                          const E* __restrict__ r,
+                                                          const E* __restrict__ g, float eps,
+                                                          E* __restrict__ h, E* __restrict__ y,
+                                                          float* __restrict__ rstd, int N, int C) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= N) return;
+    const size_t base = (size_t)row * C + 4 * lane;
+    f32x4 v[NCH];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        f32x4 a = load4(x + base + 256 * j);
+        if (r != nullptr) a = round4<E>(a + load4(r + base + 256 * j));
+        v[j] = a;
+        ss += a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3];
+    }
+    const float rs = 1.f / sqrtf(wave_sum(ss) / (float)C + eps);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        if (h != nullptr) store4(h + base + 256 * j, v[j]);
+        store4(y + base + 256 * j, v[j] * rs * load4(g + 4 * lane + 256 * j));
+    }
+    if (lane == 0) rstd[row] = rs;
+}
+
+// One wave per row, rows grid-strided; each workgroup leaves its column sums of
+// dy * h^ in part[blockIdx.x][C] (fp32) for the dg reduction.
+template <typename E, int NCH>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
+    const E* __restrict__ h, const E* __restrict__ g, const float* __restrict__ rstd,
+    const E* __restrict__ dy, const E* __restrict__ dres, E* __restrict__ dh,
+    float* __restrict__ part, int N, int C) {
+    __shared__ f32x4 red[4][64][4];  // per wave: its lanes' column sums, 4 chunks at a time
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 gg[NCH], acc[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        acc[j] = zero;
+        gg[j] = load4(g + 4 * lane + 256 * j);
+    }
+    for (int row = blockIdx.x * 4 + wave; row < N; row += gridDim.x * 4) {
+        const size_t base = (size_t)row * C + 4 * lane;
+        const float rs = rstd[row];
+        f32x4 hh[NCH], gd[NCH];
+        float dot = 0.f;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            hh[j] = load4(h + base + 256 * j) * rs;
+            const f32x4 d = load4(dy + base + 256 * j);
+            gd[j] = gg[j] * d;
+            acc[j] += d * hh[j];
+            const f32x4 p = hh[j] * gd[j];
+            dot += p[0] + p[1] + p[2] + p[3];
+        }
+        const float mean = wave_sum(dot) / (float)C;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            f32x4 o = (gd[j] - hh[j] * mean) * rs;
+            if (dres != nullptr) o += load4(dres + base + 256 * j);
+            store4(dh + base + 256 * j, o);
+        }
+    }
+    // the workgroup's column sums: four waves added through LDS, four chunks at a time
+#pragma unroll
+    for (int j0 = 0; j0 < NCH; j0 += 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) red[wave][lane][k] = j0 + k < NCH ? acc[j0 + k] : zero;
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (j0 + k < NCH) {
+                    const f32x4 s = red[0][lane][k] + red[1][lane][k] + red[2][lane][k] +
+                                    red[3][lane][k];
+                    *reinterpret_cast<f32x4*>(part + (size_t)blockIdx.x * C + 4 * lane +
+                                              256 * (j0 + k)) = s;
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// dg[c] = sum over the workgroups' partial column sums (fixed order: deterministic).
+__global__ __launch_bounds__(256) void rmsnorm_dg_kernel(const float* __restrict__ part,
+                                                         float* __restrict__ dg, int nparts,
+                                                         int C) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= C) return;
+    float s = 0.f;
+    for (int i = 0; i < nparts; ++i) s += part[(size_t)i * C + c];
+    dg[c] = s;
+}
+
+__device__ __forceinline__ float sigmoid_f(float a) { return 1.f / (1.f + __expf(-a)); }
+
+// One thread per 8 consecutive outputs of a row.
+template <typename E, bool BACKWARD>
+__global__ __launch_bounds__(256) void swiglu_kernel(const E* __restrict__ u,
+                                                     const E* __restrict__ dout,
+                                                     E* __restrict__ out, long long n8, int F) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const int f8 = F >> 3;
+    const long long row = i / f8;
+    const int col = (int)(i - row * f8) * 8;
+    const E* ur = u + row * 2 * F;
+    const u32x4 wa = *reinterpret_cast<const u32x4*>(ur + col);
+    const u32x4 wb = *reinterpret_cast<const u32x4*>(ur + F + col);
+    if constexpr (!BACKWARD) {
+        u32x4 w;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const f32x2 a = unpack2<E>(wa[p]), b = unpack2<E>(wb[p]);
+            w[p] = pack2<E>(a[0] * sigmoid_f(a[0]) * b[0], a[1] * sigmoid_f(a[1]) * b[1]);
+        }
+        *reinterpret_cast<u32x4*>(out + row * F + col) = w;
+    } else {
+        const u32x4 wd = *reinterpret_cast<const u32x4*>(dout + row * F + col);
+        u32x4 da, db;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const f32x2 a = unpack2<E>(wa[p]), b = unpack2<E>(wb[p]), d = unpack2<E>(wd[p]);
+            float ga[2], gb[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float s = sigmoid_f(a[e]);
+                ga[e] = d[e] * b[e] * s * (1.f + a[e] * (1.f - s));
+                gb[e] = d[e] * a[e] * s;
+            }
+            da[p] = pack2<E>(ga[0], ga[1]);
+            db[p] = pack2<E>(gb[0], gb[1]);
+        }
+        E* gr = out + row * 2 * F;
+        *reinterpret_cast<u32x4*>(gr + col) = da;
+        *reinterpret_cast<u32x4*>(gr + F + col) = db;
+    }
+}
+
+// Explicit instantiations: the host pass does not always emit the launch stub of
+// a kernel template with a 16-bit element-type argument on its own.
+#define ATTN_NORM_INST(E_, K_)                                                                  \
+    template __global__ void rmsnorm_fwd_kernel<E_, K_>(const E_*, const E_*, const E_*, float, \
+                                                        E_*, E_*, float*, int, int);            \
+    template __global__ void rmsnorm_bwd_kernel<E_, K_>(const E_*, const E_*, const float*,     \
+                                                        const E_*, const E_*, E_*, float*, int, \
+                                                        int);
+#define ATTN_NORM_INST_ALL(E_)                                                                  \
+    ATTN_NORM_INST(E_, 1) ATTN_NORM_INST(E_, 2) ATTN_NORM_INST(E_, 3) ATTN_NORM_INST(E_, 4)     \
+    ATTN_NORM_INST(E_, 5) ATTN_NORM_INST(E_, 6) ATTN_NORM_INST(E_, 7) ATTN_NORM_INST(E_, 8)     \
+    ATTN_NORM_INST(E_, 9) ATTN_NORM_INST(E_, 10) ATTN_NORM_INST(E_, 11) ATTN_NORM_INST(E_, 12)  \
+    ATTN_NORM_INST(E_, 13) ATTN_NORM_INST(E_, 14) ATTN_NORM_INST(E_, 15) ATTN_NORM_INST(E_, 16)
+ATTN_NORM_INST_ALL(bf16) ATTN_NORM_INST_ALL(f16)
+#undef ATTN_NORM_INST_ALL
+#undef ATTN_NORM_INST
+template __global__ void swiglu_kernel<bf16, false>(const bf16*, const bf16*, bf16*, long long, int);
+template __global__ void swiglu_kernel<bf16, true>(const bf16*, const bf16*, bf16*, long long, int);
+template __global__ void swiglu_kernel<f16, false>(const f16*, const f16*, f16*, long long, int);
+template __global__ void swiglu_kernel<f16, true>(const f16*, const f16*, f16*, long long, int);
+
+// Calls f(std::integral_constant<int, nch>{}) for nch in 1 .. kNormMaxChunks.
+template <int K = 1, typename F>
+static hipError_t with_chunks(int nch, F&& f) {
+    if constexpr (K > kNormMaxChunks) {
+        return hipErrorInvalidValue;
+    } else {
+        if (nch == K) return f(std::integral_constant<int, K>{});
+        return with_chunks<K + 1>(nch, f);
+    }
+}
+
+int rmsnorm_bwd_parts(int N) {
+    const int wgs = (N + 3) / 4;
+    return wgs < 1024 ? wgs : 1024;
+}
+
+template <typename E>
+static hipError_t rmsnorm_fwd_t(const void* x, const void* r, const void* g, float eps, void* h,
+                                void* y, float* rstd, int N, int C, hipStream_t st) {
+    return with_chunks(C >> 8, [&](auto K) {
+        hipLaunchKernelGGL((rmsnorm_fwd_kernel<E, decltype(K)::value>),
+                           dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, (const E*)x,
+                           (const E*)r, (const E*)g, eps, (E*)h, (E*)y, rstd, N, C);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_rmsnorm_fwd(const void* x, const void* r, const void* g, float eps, void* h,
+                              void* y, float* rstd, int N, int C, bool f16_storage,
+                              hipStream_t st) {
+    return f16_storage ? rmsnorm_fwd_t<f16>(x, r, g, eps, h, y, rstd, N, C, st)
+                       : rmsnorm_fwd_t<bf16>(x, r, g, eps, h, y, rstd, N, C, st);
+}
+
+template <typename E>
+static hipError_t rmsnorm_bwd_t(const void* h, const void* g, const float* rstd, const void* dy,
+                                const void* dres, void* dh, float* dg, float* part, int N,
+                                int C, hipStream_t st) {
+    const int parts = rmsnorm_bwd_parts(N);
+    hipError_t e = with_chunks(C >> 8, [&](auto K) {
+        hipLaunchKernelGGL((rmsnorm_bwd_kernel<E, decltype(K)::value>), dim3((unsigned)parts),
+                           dim3(256), 0, st, (const E*)h, (const E*)g, rstd, (const E*)dy,
+                           (const E*)dres, (E*)dh, part, N, C);
+        return hipGetLastError();
+    });
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(rmsnorm_dg_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, st,
+                       part, dg, parts, C);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bwd(const void* h, const void* g, const float* rstd, const void* dy,
+                              const void* dres, void* dh, float* dg, float* part, int N, int C,
+                              bool f16_storage, hipStream_t st) {
+    return f16_storage ? rmsnorm_bwd_t<f16>(h, g, rstd, dy, dres, dh, dg, part, N, C, st)
+                       : rmsnorm_bwd_t<bf16>(h, g, rstd, dy, dres, dh, dg, part, N, C, st);
+}
+
+template <typename E>
+static hipError_t swiglu_t(const void* u, const void* dout, void* out, int N, int F,
+                           bool backward, hipStream_t st) {
+    const long long n8 = (long long)N * (F / 8);
+    const unsigned blocks = (unsigned)((n8 + 255) / 256);
+    if (backward)
+        hipLaunchKernelGGL((swiglu_kernel<E, true>), dim3(blocks), dim3(256), 0, st, (const E*)u,
+                           (const E*)dout, (E*)out, n8, F);
+    else
+        hipLaunchKernelGGL((swiglu_kernel<E, false>), dim3(blocks), dim3(256), 0, st,
+                           (const E*)u, (const E*)nullptr, (E*)out, n8, F);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const void* u, const void* dout, void* out, int N, int F, bool backward,
+                         bool f16_storage, hipStream_t st) {
+    return f16_storage ? swiglu_t<f16>(u, dout, out, N, F, backward, st)
+                       : swiglu_t<bf16>(u, dout, out, N, F, backward, st);
+}
+
+}  // namespace attn

@@ -299,6 +299,66 @@ int attn_decode(const void* q, const void* cache, size_t cache_bytes,
                 void* workspace, size_t workspace_bytes, int pos,
                 int B, int H, int Tmax, int D, int dtype, void* stream);
 
+/*
+ * The per-layer kernels next to attention. The pages list RMSNorm and SwiGLU
+ * among the engine's hand-written CUDA kernels ("Show HN: NanoEuler",
+ * paragraph 2); each layer is causal attention plus a feed-forward network of
+ * two linear transforms with a Swish activation, both wrapped in residual
+ * connections ("Tiny Hackable CUDA", section 3). They give no formulas; the
+ * readings implemented here:
+ *   h = x + r                      (the residual stream, stored in dtype)
+ *   y = h * rstd * g,  rstd = 1 / sqrt(mean over the C features of h^2 + eps)
+ *   swiglu(u) = silu(a) * b for u = [a | b] (the fused gate/up projection),
+ *   silu(a) = a * sigmoid(a)
+ * 16-bit path only (ATTN_BF16, ATTN_F16; ATTN_F32 gets ATTN_ERR_DTYPE); every
+ * tensor is row-major with rows of C (or 2F / F) elements, fp32 arithmetic.
+ */
+
+/*
+ * attn_rmsnorm_fwd - residual add + RMSNorm of N rows of C features
+ * (C a multiple of 256, 256 <= C <= 4096; N*C < 2^31).
+ *   x         [N, C] dtype, input
+ *   res       [N, C] dtype, residual added to x (NULL: h = x)
+ *   g         [C] dtype, per-feature gain
+ *   eps       > 0 (ATTN_ERR_VALUE otherwise); 1e-5 for the model read here
+ *   h         [N, C] dtype, output x + res as stored (NULL: not written)
+ *   y         [N, C] dtype, output
+ *   rstd      [N] fp32, output (kept for the backward)
+ */
+int attn_rmsnorm_fwd(const void* x, const void* res, const void* g, float eps,
+                     void* h, void* y, float* rstd, int N, int C, int dtype, void* stream);
+
+/* attn_rmsnorm_bwd_workspace_bytes - min(ceil(N/4), 1024) * C fp32, rounded up to 256. */
+size_t attn_rmsnorm_bwd_workspace_bytes(int N, int C, int dtype);
+
+/*
+ * attn_rmsnorm_bwd - gradients of L = sum(y * dy) + sum(h * dres):
+ *   dh = rstd * (g*dy - h^ * mean(h^ * g * dy)) + dres, h^ = h * rstd,
+ * the gradient of x and of res alike; dg = sum over rows of dy * h^ (a fixed
+ * reduction order: deterministic).
+ *   h, g, rstd  the forward's h (or x when it had no residual), gain and rstd
+ *   dy          [N, C] dtype;  dres [N, C] dtype or NULL (zero)
+ *   dh          [N, C] dtype, output;  dg [C] fp32, output
+ *   workspace   at least attn_rmsnorm_bwd_workspace_bytes()
+ */
+int attn_rmsnorm_bwd(const void* h, const void* g, const float* rstd, const void* dy,
+                     const void* dres, void* dh, float* dg, void* workspace,
+                     size_t workspace_bytes, int N, int C, int dtype, void* stream);
+
+/*
+ * attn_swiglu_fwd - out = silu(a) * b for each row u = [a | b] of the fused
+ * gate/up projection. u [N, 2F] dtype, out [N, F] dtype; F a multiple of 8,
+ * 2*N*F < 2^31.
+ */
+int attn_swiglu_fwd(const void* u, void* out, int N, int F, int dtype, void* stream);
+
+/*
+ * attn_swiglu_bwd - du = [da | db], [N, 2F] dtype, for upstream dout [N, F]:
+ * da = dout * b * s * (1 + a * (1 - s)), db = dout * silu(a), s = sigmoid(a).
+ */
+int attn_swiglu_bwd(const void* u, const void* dout, void* du, int N, int F, int dtype,
+                    void* stream);
+
 /* attn_status_string - static, human-readable name of a status code. */
 const char* attn_status_string(int status);
 

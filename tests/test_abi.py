@@ -38,8 +38,9 @@ def test_header_declares_the_entry_points():
     for n in ("attn_fwd", "attn_fwd_rotated", "attn_rotate_qk", "attn_saved_bytes", "attn_bwd",
               "attn_bwd_prep", "attn_bwd_grads", "attn_rope_tables", "attn_bwd_workspace_bytes",
               "attn_fwd_packed", "attn_bwd_packed", "attn_kv_cache_bytes", "attn_kv_append",
-              "attn_decode_workspace_bytes", "attn_decode", "attn_status_string",
-              "attn_last_hip_error"):
+              "attn_decode_workspace_bytes", "attn_decode", "attn_rmsnorm_fwd",
+              "attn_rmsnorm_bwd_workspace_bytes", "attn_rmsnorm_bwd", "attn_swiglu_fwd",
+              "attn_swiglu_bwd", "attn_status_string", "attn_last_hip_error"):
         assert n in names
 
 
@@ -239,6 +240,53 @@ def test_decode_entry_points_reject_bad_arguments(lib):
     assert g(workspace=MIS) == 4
     assert g(o=FAKE) == 7                                 # o aliases q
     assert g(workspace=FAKE + 16) == 7                    # workspace aliases the cache
+
+
+def test_layer_entry_points_reject_bad_arguments(lib):
+    assert attn.attn_rmsnorm_bwd_workspace_bytes(8192, 768, 0) == 1024 * 768 * 4
+    assert attn.attn_rmsnorm_bwd_workspace_bytes(5, 256, 2) == 2 * 256 * 4
+    assert attn.attn_rmsnorm_bwd_workspace_bytes(5, 300, 0) == 0
+    fb = dict(x=FAKE, res=FAKE + 16, g=FAKE + 32, eps=1e-5, h=FAKE + 48, y=FAKE + 64,
+              rstd=FAKE + 80, N=4, C=256, dtype=0, stream=0)
+    f = lambda **o: status_of(lambda: attn.attn_rmsnorm_fwd(**{**fb, **o}))
+    assert f(x=0) == 1
+    assert f(y=0) == 1
+    assert f(C=300) == 2
+    assert f(C=4352) == 2
+    assert f(N=0) == 2
+    assert f(dtype=1) == 3
+    assert f(eps=0.0) == 8
+    assert f(eps=float("nan")) == 8
+    assert f(res=MIS) == 4
+    assert f(h=MIS) == 4
+    assert f(y=FAKE) == 7                                 # y aliases x
+    assert f(h=FAKE + 16) == 7                            # h aliases res
+    bb = dict(h=FAKE, g=FAKE + 16, rstd=FAKE + 32, dy=FAKE + 48, dres=FAKE + 64, dh=FAKE + 80,
+              dg=FAKE + 96, workspace=FAKE + 112, workspace_bytes=1024, N=4, C=256, dtype=0,
+              stream=0)
+    g = lambda **o: status_of(lambda: attn.attn_rmsnorm_bwd(**{**bb, **o}))
+    assert g(dy=0) == 1
+    assert g(C=128) == 2
+    assert g(dtype=1) == 3
+    assert g(dres=MIS) == 4
+    assert g(workspace=0) == 5
+    assert g(workspace_bytes=1023) == 5
+    assert g(dh=FAKE) == 7                                # dh aliases h
+    assert g(dg=FAKE + 64) == 7                           # dg aliases dres
+    sf = lambda **o: status_of(lambda: attn.attn_swiglu_fwd(
+        **{**dict(u=FAKE, out=FAKE + 16, N=2, F=8, dtype=0, stream=0), **o}))
+    assert sf(u=0) == 1
+    assert sf(F=12) == 2
+    assert sf(F=0) == 2
+    assert sf(dtype=1) == 3
+    assert sf(out=MIS) == 4
+    assert sf(out=FAKE) == 7
+    sb = lambda **o: status_of(lambda: attn.attn_swiglu_bwd(
+        **{**dict(u=FAKE, dout=FAKE + 16, du=FAKE + 32, N=2, F=8, dtype=0, stream=0), **o}))
+    assert sb(dout=0) == 1
+    assert sb(N=0) == 2
+    assert sb(dtype=7) == 3
+    assert sb(du=FAKE + 16) == 7
 
 
 def test_rope_tables_reject_bad_arguments(lib):

@@ -61,6 +61,40 @@ WORKLOADS = {
     )
 }
 
+# the per-layer kernels next to attention, over the headline batch's B*T = 8192
+# token rows: RMSNorm over the model width 768, SwiGLU over a feed-forward width
+# of 2048 (two thirds of 4 x 768, the usual SwiGLU sizing)
+LAYER_WORKLOADS = {
+    "rmsnorm_bf16_n8192c768": ("rmsnorm", 8192, 768, "bf16"),
+    "swiglu_bf16_n8192f2048": ("swiglu", 8192, 2048, "bf16"),
+}
+
+
+def layer_inputs(kind, N, width, dtype, seed=0):
+    """Seeded inputs of a per-layer kernel as CPU torch tensors in `dtype`.
+
+    rmsnorm (width C): x, r ~ N(0, 1) [N, C]; g ~ 1 + N(0, 0.1^2) [C];
+    dy, dres ~ N(0, 0.1^2) [N, C]. swiglu (width F): u ~ N(0, 1) [N, 2F];
+    dout ~ N(0, 0.1^2) [N, F]. Drawn in that order with PCG64(seed).
+    """
+    import torch
+    rng = np.random.default_rng(seed)
+    td = torch_dtype(dtype)
+    t = lambda a: torch.from_numpy(a).to(td)
+    if kind == "rmsnorm":
+        x = rng.standard_normal((N, width))
+        r = rng.standard_normal((N, width))
+        g = 1.0 + 0.1 * rng.standard_normal(width)
+        dy = 0.1 * rng.standard_normal((N, width))
+        dres = 0.1 * rng.standard_normal((N, width))
+        return dict(x=t(x), r=t(r), g=t(g), dy=t(dy), dres=t(dres))
+    if kind == "swiglu":
+        u = rng.standard_normal((N, 2 * width))
+        dout = 0.1 * rng.standard_normal((N, width))
+        return dict(u=t(u), dout=t(dout))
+    raise ValueError(f"unknown layer kind {kind!r}")
+
+
 # the workload the throughput figure is quoted on
 HEADLINE = "gpt2s_bf16_b8h12t1024d64"
 TINY = "tiny_f32_b1h2t64d64"
