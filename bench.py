@@ -93,6 +93,8 @@ def main():
         return bench_packed(args, dev)
     if (args.workload or "").startswith("decode_"):
         return bench_decode(args, dev)
+    if args.workload in workloads.LAYER_WORKLOADS:
+        return bench_layer(args, dev)
 
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
@@ -369,6 +371,83 @@ def bench_decode(args, dev):
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                      "bytes_per_launch": alg},
+    }), flush=True)
+
+
+def bench_layer(args, dev):
+    """One JSON line for a per-layer workload (residual add + RMSNorm, or SwiGLU):
+    the forward and the backward each timed over K back-to-back launches between
+    two HIP events; HBM roofline on the algorithmic bytes (every input read
+    once, every output written once)."""
+    import torch
+
+    import causal_attention_attn_amd as attn
+    import workloads
+
+    kind, N, W, dt_name = workloads.LAYER_WORKLOADS[args.workload]
+    code = {"bf16": attn.ATTN_BF16, "f16": attn.ATTN_F16}[dt_name]
+    x = {n: t.to(dev) for n, t in workloads.layer_inputs(kind, N, W, dt_name).items()}
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    if kind == "rmsnorm":
+        C = W
+        h, y, dh = (torch.empty_like(x["x"]) for _ in range(3))
+        rstd = torch.empty(N, dtype=torch.float32, device=dev)
+        dg = torch.empty(C, dtype=torch.float32, device=dev)
+        nw = attn.attn_rmsnorm_bwd_workspace_bytes(N, C, code)
+        ws = torch.empty(nw, dtype=torch.uint8, device=dev)
+
+        def fwd():
+            attn.attn_rmsnorm_fwd(x["x"], x["r"], x["g"], 1e-5, h, y, rstd, N, C, code, sh)
+
+        def bwd():
+            attn.attn_rmsnorm_bwd(h, x["g"], rstd, x["dy"], x["dres"], dh, dg, ws, nw, N, C, code,
+                                  sh)
+        # fwd: x, r read, h, y written (+ g, rstd); bwd: h, dy, dres read, dh written (+ g, rstd, dg)
+        b_fwd = 4 * N * C * 2 + C * 2 + N * 4
+        b_bwd = 4 * N * C * 2 + C * 2 + N * 4 + C * 4
+        shape = {"N": N, "C": C}
+    else:
+        F = W
+        out = torch.empty((N, F), dtype=x["u"].dtype, device=dev)
+        du = torch.empty_like(x["u"])
+
+        def fwd():
+            attn.attn_swiglu_fwd(x["u"], out, N, F, code, sh)
+
+        def bwd():
+            attn.attn_swiglu_bwd(x["u"], x["dout"], du, N, F, code, sh)
+        b_fwd = N * 2 * F * 2 + N * F * 2
+        b_bwd = N * 2 * F * 2 + N * F * 2 + N * 2 * F * 2
+        shape = {"N": N, "F": F}
+
+    def timed(f):
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(torch.cuda.current_stream(dev))
+        for _ in range(args.steps):
+            f()
+        b.record(torch.cuda.current_stream(dev))
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps * 1e3       # us
+
+    t_f = min(timed(fwd) for _ in range(3))
+    t_b = min(timed(bwd) for _ in range(3))
+    gbs = lambda b, t: round(b / (t * 1e-6) / 1e9, 1)
+    value = gbs(b_fwd + b_bwd, t_f + t_b)
+    dom_b, dom_t, dom = (b_bwd, t_b, "bwd") if t_b >= t_f else (b_fwd, t_f, "fwd")
+    print(json.dumps({
+        "metric": f"{kind} forward + backward, GB/s of algorithmic HBM traffic", "value": value,
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "dtype": dt_name, "data": "synthetic",
+        "config": {"workload": args.workload, **shape},
+        "kernels": {"fwd": {"avg_us": round(t_f, 3), "gbs": gbs(b_fwd, t_f), "bytes": b_fwd},
+                    "bwd": {"avg_us": round(t_b, 3), "gbs": gbs(b_bwd, t_b), "bytes": b_bwd}},
+        "roofline": {"kernel": f"{kind} {dom}", "bound": "hbm", "achieved": gbs(dom_b, dom_t),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(dom_b / (dom_t * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": None},
     }), flush=True)
 
 

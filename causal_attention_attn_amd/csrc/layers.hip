@@ -92,26 +92,46 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
         acc[j] = zero;
         gg[j] = load4(g + 4 * lane + 256 * j);
     }
-    for (int row = blockIdx.x * 4 + wave; row < N; row += gridDim.x * 4) {
-        const size_t base = (size_t)row * C + 4 * lane;
-        const float rs = rstd[row];
-        f32x4 hh[NCH], gd[NCH];
-        float dot = 0.f;
+    // RP rows per pass (two while they fit in registers), all of their loads
+    // issued before any arithmetic
+    constexpr int RP = NCH <= 8 ? 2 : 1;
+    const int stride = gridDim.x * 4;
+    for (int row0 = blockIdx.x * 4 + wave; row0 < N; row0 += RP * stride) {
+        f32x4 hv[RP][NCH], dv[RP][NCH], rv[RP][NCH];
+        float rs[RP];
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            hh[j] = load4(h + base + 256 * j) * rs;
-            const f32x4 d = load4(dy + base + 256 * j);
-            gd[j] = gg[j] * d;
-            acc[j] += d * hh[j];
-            const f32x4 p = hh[j] * gd[j];
-            dot += p[0] + p[1] + p[2] + p[3];
+        for (int q = 0; q < RP; ++q) {
+            const int row = row0 + q * stride;
+            if (row < N) {  // uniform
+                const size_t base = (size_t)row * C + 4 * lane;
+                rs[q] = rstd[row];
+#pragma unroll
+                for (int j = 0; j < NCH; ++j) {
+                    hv[q][j] = load4(h + base + 256 * j);
+                    dv[q][j] = load4(dy + base + 256 * j);
+                    rv[q][j] = dres != nullptr ? load4(dres + base + 256 * j) : zero;
+                }
+            }
         }
-        const float mean = wave_sum(dot) / (float)C;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            f32x4 o = (gd[j] - hh[j] * mean) * rs;
-            if (dres != nullptr) o += load4(dres + base + 256 * j);
-            store4(dh + base + 256 * j, o);
+        for (int q = 0; q < RP; ++q) {
+            const int row = row0 + q * stride;
+            if (row >= N) break;  // uniform
+            const size_t base = (size_t)row * C + 4 * lane;
+            f32x4 hh[NCH], gd[NCH];
+            float dot = 0.f;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                hh[j] = hv[q][j] * rs[q];
+                gd[j] = gg[j] * dv[q][j];
+                acc[j] += dv[q][j] * hh[j];
+                const f32x4 p = hh[j] * gd[j];
+                dot += p[0] + p[1] + p[2] + p[3];
+            }
+            const float mean = wave_sum(dot) / (float)C;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+                store4(dh + base + 256 * j, (gd[j] - hh[j] * mean) * rs[q] + rv[q][j]);
         }
     }
     // the workgroup's column sums: four waves added through LDS, four chunks at a time
@@ -135,15 +155,35 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
     }
 }
 
-// dg[c] = sum over the workgroups' partial column sums (fixed order: deterministic).
-__global__ __launch_bounds__(256) void rmsnorm_dg_kernel(const float* __restrict__ part,
-                                                         float* __restrict__ dg, int nparts,
-                                                         int C) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= C) return;
+// dg[c] = sum over the workgroups' partial column sums. A block of 1024 threads
+// takes 64 columns; thread (k, c) adds partials k, k + 16, ... of its column with
+// 16 loads in flight at a time (a load per iteration would pay the memory latency
+// nparts times), then the 16 groups are added in a fixed order: deterministic.
+__global__ __launch_bounds__(1024) void rmsnorm_dg_kernel(const float* __restrict__ part,
+                                                          float* __restrict__ dg, int nparts,
+                                                          int C) {
+    __shared__ float red[16][64];
+    const int cx = threadIdx.x & 63, k0 = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + cx;  // C is a multiple of 256: always < C
     float s = 0.f;
-    for (int i = 0; i < nparts; ++i) s += part[(size_t)i * C + c];
-    dg[c] = s;
+    for (int i0 = k0; i0 < nparts; i0 += 16 * 16) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int i = i0 + 16 * j;
+            v[j] = i < nparts ? part[(size_t)i * C + c] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s += v[j];
+    }
+    red[k0][cx] = s;
+    __syncthreads();
+    if (k0 == 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) t += red[j][cx];
+        dg[c] = t;
+    }
 }
 
 __device__ __forceinline__ float sigmoid_f(float a) { return 1.f / (1.f + __expf(-a)); }
@@ -258,8 +298,8 @@ static hipError_t rmsnorm_bwd_t(const void* h, const void* g, const float* rstd,
         return hipGetLastError();
     });
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(rmsnorm_dg_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, st,
-                       part, dg, parts, C);
+    hipLaunchKernelGGL(rmsnorm_dg_kernel, dim3((unsigned)(C / 64)), dim3(1024), 0, st, part, dg,
+                       parts, C);
     return hipGetLastError();
 }
 
