@@ -310,10 +310,11 @@ def bench_packed(args, dev):
 
 def bench_decode(args, dev):
     """One JSON line for a decode workload: one generation step (attn_decode at
-    the cache's last position, its partial and combine kernels) and one step with
-    the new token's append (attn_kv_append of one position + attn_decode), each
-    timed over K back-to-back launches between two HIP events; the roofline is
-    HBM: the step must read every cached K' and V row of positions 0 .. pos."""
+    the cache's last position, its partial and combine kernels), the step with
+    the new token's append as two calls (attn_kv_append of one position +
+    attn_decode) and as one (attn_decode_step), each timed over K back-to-back
+    launches between two HIP events; the roofline is HBM: the step must read
+    every cached K' and V row of positions 0 .. pos."""
     import torch
 
     import causal_attention_attn_amd as attn
@@ -354,8 +355,13 @@ def bench_decode(args, dev):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / args.steps * 1e3       # us
 
+    def fused():
+        attn.attn_decode_step(q, k1, v1, cache.buf, cache.nbytes, cache.cs, cache.sn, o, lse,
+                              cache.ws, cache.ws_bytes, pos, B, H, T, D, dt, sh)
+
     t_dec = min(timed(decode) for _ in range(3))
     t_step = min(timed(step) for _ in range(3))
+    t_fused = min(timed(fused) for _ in range(3))
     # algorithmic bytes of one step: K' (fp16) and V rows 0 .. pos of every head,
     # the query and the output row, and lse
     alg = B * H * ((pos + 1) * D * 2 * 2 + 2 * D * 2 + 4)
@@ -367,6 +373,7 @@ def bench_decode(args, dev):
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "cache_positions": T, "pos": pos, "D": D},
         "us_per_decode": round(t_dec, 3), "us_per_append_and_decode": round(t_step, 3),
+        "us_per_fused_step": round(t_fused, 3),
         "roofline": {"kernel": "decode (partial + combine)", "bound": "hbm",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,

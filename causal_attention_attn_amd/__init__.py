@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     attn_bwd_prep,
     attn_bwd_workspace_bytes,
     attn_decode,
+    attn_decode_step,
     attn_decode_workspace_bytes,
     attn_fwd,
     attn_fwd_packed,

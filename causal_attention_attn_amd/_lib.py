@@ -45,6 +45,8 @@ _SIGS = {
     "attn_kv_append": (_I, [_P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _I, _P]),
     "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _Z, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _P]),
+    "attn_decode_step": (_I, [_P, _P, _P, _P, _Z, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I,
+                              _I, _P]),
     "attn_rmsnorm_fwd": (_I, [_P, _P, _P, ctypes.c_float, _P, _P, _P, _I, _I, _I, _P]),
     "attn_rmsnorm_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
     "attn_rmsnorm_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _P]),
@@ -189,6 +191,13 @@ def attn_decode(q, cache, cache_bytes, cos_tab, sin_tab, o, lse, workspace, work
     _call("attn_decode", _ptr(q), _ptr(cache), int(cache_bytes), _ptr(cos_tab), _ptr(sin_tab),
           _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes), pos, B, H, Tmax, D, dtype,
           _stream(stream))
+
+
+def attn_decode_step(q, k_new, v_new, cache, cache_bytes, cos_tab, sin_tab, o, lse, workspace,
+                     workspace_bytes, pos, B, H, Tmax, D, dtype, stream=None):
+    _call("attn_decode_step", _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cache), int(cache_bytes),
+          _ptr(cos_tab), _ptr(sin_tab), _ptr(o), _ptr(lse), _ptr(workspace),
+          int(workspace_bytes), pos, B, H, Tmax, D, dtype, _stream(stream))
 
 
 def attn_rmsnorm_fwd(x, res, g, eps, h, y, rstd, N, C, dtype, stream=None):

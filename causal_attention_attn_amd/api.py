@@ -156,3 +156,16 @@ class KVCache:
                          self.ws, self.ws_bytes, pos, self.B, self.H, self.Tmax, self.D,
                          self.code)
         return o, lse
+
+    def step(self, q, k_new, v_new, pos):
+        """One generation step in one launch: append the new token's pre-RoPE key
+        and value ([B, H, D]) at position pos and decode its query there."""
+        for t in (q, k_new, v_new):
+            if tuple(t.shape) != (self.B, self.H, self.D) or t.dtype != self.dtype:
+                raise ValueError("q, k_new and v_new must be [B, H, D] of the cache's dtype")
+        o = torch.empty_like(q)
+        lse = torch.empty((self.B, self.H), dtype=torch.float32, device=q.device)
+        _lib.attn_decode_step(q.contiguous(), k_new.contiguous(), v_new.contiguous(), self.buf,
+                              self.nbytes, self.cs, self.sn, o, lse, self.ws, self.ws_bytes, pos,
+                              self.B, self.H, self.Tmax, self.D, self.code)
+        return o, lse

@@ -402,7 +402,28 @@ int attn_decode(const void* q, const void* cache, size_t cache_bytes, const floa
         return ATTN_ERR_WORKSPACE;
     if (misaligned(workspace)) return ATTN_ERR_ALIGN;
     if (any_alias({o, lse, workspace}, {q, cache, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
-    return hip_status(attn::launch_decode(q, cache, cos_tab, sin_tab, o, lse,
+    return hip_status(attn::launch_decode(q, nullptr, nullptr, cache, cos_tab, sin_tab, o, lse,
+                                          static_cast<float*>(workspace), pos, B, H, Tmax, D,
+                                          dtype == ATTN_F16, static_cast<hipStream_t>(stream)));
+}
+
+int attn_decode_step(const void* q, const void* k_new, const void* v_new, void* cache,
+                     size_t cache_bytes, const float* cos_tab, const float* sin_tab, void* o,
+                     float* lse, void* workspace, size_t workspace_bytes, int pos, int B, int H,
+                     int Tmax, int D, int dtype, void* stream) {
+    int st = check_cache_shape(B, H, Tmax, D, dtype);
+    if (st) return st;
+    if (pos < 0 || pos >= Tmax) return ATTN_ERR_SHAPE;
+    st = check_ptrs({q, k_new, v_new, cache, cos_tab, sin_tab, o, lse});
+    if (st) return st;
+    if (cache_bytes < cache_need(B, H, Tmax, D)) return ATTN_ERR_WORKSPACE;
+    if (workspace == nullptr || workspace_bytes < decode_ws_need(B, H, Tmax, D))
+        return ATTN_ERR_WORKSPACE;
+    if (misaligned(workspace)) return ATTN_ERR_ALIGN;
+    if (any_alias({o, lse, workspace, cache}, {q, k_new, v_new, cos_tab, sin_tab}) ||
+        any_alias({o, lse, workspace}, {cache}))
+        return ATTN_ERR_ALIAS;
+    return hip_status(attn::launch_decode(q, k_new, v_new, cache, cos_tab, sin_tab, o, lse,
                                           static_cast<float*>(workspace), pos, B, H, Tmax, D,
                                           dtype == ATTN_F16, static_cast<hipStream_t>(stream)));
 }

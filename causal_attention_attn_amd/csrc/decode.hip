@@ -36,6 +36,19 @@ constexpr int kSlice = 64;  // keys per wave (one partial result each)
 template <int D>
 constexpr int partial_stride() { return D + 4; }  // o[D], m, l, 2 pad: 16-byte rows
 
+// R_u k for one 16-byte chunk (4 feature pairs) of a key row, rounded once to fp16.
+template <typename E>
+__device__ __forceinline__ u32x4 rotate_key_chunk(u32x4 wk, f32x4 cv, f32x4 sv) {
+    u32x4 rk;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f32x2 kp = unpack2<E>(wk[p]);
+        const float k0 = kp[0], k1 = kp[1];
+        rk[p] = pack2<f16>(k0 * cv[p] - k1 * sv[p], k0 * sv[p] + k1 * cv[p]);
+    }
+    return rk;
+}
+
 // Append n tokens to the cache: K' rows R_u k_u (u = pos0 + i) rounded once to
 // fp16, V rows copied. k and v are [B, H, n, D]. One thread per 8 features.
 template <int D, typename E>
@@ -60,24 +73,22 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const E* __restrict__ k,
     const u32x4 wv = *reinterpret_cast<const u32x4*>(v + src);
     const f32x4 cv = *reinterpret_cast<const f32x4*>(cs + (long long)u * (D / 2) + 4 * c);
     const f32x4 sv = *reinterpret_cast<const f32x4*>(sn + (long long)u * (D / 2) + 4 * c);
-    u32x4 rk;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const f32x2 kp = unpack2<E>(wk[p]);
-        const float k0 = kp[0], k1 = kp[1];
-        rk[p] = pack2<f16>(k0 * cv[p] - k1 * sv[p], k0 * sv[p] + k1 * cv[p]);
-    }
-    *reinterpret_cast<u32x4*>(kc + dst) = rk;
+    *reinterpret_cast<u32x4*>(kc + dst) = rotate_key_chunk<E>(wk, cv, sv);
     *reinterpret_cast<u32x4*>(vc + dst) = wv;
 }
 
 // One wave per (head, 64-key slice). Lane l holds 16-byte chunk l % NC of rows
-// l / NC, l / NC + RPI, ... of the slice, for K' and for V.
-template <int D, typename E>
+// l / NC, l / NC + RPI, ... of the slice, for K' and for V. APPEND: the token at
+// position pos is new (knew, vnew [B, H, D], pre-RoPE k): the cache is read up
+// to pos - 1 only, and the wave whose slice holds pos rotates the new key,
+// uses it and the new value directly, and writes both into cache row pos (no
+// other wave reads that row).
+template <int D, typename E, bool APPEND>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
-    const E* __restrict__ q, const f16* __restrict__ kc, const E* __restrict__ vc,
+    const E* __restrict__ q, f16* __restrict__ kc, E* __restrict__ vc,
     const float* __restrict__ cs, const float* __restrict__ sn, float* __restrict__ part,
-    int Tmax, int pos, int nsplit, int nwaves, float qs) {
+    const E* __restrict__ knew, const E* __restrict__ vnew, int Tmax, int pos, int nsplit,
+    int nwaves, float qs) {
     constexpr int NC = D / 8;          // 16-byte chunks per row
     constexpr int RPI = 64 / NC;       // rows per load instruction
     constexpr int NI = kSlice / RPI;   // load instructions per operand
@@ -88,8 +99,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int bh = gw / nsplit, u0 = (gw % nsplit) * kSlice;
     const int cc = lane % NC, rl = lane / NC;
 
-    // cache rows 0 .. pos of this head; rows past pos read as zeros
-    const uint32_t bytes = (uint32_t)(pos + 1) * D * 2;
+    // cache rows 0 .. pos of this head (0 .. pos - 1 when appending); rows past
+    // them read as zeros
+    const uint32_t bytes = (uint32_t)(APPEND ? pos : pos + 1) * D * 2;
     const rsrc_t kb = make_rsrc(kc + (size_t)bh * Tmax * D, bytes);
     const rsrc_t vb = make_rsrc(vc + (size_t)bh * Tmax * D, bytes);
     u32x4 kr[NI], vr[NI];
@@ -110,6 +122,26 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         const f32x2 x = unpack2<E>(wq[p]);
         qh[p] = __builtin_bit_cast(f16x2, pack2<f16>((x[0] * c4[p] - x[1] * s4[p]) * qs,
                                                      (x[0] * s4[p] + x[1] * c4[p]) * qs));
+    }
+    if constexpr (APPEND) {
+        if (pos - u0 < kSlice) {  // uniform: this wave's slice holds the new row
+            const int r = pos - u0;
+            if (rl == r % RPI) {
+                const size_t cell = ((size_t)bh * Tmax + pos) * D + 8 * cc;
+                const u32x4 kn = rotate_key_chunk<E>(
+                    *reinterpret_cast<const u32x4*>(knew + (size_t)bh * D + 8 * cc), c4, s4);
+                const u32x4 vn = *reinterpret_cast<const u32x4*>(vnew + (size_t)bh * D + 8 * cc);
+                *reinterpret_cast<u32x4*>(kc + cell) = kn;
+                *reinterpret_cast<u32x4*>(vc + cell) = vn;
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    if (i == r / RPI) {
+                        kr[i] = kn;
+                        vr[i] = vn;
+                    }
+                }
+            }
+        }
     }
 
     // scores in log2 units; the NC lanes of a row add their chunks' dot products
@@ -212,9 +244,12 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     template __global__ void kv_append_kernel<D_, E_>(const E_*, const E_*, const float*,      \
                                                       const float*, f16*, E_*, int, int, int,  \
                                                       long long);                              \
-    template __global__ void decode_partial_kernel<D_, E_>(const E_*, const f16*, const E_*,   \
-                                                           const float*, const float*, float*, \
-                                                           int, int, int, int, float);         \
+    template __global__ void decode_partial_kernel<D_, E_, false>(                            \
+        const E_*, f16*, E_*, const float*, const float*, float*, const E_*, const E_*, int, int, \
+        int, int, float);                                                                      \
+    template __global__ void decode_partial_kernel<D_, E_, true>(                             \
+        const E_*, f16*, E_*, const float*, const float*, float*, const E_*, const E_*, int, int, \
+        int, int, float);                                                                      \
     template __global__ void decode_combine_kernel<D_, E_>(const float*, E_*, float*, int);
 ATTN_DEC_INST(64, bf16) ATTN_DEC_INST(128, bf16) ATTN_DEC_INST(64, f16) ATTN_DEC_INST(128, f16)
 #undef ATTN_DEC_INST
@@ -250,18 +285,25 @@ hipError_t launch_kv_append(const void* k, const void* v, const float* cs, const
 }
 
 template <int D, typename E>
-static hipError_t launch_decode_t(const void* q, const void* cache, const float* cs,
-                                  const float* sn, void* o, float* lse, float* ws, int pos,
-                                  int B, int H, int Tmax, hipStream_t st) {
+static hipError_t launch_decode_t(const void* q, const void* knew, const void* vnew,
+                                  const void* cache, const float* cs, const float* sn, void* o,
+                                  float* lse, float* ws, int pos, int B, int H, int Tmax,
+                                  hipStream_t st) {
     const int nsplit = decode_slices(pos);
     const int nwaves = B * H * nsplit;
     const size_t kbytes = (size_t)B * H * Tmax * D * 2;
-    const f16* kc = static_cast<const f16*>(cache);
-    const E* vc = reinterpret_cast<const E*>(static_cast<const char*>(cache) + kbytes);
+    f16* kc = static_cast<f16*>(const_cast<void*>(cache));
+    E* vc = reinterpret_cast<E*>(static_cast<char*>(const_cast<void*>(cache)) + kbytes);
     const float qs = kLog2e / sqrtf((float)D);
-    hipLaunchKernelGGL((decode_partial_kernel<D, E>), dim3((unsigned)((nwaves + 3) / 4)),
-                       dim3(256), 0, st, (const E*)q, kc, vc, cs, sn, ws, Tmax, pos, nsplit,
-                       nwaves, qs);
+    const dim3 grid((unsigned)((nwaves + 3) / 4)), block(256);
+    if (knew != nullptr)
+        hipLaunchKernelGGL((decode_partial_kernel<D, E, true>), grid, block, 0, st, (const E*)q,
+                           kc, vc, cs, sn, ws, (const E*)knew, (const E*)vnew, Tmax, pos, nsplit,
+                           nwaves, qs);
+    else
+        hipLaunchKernelGGL((decode_partial_kernel<D, E, false>), grid, block, 0, st, (const E*)q,
+                           kc, vc, cs, sn, ws, (const E*)nullptr, (const E*)nullptr, Tmax, pos,
+                           nsplit, nwaves, qs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D, E>), dim3((unsigned)(B * H)), dim3(D), 0, st,
@@ -269,14 +311,18 @@ static hipError_t launch_decode_t(const void* q, const void* cache, const float*
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const void* q, const void* cache, const float* cs, const float* sn,
-                         void* o, float* lse, float* ws, int pos, int B, int H, int Tmax, int D,
-                         bool f16_storage, hipStream_t st) {
+hipError_t launch_decode(const void* q, const void* knew, const void* vnew, const void* cache,
+                         const float* cs, const float* sn, void* o, float* lse, float* ws, int pos,
+                         int B, int H, int Tmax, int D, bool f16_storage, hipStream_t st) {
     if (f16_storage)
-        return D == 64 ? launch_decode_t<64, f16>(q, cache, cs, sn, o, lse, ws, pos, B, H, Tmax, st)
-                       : launch_decode_t<128, f16>(q, cache, cs, sn, o, lse, ws, pos, B, H, Tmax, st);
-    return D == 64 ? launch_decode_t<64, bf16>(q, cache, cs, sn, o, lse, ws, pos, B, H, Tmax, st)
-                   : launch_decode_t<128, bf16>(q, cache, cs, sn, o, lse, ws, pos, B, H, Tmax, st);
+        return D == 64 ? launch_decode_t<64, f16>(q, knew, vnew, cache, cs, sn, o, lse, ws, pos,
+                                                  B, H, Tmax, st)
+                       : launch_decode_t<128, f16>(q, knew, vnew, cache, cs, sn, o, lse, ws, pos,
+                                                   B, H, Tmax, st);
+    return D == 64 ? launch_decode_t<64, bf16>(q, knew, vnew, cache, cs, sn, o, lse, ws, pos, B,
+                                               H, Tmax, st)
+                   : launch_decode_t<128, bf16>(q, knew, vnew, cache, cs, sn, o, lse, ws, pos, B,
+                                                H, Tmax, st);
 }
 
 }  // namespace attn

@@ -75,9 +75,11 @@ size_t decode_workspace_floats(int B, int H, int Tmax, int D);     // partials f
 hipError_t launch_kv_append(const void* k, const void* v, const float* cs, const float* sn,
                             void* cache, int pos0, int n, int B, int H, int Tmax, int D,
                             bool f16_storage, hipStream_t s);
-hipError_t launch_decode(const void* q, const void* cache, const float* cs, const float* sn,
-                         void* o, float* lse, float* ws, int pos, int B, int H, int Tmax, int D,
-                         bool f16_storage, hipStream_t s);
+// knew, vnew: the new token's pre-RoPE key and value [B, H, D], written into cache
+// row pos by the same launch; both null: row pos is already in the cache.
+hipError_t launch_decode(const void* q, const void* knew, const void* vnew, const void* cache,
+                         const float* cs, const float* sn, void* o, float* lse, float* ws, int pos,
+                         int B, int H, int Tmax, int D, bool f16_storage, hipStream_t s);
 
 // The per-layer kernels next to attention (16-bit path): residual add +
 // RMSNorm and SwiGLU.

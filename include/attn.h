@@ -359,6 +359,18 @@ int attn_swiglu_fwd(const void* u, void* out, int N, int F, int dtype, void* str
 int attn_swiglu_bwd(const void* u, const void* dout, void* du, int N, int F, int dtype,
                     void* stream);
 
+/*
+ * attn_decode_step - a whole generation step in one launch: attn_kv_append of
+ * the new token at position pos (k_new, v_new [B, H, D] dtype, pre-RoPE k),
+ * then attn_decode at pos, with the same results. The new key and value are
+ * used directly by the step and written into cache row pos. Arguments and
+ * rules as attn_decode, plus k_new and v_new; the cache is an output here.
+ */
+int attn_decode_step(const void* q, const void* k_new, const void* v_new, void* cache,
+                     size_t cache_bytes, const float* cos_tab, const float* sin_tab,
+                     void* o, float* lse, void* workspace, size_t workspace_bytes, int pos,
+                     int B, int H, int Tmax, int D, int dtype, void* stream);
+
 /* attn_status_string - static, human-readable name of a status code. */
 const char* attn_status_string(int status);
 

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
     for n in ("attn_fwd", "attn_fwd_rotated", "attn_rotate_qk", "attn_saved_bytes", "attn_bwd",
               "attn_bwd_prep", "attn_bwd_grads", "attn_rope_tables", "attn_bwd_workspace_bytes",
               "attn_fwd_packed", "attn_bwd_packed", "attn_kv_cache_bytes", "attn_kv_append",
-              "attn_decode_workspace_bytes", "attn_decode", "attn_rmsnorm_fwd",
+              "attn_decode_workspace_bytes", "attn_decode", "attn_decode_step", "attn_rmsnorm_fwd",
               "attn_rmsnorm_bwd_workspace_bytes", "attn_rmsnorm_bwd", "attn_swiglu_fwd",
               "attn_swiglu_bwd", "attn_status_string", "attn_last_hip_error"):
         assert n in names
@@ -240,6 +240,18 @@ def test_decode_entry_points_reject_bad_arguments(lib):
     assert g(workspace=MIS) == 4
     assert g(o=FAKE) == 7                                 # o aliases q
     assert g(workspace=FAKE + 16) == 7                    # workspace aliases the cache
+    sb = dict(q=FAKE, k_new=FAKE + 112, v_new=FAKE + 128, cache=FAKE + 16, cache_bytes=cb,
+              cos_tab=FAKE + 32, sin_tab=FAKE + 48, o=FAKE + 64, lse=FAKE + 80,
+              workspace=FAKE + 96, workspace_bytes=512, pos=3, B=1, H=1, Tmax=8, D=64, dtype=0,
+              stream=0)
+    h = lambda **o: status_of(lambda: attn.attn_decode_step(**{**sb, **o}))
+    assert h(k_new=0) == 1
+    assert h(pos=8) == 2
+    assert h(dtype=1) == 3
+    assert h(v_new=MIS) == 4
+    assert h(workspace_bytes=16) == 5
+    assert h(cache=FAKE + 112) == 7                       # the cache aliases k_new
+    assert h(o=FAKE + 16) == 7                            # o aliases the cache
 
 
 def test_layer_entry_points_reject_bad_arguments(lib):

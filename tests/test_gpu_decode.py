@@ -165,3 +165,26 @@ def test_steps_at_different_positions_share_a_workspace():
         else:
             first[pos] = (o.clone(), lse.clone())
             check(o.cpu(), lse.cpu(), q, k, v, pos, "bf16", f"shared workspace pos {pos}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fused_step_equals_append_then_decode(D, dtype):
+    """attn_decode_step (append + decode in one launch) gives bitwise the outputs
+    and cache contents of attn_kv_append followed by attn_decode, token by token,
+    across slice boundaries, and matches the oracle."""
+    B, H, T = 2, 3, 140
+    q, k, v = inputs(B, H, T, D, dtype, seed=51 + D)
+    a = attn.KVCache(B, H, T, D, DT[dtype], DEV)
+    b = attn.KVCache(B, H, T, D, DT[dtype], DEV)
+    for t in range(T):
+        qt, kt, vt = (x[:, :, t].contiguous().to(DEV) for x in (q, k, v))
+        a.append(kt[:, :, None], vt[:, :, None], t)
+        oa, la = a.decode(qt, t)
+        ob, lb = b.step(qt, kt, vt, t)
+        if t in (0, 1, 63, 64, 65, 127, 128, 139):
+            torch.cuda.synchronize()
+            assert torch.equal(oa, ob) and torch.equal(la, lb), t
+            check(ob.cpu(), lb.cpu(), q, k, v, t, dtype, f"fused step {dtype} D{D} pos {t}")
+    torch.cuda.synchronize()
+    assert torch.equal(a.buf, b.buf)
