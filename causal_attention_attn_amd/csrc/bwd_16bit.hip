@@ -73,6 +73,48 @@ struct RowTables {
     }
 };
 
+// Epilogue stores through LDS. A wave's 32 output rows (2D bytes each) are put
+// into a 32 x 2D-byte LDS buffer in the accumulator layout (lane (c, h) owns
+// features 32b + 8g + 4h .. +3 of row c: 8 bytes), with the 16-byte chunks of
+// row r rotated by XOR with r & 7 so that the rows of a put spread over the
+// banks; then each 16-byte store of the wave covers 64 x 16 / 2D whole rows
+// (contiguous in a plain head) instead of 16 bytes of 32 rows.
+template <int D>
+struct RowStage {
+    static constexpr int NCH = D / 8;     // 16-byte chunks per row
+    static constexpr int RPI = 64 / NCH;  // rows per store instruction
+    char* buf;
+    __device__ __forceinline__ void put(int c32, int hf, int b, int g, u32x2 w) const {
+        const int ch = 4 * b + g;
+        *reinterpret_cast<u32x2*>(buf + c32 * (2 * D) + 16 * (ch ^ (c32 & 7)) + 8 * hf) = w;
+    }
+    // rows row0 .. row0+31 (those below T) of a head whose rows are `pitch`
+    // elements apart
+    template <typename E>
+    __device__ __forceinline__ void store(E* head, int row0, int T, int pitch, int lane) const {
+        const int c = lane % NCH;
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+            const int r = it * RPI + lane / NCH;
+            const u32x4 w =
+                *reinterpret_cast<const u32x4*>(buf + r * (2 * D) + 16 * (c ^ (r & 7)));
+            if (row0 + r < T)
+                *reinterpret_cast<u32x4*>(row_ptr(head, row0 + r, pitch) + 8 * c) = w;
+        }
+    }
+};
+
+// This wave's staging buffer once the ring is idle: one of the ring's stage
+// buffers (64 x 2D bytes each: room for two outputs of 32 rows).
+template <int D>
+__device__ __forceinline__ char* stage_buffer(const Ring& rg, int wave) {
+    constexpr int NS = BwdTile<D>::NS;
+    if (wave == 0) return rg.k[0];
+    if (wave == 1) return rg.k[1];
+    if constexpr (NS > 2) return wave == 2 ? rg.k[2] : rg.v[0];
+    else return wave == 2 ? rg.v[0] : rg.v[1];
+}
+
 // One 64-key tile of the dq kernel for one wave (32 queries). DIAG: the tile may
 // reach this wave's diagonal (32-key blocks above it skipped, the diagonal one masked).
 template <int D, typename E, bool DIAG>
@@ -251,25 +293,24 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
     }
     wait_vmcnt<0>();
 
-    if (tq < T) {
-        E* out = STRIDED ? row_ptr(dq + vhead, tq, vst) : dq + hoff + (size_t)tq * D;
+    __syncthreads();  // the ring is idle: its stage buffers hold the output rows
+    const RowStage<D> sg = {stage_buffer<D>(rg, wave)};
 #pragma unroll
-        for (int b = 0; b < C::DB; ++b) {
+    for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = 32 * b + 8 * g + 4 * hf;
-                const f32x2 c2 = tb.c[b][g], s2 = tb.s[b][g];
-                u32x2 w;
+        for (int g = 0; g < 4; ++g) {
+            const f32x2 c2 = tb.c[b][g], s2 = tb.s[b][g];
+            u32x2 w;
 #pragma unroll
-                for (int pr = 0; pr < 2; ++pr) {
-                    const float x0 = acc[b][4 * g + 2 * pr] * scale;
-                    const float x1 = acc[b][4 * g + 2 * pr + 1] * scale;
-                    w[pr] = pack2<E>(x0 * c2[pr] + x1 * s2[pr], x1 * c2[pr] - x0 * s2[pr]);
-                }
-                *reinterpret_cast<u32x2*>(out + d) = w;
+            for (int pr = 0; pr < 2; ++pr) {
+                const float x0 = acc[b][4 * g + 2 * pr] * scale;
+                const float x1 = acc[b][4 * g + 2 * pr + 1] * scale;
+                w[pr] = pack2<E>(x0 * c2[pr] + x1 * s2[pr], x1 * c2[pr] - x0 * s2[pr]);
             }
+            sg.put(c32, hf, b, g, w);
         }
     }
+    sg.store(dq + vhead, wq0, T, vst, lane);
 }
 
 // One 64-query tile of the dk/dv kernel for one wave (32 keys). DIAG: the tile
@@ -470,28 +511,28 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
     }
     wait_vmcnt<0>();
 
-    if (tk < T) {
-        E* ko = STRIDED ? row_ptr(dk + vhead, tk, vst) : dk + hoff + (size_t)tk * D;
-        E* vo = STRIDED ? row_ptr(dv + vhead, tk, vst) : dv + hoff + (size_t)tk * D;
+    __syncthreads();  // the ring is idle: its stage buffers hold the output rows
+    const RowStage<D> sk = {stage_buffer<D>(rg, wave)};
+    const RowStage<D> sv = {sk.buf + 32 * 2 * D};
 #pragma unroll
-        for (int b = 0; b < C::DB; ++b) {
+    for (int b = 0; b < C::DB; ++b) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = 32 * b + 8 * g + 4 * hf;
-                const f32x2 c2 = tb.c[b][g], s2 = tb.s[b][g];
-                u32x2 wk, wv;
+        for (int g = 0; g < 4; ++g) {
+            const f32x2 c2 = tb.c[b][g], s2 = tb.s[b][g];
+            u32x2 wk, wv;
 #pragma unroll
-                for (int pr = 0; pr < 2; ++pr) {
-                    const float x0 = dka[b][4 * g + 2 * pr] * scale;
-                    const float x1 = dka[b][4 * g + 2 * pr + 1] * scale;
-                    wk[pr] = pack2<E>(x0 * c2[pr] + x1 * s2[pr], x1 * c2[pr] - x0 * s2[pr]);
-                    wv[pr] = pack2<E>(dva[b][4 * g + 2 * pr], dva[b][4 * g + 2 * pr + 1]);
-                }
-                *reinterpret_cast<u32x2*>(ko + d) = wk;
-                *reinterpret_cast<u32x2*>(vo + d) = wv;
+            for (int pr = 0; pr < 2; ++pr) {
+                const float x0 = dka[b][4 * g + 2 * pr] * scale;
+                const float x1 = dka[b][4 * g + 2 * pr + 1] * scale;
+                wk[pr] = pack2<E>(x0 * c2[pr] + x1 * s2[pr], x1 * c2[pr] - x0 * s2[pr]);
+                wv[pr] = pack2<E>(dva[b][4 * g + 2 * pr], dva[b][4 * g + 2 * pr + 1]);
             }
+            sk.put(c32, hf, b, g, wk);
+            sv.put(c32, hf, b, g, wv);
         }
     }
+    sk.store(dk + vhead, wk0, T, vst, lane);
+    sv.store(dv + vhead, wk0, T, vst, lane);
 }
 
 // The gradient kernel: one launch runs both kinds of item, so the light items
