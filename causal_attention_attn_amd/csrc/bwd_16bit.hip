@@ -539,11 +539,14 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
 // of one kind fill the gaps left by the other and there is a single tail.
 // Item classes alternate dk/dv key block r and dq q-block nqb-1-r
 // (r = 0, 1, ...), which is heaviest first up to the 4:3 ratio of their
-// products per tile; each class holds one item per head.
+// products per tile; each class holds one item per head. Workgroup i runs item
+// i: the grid is several times the resident slots, and once the first ones are
+// placed the dispatcher hands the next workgroup id to whichever slot frees
+// first, so ids in falling order of work are longest-first list scheduling
+// (the forward's round reversal would start light items before heavy ones).
 template <int D, typename E, bool STRIDED>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd16_kernel(BwdPtrs<E> pp, int nqb,
-                                                                         int nkb, int kinds,
-                                                                         int ncu) {
+                                                                         int nkb, int kinds) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int T3 = NS > 2 ? C::TILE : 1024;
@@ -555,8 +558,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd16_kernel(BwdPtrs<E> 
 
     // kinds: 1 = dq items only, 2 = dk/dv items only, 3 = both
     const int per = kinds == 3 ? 2 : 1;
-    const int nclass = per * max(nqb, nkb);
-    const int item = snake_item(blockIdx.x, ncu, nclass * pp.BH);
+    const int item = blockIdx.x;
     const int c = item / pp.BH, bh = item % pp.BH;
     const int r = c / per;
     const bool is_dkdv = kinds == 2 || (kinds == 3 && (c % 2) == 0);
@@ -582,10 +584,10 @@ static hipError_t launch_grads(const BwdArgs& a, int kinds) {
     // row pitch D for both means plain [B, H, T, D] (see Layout)
     if (a.lqkv.st != a.D || a.lo.st != a.D)
         hipLaunchKernelGGL((bwd16_kernel<D, E, true>), dim3(items), dim3(C::NT), 0, a.stream, pp,
-                           nqb, nkb, kinds, device_cu_count());
+                           nqb, nkb, kinds);
     else
         hipLaunchKernelGGL((bwd16_kernel<D, E, false>), dim3(items), dim3(C::NT), 0, a.stream, pp,
-                           nqb, nkb, kinds, device_cu_count());
+                           nqb, nkb, kinds);
     return hipGetLastError();
 }
 
