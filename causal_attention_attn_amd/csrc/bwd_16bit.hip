@@ -55,8 +55,10 @@ struct BwdTile {
 
 // The RoPE table entries this lane's epilogue needs to rotate its row t back:
 // features d = 32b + 8g + 4h .. +3 (h = lane >> 5), i.e. the cos/sin pairs
-// d/2, d/2 + 1. Loaded when an item starts, so their latency hides behind the
-// item's tile loop. Rows past the end read row 0 (their results are not stored).
+// d/2, d/2 + 1. Loaded once the item's tile loop is done, so that the loop
+// runs without these 32 registers (held through the loop they pushed the
+// kernel to its register limit and into spills). Rows past the end read row 0
+// (their results are not stored).
 template <int D>
 struct RowTables {
     f32x2 c[D / 32][4], s[D / 32][4];
@@ -247,8 +249,6 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
     const int kend = min(T, q0 + C::QM);
     const int ntiles = (kend + C::KN - 1) / C::KN;
     const int nfull = min(ntiles, q0 / C::KN);
-    RowTables<D> tb;
-    tb.load(cs, sn, tq, T, hf);
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) {
         if (s < ntiles) {
@@ -291,6 +291,8 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
         else if constexpr (NS > 2)
             dq_step<D, E, 2, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
     }
+    RowTables<D> tb;
+    tb.load(cs, sn, tq, T, hf);
     wait_vmcnt<0>();
 
     __syncthreads();  // the ring is idle: its stage buffers hold the output rows
@@ -464,8 +466,6 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
     const int qt0 = k0 / C::QN;
     const int nqt = (T + C::QN - 1) / C::QN;
     const int qfull = min(nqt, (k0 + C::KM) / C::QN);  // from here on no query precedes a key
-    RowTables<D> tb;
-    tb.load(cs, sn, tk, T, hf);
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
         if (qt0 + s < nqt) x.issue(ld, qt0 + s, rg.k[s], rg.v[s], rg.x[s]);
@@ -509,6 +509,8 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
         else if (stg == 1) dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
         else if constexpr (NS > 2) dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
+    RowTables<D> tb;
+    tb.load(cs, sn, tk, T, hf);
     wait_vmcnt<0>();
 
     __syncthreads();  // the ring is idle: its stage buffers hold the output rows

@@ -215,6 +215,7 @@ struct FwdCtx {
     const E* v;
     int vst;  // elements between consecutive rows of v
     int T, wq0, lane, wave;
+    int ntiles;  // key tiles of the block (no tile past the last one is loaded)
 };
 
 // Step n of the tile loop; tile n sits in ring stage STG = n % NS and its K
@@ -238,9 +239,13 @@ __device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, KOps<
     wait_vmcnt<C::LPT * (NS - 3)>();
     ring_barrier();
     const int nx = n + NS - 1;
-    ld.issue(x.kr, x.T, nx * C::BN, rg.k[FREE], x.wave);
-    if constexpr (STRIDED) ld.issue_strided(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave, x.vst);
-    else ld.issue(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave);
+    // full steps load unchecked: their tile nx lies past the block's last one
+    // only for a ragged T, and is then read within the head or as zeros
+    if (!DIAG || nx < x.ntiles) {
+        ld.issue(x.kr, x.T, nx * C::BN, rg.k[FREE], x.wave);
+        if constexpr (STRIDED) ld.issue_strided(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave, x.vst);
+        else ld.issue(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave);
+    }
     if (live) fwd_softmax_pv<D, E, DIAG>(st, s, rg.v[STG], of, k0, x.wq0, n == 0);
     read_k(kr, rg.k[NXT], of);
 }
@@ -271,19 +276,19 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
     const size_t hoff = (size_t)bh * T * D;
     const int wq0 = q0 + wave * 32;
     const int tq = wq0 + c32;
-    // v and o: [B, H, T, D] unless STRIDED (then where their layouts put them)
-    const FwdCtx<D, E> x = {kr + hoff, v + (STRIDED ? lv.head(bh, H) : (long long)hoff),
-                            STRIDED ? lv.st : D, T, wq0, lane, wave};
-    const TileLoads<D, 64, 4> ld(wave, lane);
-    const OperandOffs<D> of(lane);
-
     const int kend = min(T, q0 + C::BM);
     const int ntiles = (kend + C::BN - 1) / C::BN;
     const int nfull = min(ntiles, q0 / C::BN);  // tiles wholly below every query of the block
+    // v and o: [B, H, T, D] unless STRIDED (then where their layouts put them)
+    const FwdCtx<D, E> x = {kr + hoff, v + (STRIDED ? lv.head(bh, H) : (long long)hoff),
+                            STRIDED ? lv.st : D, T, wq0, lane, wave, ntiles};
+    const TileLoads<D, 64, 4> ld(wave, lane);
+    const OperandOffs<D> of(lane);
 
-    // prologue: tiles 0 .. NS-2 in flight (tiles past the end read as zeros)
+    // prologue: tiles 0 .. NS-2 in flight (rows past T read as zeros)
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) {
+        if (s >= ntiles) break;
         ld.issue(x.kr, T, s * C::BN, rg.k[s], wave);
         if constexpr (STRIDED) ld.issue_strided(x.v, T, s * C::BN, rg.v[s], wave, x.vst);
         else ld.issue(x.v, T, s * C::BN, rg.v[s], wave);
