@@ -249,16 +249,11 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
     const int kend = min(T, q0 + C::QM);
     const int ntiles = (kend + C::KN - 1) / C::KN;
     const int nfull = min(ntiles, q0 / C::KN);
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s) {
-        if (s < ntiles) {
-            ld.issue(kh, T, s * C::KN, rg.k[s], wave);
-            if constexpr (STRIDED) ld.issue_strided(vh, T, s * C::KN, rg.v[s], wave, vst);
-            else ld.issue(vh, T, s * C::KN, rg.v[s], wave);
-        }
-    }
-
-    // this lane's query: rotated q (fp16), dO (E) and its two row offsets
+    // tile 0, then this lane's query: rotated q (fp16), dO (E) and its two row
+    // offsets, then tiles 1 .. NS-2; the first step waits for tile 0 and the query only
+    ld.issue(kh, T, 0, rg.k[0], wave);
+    if constexpr (STRIDED) ld.issue_strided(vh, T, 0, rg.v[0], wave, vst);
+    else ld.issue(vh, T, 0, rg.v[0], wave);
     f16x8 qf[C::DK];
     vec8<E> df[C::DK];
 #pragma unroll
@@ -269,6 +264,14 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
     }
     const float nlt = tq < T ? ws[(size_t)bh * T + tq] : 0.f;
     const float ndl = tq < T ? ws[(size_t)BH * T + (size_t)bh * T + tq] : 0.f;
+#pragma unroll
+    for (int s = 1; s < NS - 1; ++s) {
+        if (s < ntiles) {
+            ld.issue(kh, T, s * C::KN, rg.k[s], wave);
+            if constexpr (STRIDED) ld.issue_strided(vh, T, s * C::KN, rg.v[s], wave, vst);
+            else ld.issue(vh, T, s * C::KN, rg.v[s], wave);
+        }
+    }
     const f32x16 nl = splat16(nlt), nd = splat16(ndl);
 
     f32x16 acc[C::DB];
@@ -466,10 +469,9 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
     const int qt0 = k0 / C::QN;
     const int nqt = (T + C::QN - 1) / C::QN;
     const int qfull = min(nqt, (k0 + C::KM) / C::QN);  // from here on no query precedes a key
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (qt0 + s < nqt) x.issue(ld, qt0 + s, rg.k[s], rg.v[s], rg.x[s]);
-
+    // tile qt0, this lane's key and value, then tiles qt0+1 .. qt0+NS-2; the
+    // first step waits for tile qt0 and the key and value only
+    x.issue(ld, qt0, rg.k[0], rg.v[0], rg.x[0]);
     const rsrc_t kbuf = make_rsrc(kr + hoff, hbytes);
     const rsrc_t vbuf = make_rsrc(v + vhead, STRIDED ? pp.lv.head_bytes(T, D) : hbytes);
     f16x8 kf[C::DK];
@@ -480,6 +482,9 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
         kf[c] = __builtin_bit_cast(f16x8, buf_load16(kbuf, (uint32_t)tk * D * 2 + col));
         vf[c] = as_vec8<vec8<E>>(buf_load16(vbuf, (uint32_t)tk * vst * 2 + col));
     }
+#pragma unroll
+    for (int s = 1; s < NS - 1; ++s)
+        if (qt0 + s < nqt) x.issue(ld, qt0 + s, rg.k[s], rg.v[s], rg.x[s]);
     f32x16 dva[C::DB], dka[C::DB];
 #pragma unroll
     for (int b = 0; b < C::DB; ++b) dva[b] = dka[b] = f32x16{};

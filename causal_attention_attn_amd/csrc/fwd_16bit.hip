@@ -285,20 +285,25 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
     const TileLoads<D, 64, 4> ld(wave, lane);
     const OperandOffs<D> of(lane);
 
-    // prologue: tiles 0 .. NS-2 in flight (rows past T read as zeros)
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s) {
-        if (s >= ntiles) break;
-        ld.issue(x.kr, T, s * C::BN, rg.k[s], wave);
-        if constexpr (STRIDED) ld.issue_strided(x.v, T, s * C::BN, rg.v[s], wave, x.vst);
-        else ld.issue(x.v, T, s * C::BN, rg.v[s], wave);
-    }
+    // prologue: tile 0, this lane's query, then tiles 1 .. NS-2 (rows past T read
+    // as zeros); the first step waits for tile 0 and the query only
+    ld.issue(x.kr, T, 0, rg.k[0], wave);
+    if constexpr (STRIDED) ld.issue_strided(x.v, T, 0, rg.v[0], wave, x.vst);
+    else ld.issue(x.v, T, 0, rg.v[0], wave);
 
     const rsrc_t qh = make_rsrc(qr + hoff, (uint32_t)T * D * 2);
     f16x8 qf[C::DK];
 #pragma unroll
     for (int c = 0; c < C::DK; ++c)
         qf[c] = __builtin_bit_cast(f16x8, buf_load16(qh, (uint32_t)(tq * D + 16 * c + 8 * hf) * 2));
+
+#pragma unroll
+    for (int s = 1; s < NS - 1; ++s) {
+        if (s >= ntiles) break;
+        ld.issue(x.kr, T, s * C::BN, rg.k[s], wave);
+        if constexpr (STRIDED) ld.issue_strided(x.v, T, s * C::BN, rg.v[s], wave, x.vst);
+        else ld.issue(x.v, T, s * C::BN, rg.v[s], wave);
+    }
 
     FwdState<D> st;
 #pragma unroll
