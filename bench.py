@@ -377,7 +377,7 @@ def bench_decode(args, dev):
         "config": {"workload": w.name, "B": B, "H": H, "cache_positions": T, "pos": pos, "D": D},
         "us_per_decode": round(t_dec, 3), "us_per_append_and_decode": round(t_step, 3),
         "us_per_fused_step": round(t_fused, 3),
-        "roofline": {"kernel": "decode (partial + combine)", "bound": "hbm",
+        "roofline": {"kernel": "decode step (one workgroup per head from 64 heads, else partial + combine)", "bound": "hbm",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                      "bytes_per_launch": alg},

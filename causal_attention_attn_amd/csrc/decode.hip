@@ -15,15 +15,18 @@
 // A step reads (pos + 1) K' and V rows per head and does O(D) arithmetic per
 // row: it is bound by memory, not by MFMA (one query row is no contraction
 // worth a matrix core). The keys of a head are split into 64-key slices, one
-// slice per wave, so that even a handful of heads fills the chip:
-//   partial kernel  a wave loads its slice's K' and V rows with coalesced
-//                   16-byte loads (a row's 16-byte chunks on consecutive lanes),
-//                   forms the scores with fp16 dot products against the
-//                   rotated, log2(e)/sqrt(D)-scaled query, and keeps
-//                   (max m, sum l, unnormalised o) of its slice;
-//   combine kernel  per head, merges the slices: M = max m_i,
-//                   o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, and
-//                   lse = (M + log2 L) ln 2.
+// slice per wave: a wave loads its slice's K' and V rows with coalesced 16-byte
+// loads (a row's 16-byte chunks on consecutive lanes), forms the scores with
+// fp16 dot products against the rotated, log2(e)/sqrt(D)-scaled query, and keeps
+// (max m, sum l, unnormalised o) of its slice. The slices of a head are then
+// merged: M = max m_i, o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i and
+// lse = (M + log2 L) ln 2. Two launch shapes:
+//   with many heads (kHeadKernelMinHeads or more), one workgroup per head
+//                   (decode_head_kernel): its waves take the head's slices
+//                   and merge them through LDS, all in one launch;
+//   with few heads, waves of all heads spread over the chip (partial kernel,
+//                   partials to the workspace) and a combine kernel merges
+//                   each head's slices.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -32,6 +35,12 @@ namespace attn {
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kSlice = 64;  // keys per wave (one partial result each)
+// heads from which one workgroup per head (decode_head_kernel) is used
+constexpr int kHeadKernelMinHeads = 64;
+// waves per workgroup of decode_head_kernel at most (its registers: 16 waves of
+// D = 64 or 8 of D = 128 fit a CU without spills)
+template <int D>
+constexpr int kHeadWaves() { return D == 64 ? 16 : 8; }
 
 template <int D>
 constexpr int partial_stride() { return D + 4; }  // o[D], m, l, 2 pad: 16-byte rows
@@ -238,6 +247,142 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     if (d == 0) lse[bh] = (M + log2f(L)) * kLn2;
 }
 
+// One workgroup per head, one wave per 64-key slice (a wave takes slices w,
+// w + W, ... when a head has more than W = blockDim / 64 of them): every wave
+// keeps the running (max, sum, unnormalised o) of its slices, rescaling them when
+// its maximum grows, and the waves' results are merged through LDS by the same
+// workgroup - the whole step in one launch, without the partials' round trip
+// through memory. Used when there are enough heads to spread over the CUs.
+template <int D, typename E, bool APPEND>
+__global__ __launch_bounds__(64 * kHeadWaves<D>()) void decode_head_kernel(
+    const E* __restrict__ q, f16* __restrict__ kc, E* __restrict__ vc,
+    const float* __restrict__ cs, const float* __restrict__ sn, E* __restrict__ o,
+    float* __restrict__ lse, const E* __restrict__ knew, const E* __restrict__ vnew, int Tmax,
+    int pos, int nsplit, float qs) {
+    constexpr int NC = D / 8;          // 16-byte chunks per row
+    constexpr int RPI = 64 / NC;       // rows per load instruction
+    constexpr int NI = kSlice / RPI;   // load instructions per operand
+    constexpr int PS = partial_stride<D>();
+    __shared__ float sp[kHeadWaves<D>() * PS];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int bh = blockIdx.x;
+    const int cc = lane % NC, rl = lane / NC;
+    const uint32_t bytes = (uint32_t)(APPEND ? pos : pos + 1) * D * 2;
+    const rsrc_t kb = make_rsrc(kc + (size_t)bh * Tmax * D, bytes);
+    const rsrc_t vb = make_rsrc(vc + (size_t)bh * Tmax * D, bytes);
+
+    // this lane's chunk of the query: R_pos q scaled by log2(e)/sqrt(D), fp16
+    const u32x4 wq = *reinterpret_cast<const u32x4*>(q + (size_t)bh * D + 8 * cc);
+    const f32x4 c4 = *reinterpret_cast<const f32x4*>(cs + (size_t)pos * (D / 2) + 4 * cc);
+    const f32x4 s4 = *reinterpret_cast<const f32x4*>(sn + (size_t)pos * (D / 2) + 4 * cc);
+    f16x2 qh[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f32x2 x = unpack2<E>(wq[p]);
+        qh[p] = __builtin_bit_cast(f16x2, pack2<f16>((x[0] * c4[p] - x[1] * s4[p]) * qs,
+                                                     (x[0] * s4[p] + x[1] * c4[p]) * qs));
+    }
+
+    float M = -INFINITY, l = 0.f;  // M: the wave's running maximum (uniform)
+    float oa[8] = {};
+    for (int sl = wave; sl < nsplit; sl += nw) {
+        const int u0 = sl * kSlice;
+        u32x4 kr[NI], vr[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t off = (uint32_t)((u0 + i * RPI + rl) * D + 8 * cc) * 2;
+            kr[i] = buf_load16(kb, off);
+            vr[i] = buf_load16(vb, off);
+        }
+        if constexpr (APPEND) {
+            if (pos - u0 < kSlice) {  // uniform: this slice holds the new row
+                const int r = pos - u0;
+                if (rl == r % RPI) {
+                    const size_t cell = ((size_t)bh * Tmax + pos) * D + 8 * cc;
+                    const u32x4 kn = rotate_key_chunk<E>(
+                        *reinterpret_cast<const u32x4*>(knew + (size_t)bh * D + 8 * cc), c4, s4);
+                    const u32x4 vn =
+                        *reinterpret_cast<const u32x4*>(vnew + (size_t)bh * D + 8 * cc);
+                    *reinterpret_cast<u32x4*>(kc + cell) = kn;
+                    *reinterpret_cast<u32x4*>(vc + cell) = vn;
+#pragma unroll
+                    for (int i = 0; i < NI; ++i) {
+                        if (i == r / RPI) {
+                            kr[i] = kn;
+                            vr[i] = vn;
+                        }
+                    }
+                }
+            }
+        }
+        float s[NI];
+        float m = M;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t kw = kr[i][p];
+                acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, kw), qh[p], acc, false);
+            }
+#pragma unroll
+            for (int x = 1; x < NC; x <<= 1) acc += __shfl_xor(acc, x);
+            s[i] = u0 + i * RPI + rl <= pos ? acc : -INFINITY;
+            m = fmaxf(m, s[i]);
+        }
+#pragma unroll
+        for (int x = NC; x < 64; x <<= 1) m = fmaxf(m, __shfl_xor(m, x));
+        // m is finite: every slice holds row u0 <= pos
+        const float alpha = exp2_fast(M - m);  // 0 on the wave's first slice
+        l *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) oa[j] *= alpha;
+        M = m;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const float p = exp2_fast(s[i] - m);
+            l += p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f32x2 x = unpack2<E>(vr[i][e]);
+                oa[2 * e] += p * x[0];
+                oa[2 * e + 1] += p * x[1];
+            }
+        }
+    }
+    // sums over the wave's rows: the lanes that share chunk cc
+#pragma unroll
+    for (int x = NC; x < 64; x <<= 1) {
+        l += __shfl_xor(l, x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) oa[j] += __shfl_xor(oa[j], x);
+    }
+    float* dst = sp + wave * PS;
+    if (rl == 0) {
+        *reinterpret_cast<f32x4*>(dst + 8 * cc) = f32x4{oa[0], oa[1], oa[2], oa[3]};
+        *reinterpret_cast<f32x4*>(dst + 8 * cc + 4) = f32x4{oa[4], oa[5], oa[6], oa[7]};
+    }
+    if (lane == 0) {
+        dst[D] = M;  // -inf for a wave without slices (its weight below is 0)
+        dst[D + 1] = l;
+    }
+    __syncthreads();
+    float Mx = -INFINITY;
+    for (int w = 0; w < nw; ++w) Mx = fmaxf(Mx, sp[w * PS + D]);
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        float L = 0.f, O = 0.f;
+        for (int w = 0; w < nw; ++w) {
+            const float r = exp2_fast(sp[w * PS + D] - Mx);
+            L += r * sp[w * PS + D + 1];
+            O += r * sp[w * PS + d];
+        }
+        o[(size_t)bh * D + d] = static_cast<E>(O / L);
+        if (d == 0) lse[bh] = (Mx + log2f(L)) * kLn2;
+    }
+}
+
 // Explicit instantiations: the host pass does not always emit the launch stub of
 // a kernel template with a 16-bit element-type argument on its own.
 #define ATTN_DEC_INST(D_, E_)                                                                \
@@ -250,7 +395,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     template __global__ void decode_partial_kernel<D_, E_, true>(                             \
         const E_*, f16*, E_*, const float*, const float*, float*, const E_*, const E_*, int, int, \
         int, int, float);                                                                      \
-    template __global__ void decode_combine_kernel<D_, E_>(const float*, E_*, float*, int);
+    template __global__ void decode_combine_kernel<D_, E_>(const float*, E_*, float*, int);    \
+    template __global__ void decode_head_kernel<D_, E_, false>(                                \
+        const E_*, f16*, E_*, const float*, const float*, E_*, float*, const E_*, const E_*, int, \
+        int, int, float);                                                                      \
+    template __global__ void decode_head_kernel<D_, E_, true>(                                 \
+        const E_*, f16*, E_*, const float*, const float*, E_*, float*, const E_*, const E_*, int, \
+        int, int, float);
 ATTN_DEC_INST(64, bf16) ATTN_DEC_INST(128, bf16) ATTN_DEC_INST(64, f16) ATTN_DEC_INST(128, f16)
 #undef ATTN_DEC_INST
 
@@ -295,6 +446,18 @@ static hipError_t launch_decode_t(const void* q, const void* knew, const void* v
     f16* kc = static_cast<f16*>(const_cast<void*>(cache));
     E* vc = reinterpret_cast<E*>(static_cast<char*>(const_cast<void*>(cache)) + kbytes);
     const float qs = kLog2e / sqrtf((float)D);
+    if (B * H >= kHeadKernelMinHeads) {
+        const dim3 hgrid((unsigned)(B * H)), hblock(64 * (nsplit < kHeadWaves<D>() ? nsplit : kHeadWaves<D>()));
+        if (knew != nullptr)
+            hipLaunchKernelGGL((decode_head_kernel<D, E, true>), hgrid, hblock, 0, st,
+                               (const E*)q, kc, vc, cs, sn, (E*)o, lse, (const E*)knew,
+                               (const E*)vnew, Tmax, pos, nsplit, qs);
+        else
+            hipLaunchKernelGGL((decode_head_kernel<D, E, false>), hgrid, hblock, 0, st,
+                               (const E*)q, kc, vc, cs, sn, (E*)o, lse, (const E*)nullptr,
+                               (const E*)nullptr, Tmax, pos, nsplit, qs);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((nwaves + 3) / 4)), block(256);
     if (knew != nullptr)
         hipLaunchKernelGGL((decode_partial_kernel<D, E, true>), grid, block, 0, st, (const E*)q,

@@ -188,3 +188,47 @@ def test_fused_step_equals_append_then_decode(D, dtype):
             check(ob.cpu(), lb.cpu(), q, k, v, t, dtype, f"fused step {dtype} D{D} pos {t}")
     torch.cuda.synchronize()
     assert torch.equal(a.buf, b.buf)
+
+
+# 64 heads or more take one workgroup per head (its waves merge the slices in
+# LDS); Tmax spans more 64-key slices than that workgroup has waves (16 at D 64,
+# 8 at D 128), so waves also carry a running maximum over several slices
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D,Tmax", [(64, 1100), (128, 600)])
+def test_decode_many_heads(D, Tmax, dtype):
+    B, H = 4, 16
+    q, k, v = inputs(B, H, Tmax, D, dtype, seed=61 + D)
+    cache = attn.KVCache(B, H, Tmax, D, DT[dtype], DEV)
+    cache.append(k.to(DEV), v.to(DEV), 0)
+    for pos in (0, 63, 64, 511, 520, Tmax - 1):
+        o, lse = cache.decode(q[:, :, pos].contiguous().to(DEV), pos)
+        torch.cuda.synchronize()
+        check(o.cpu(), lse.cpu(), q, k, v, pos, dtype, f"many heads {dtype} D{D} pos {pos}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D,Tmax", [(64, 1100), (128, 600)])
+def test_fused_step_many_heads(D, Tmax, dtype):
+    """attn_decode_step with one workgroup per head: bitwise append + decode, and
+    the oracle, at positions on and around slice boundaries and past 16 (8) slices."""
+    B, H = 4, 16
+    q, k, v = inputs(B, H, Tmax, D, dtype, seed=71 + D)
+    a = attn.KVCache(B, H, Tmax, D, DT[dtype], DEV)
+    b = attn.KVCache(B, H, Tmax, D, DT[dtype], DEV)
+    positions = (0, 1, 64, 511, 512, Tmax - 1)
+    prev = 0
+    for pos in positions:
+        if pos > prev:  # rows prev .. pos-1 through the plain append on both caches
+            kk, vv = k[:, :, prev:pos].to(DEV), v[:, :, prev:pos].to(DEV)
+            a.append(kk, vv, prev)
+            b.append(kk, vv, prev)
+        qt, kt, vt = (x[:, :, pos].contiguous().to(DEV) for x in (q, k, v))
+        a.append(kt[:, :, None], vt[:, :, None], pos)
+        oa, la = a.decode(qt, pos)
+        ob, lb = b.step(qt, kt, vt, pos)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob) and torch.equal(la, lb), pos
+        check(ob.cpu(), lb.cpu(), q, k, v, pos, dtype, f"fused step many heads {dtype} D{D} pos {pos}")
+        prev = pos + 1
+    torch.cuda.synchronize()
+    assert torch.equal(a.buf, b.buf)
