@@ -1,20 +1,32 @@
 """Benchmark: causal RoPE attention forward + backward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--flush]
 
-One step = one forward (attn_rotate_qk then attn_fwd_rotated, which is
-exactly what attn_fwd enqueues) and one backward (attn_bwd_prep then
-attn_bwd_grads, which is exactly what attn_bwd enqueues) over one batch of
-synthetic input already resident in HBM; the RoPE tables are built before the
-timed region (they depend only on T, D and the base, like weights). Throughput
-uses the causal FLOP convention: forward 2*B*H*T^2*D, backward 2.5x forward.
+One step = one forward and one backward over one batch of synthetic input
+already resident in HBM, as a training step runs them: attn_fwd_save (the
+rotation pass, whose rotated q, k serve the forward and the backward, then the
+forward from them) then attn_bwd_saved (the per-row pre-pass and the gradient
+kernel). Each launch is made through the entry point of that stage
+(attn_rotate_qk, attn_fwd_rotated, attn_bwd_prep, attn_bwd_grads - exactly what
+the two calls enqueue) so that each can be timed. The RoPE tables are built before the timed region (they
+depend only on T, D and the base, like weights). Throughput uses the causal FLOP
+convention: forward 2*B*H*T^2*D, backward 2.5x forward.
 
-Prints ONE JSON line. The headline value is the whole step's rate over K
-steps launched back to back between two HIP events. Besides it the line carries
+Prints ONE JSON line. The headline value is the whole step's rate over K steps
+launched back to back (in blocks of steps between HIP events: mean over all K,
+and the p10 / median / p90 of the per-block step times). Besides it the line
+carries
+  plain_pair    the same step through attn_fwd + attn_bwd (the forward rotates
+                q, k on load; the backward forms the rotated q, k again with
+                the rotation pass), timed the same way;
+  flushed       with --flush: each step timed alone after 512 MB have been
+                written (cold caches);
   kernels       each kernel's average duration inside a step, from further
                 steps with a HIP event on the kernels' stream between kernels
                 (five rounds of R steps; min/max over the rounds);
-  roofline      for the kernel with the longest average duration;
+  roofline      for the kernel with the longest average duration: algorithmic
+                flops (the causal FLOP convention) / that duration, and the MFMA
+                flops the kernel actually executes;
   cpu_baseline  the float64 oracle timed on this host's cores on a bounded
                 sample of the same workload (and a parity check of the GPU
                 outputs on that sample).
@@ -32,15 +44,33 @@ sys.path.insert(0, ROOT)
 METRIC = "causal attn fwd+bwd TFLOP/s, bf16 B8 H12 T1024 D64; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16/fp16 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
+FLUSH_BYTES = 512 << 20
 
 
 def causal_flops(B, H, T, D):
-    unit = float(B) * H * T * T * D          # one causal product: 2 * (T^2/2) * D per head
-    return {"fwd": 2 * unit, "bwd": 5 * unit,
-            # products each kernel evaluates on the causal half (its own algorithmic work):
-            # the gradient kernel recomputes S and dP for dq and again for dk/dv (3 + 4)
-            "rotate_kernel": 0.0, "fwd_kernel": 2 * unit, "bwd_prep_kernel": 0.0,
-            "bwd_grads_kernel": 7 * unit}
+    """Algorithmic flops: one causal product is 2 * (T^2/2) * D per head; the
+    forward is two products (S, PV), the backward five (S, dP, dV, dQ, dK).
+    Recomputation is not counted; the gradient kernel does all the backward's
+    products."""
+    unit = float(B) * H * T * T * D
+    return {"fwd": 2 * unit, "bwd": 5 * unit, "rotate_kernel": 0.0,
+            "fwd_kernel": 2 * unit, "bwd_prep_kernel": 0.0, "bwd_grads_kernel": 5 * unit}
+
+
+def executed_mfma_flops(B, H, T, D):
+    """MFMA flops the kernels issue: every 32x32 block of (query, key) on or
+    below the diagonal in full (so the masked half of each diagonal block too).
+    The forward evaluates two products per block; the gradient kernel seven (its
+    dq items S, dP, dQ and its dk/dv items S, dP, dV, dK)."""
+    n = (T + 31) // 32
+    blk = float(B) * H * n * (n + 1) / 2 * (2 * 32 * 32 * D)
+    return {"rotate_kernel": 0.0, "fwd_kernel": 2 * blk, "bwd_prep_kernel": 0.0,
+            "bwd_grads_kernel": 7 * blk}
+
+
+def pct(xs, p):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs), p))
 
 
 def main():
@@ -49,6 +79,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--flush", action="store_true",
+                    help="also time each step alone after writing 512 MB (cold caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96,
                     help="heads of the workload the CPU oracle runs on")
@@ -100,6 +132,9 @@ def main():
     w = workloads.WORKLOADS[name]
     B, H, T, D = w.shape
     dt = {"bf16": attn.ATTN_BF16, "f16": attn.ATTN_F16, "f32": attn.ATTN_F32}[w.dtype]
+    if dt == attn.ATTN_F32:
+        print("bench.py times the 16-bit path", file=sys.stderr)
+        sys.exit(2)
     print(f"# workload {name} B{B} H{H} T{T} D{D} {w.dtype}", file=sys.stderr, flush=True)
     x = workloads.make(w, seed=0)
     g = {n: t.to(dev) for n, t in x.items()}
@@ -111,12 +146,9 @@ def main():
     wsb = attn.attn_bwd_workspace_bytes(B, H, T, D, dt)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     nsv = attn.attn_saved_bytes(B, H, T, D, dt)
-    saved = torch.empty(max(nsv, 1), dtype=torch.uint8, device=dev)
+    saved = torch.empty(nsv, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    if dt == attn.ATTN_F32:
-        print("bench.py times the 16-bit path", file=sys.stderr)
-        sys.exit(2)
 
     def rotate():
         attn.attn_rotate_qk(q, k, cs, sn, saved, nsv, B, H, T, D, dt, sh)
@@ -128,25 +160,63 @@ def main():
         attn.attn_bwd_prep(o, do, lse, ws, wsb, B, H, T, D, dt, sh)
 
     def bwd_grads():
-        attn.attn_bwd_grads(q, k, v, do, lse, cs, sn, saved, nsv, dq, dk, dv, ws, wsb, B, H, T,
-                            D, dt, sh)
+        attn.attn_bwd_grads(None, None, v, do, lse, cs, sn, saved, nsv, dq, dk, dv, ws, wsb,
+                            B, H, T, D, dt, sh)
 
-    for _ in range(args.warmup):
+    def step():
         rotate(); fwd(); bwd_prep(); bwd_grads()
-    torch.cuda.synchronize()
+
+    def plain_step():
+        attn.attn_fwd(q, k, v, cs, sn, o, lse, B, H, T, D, dt, sh)
+        attn.attn_bwd(q, k, v, o, do, lse, cs, sn, dq, dk, dv, ws, wsb, B, H, T, D, dt, sh)
 
     K = args.steps
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    BLOCK = 20 if K >= 40 else max(1, K // 2)
+
+    def timed(f):
+        """K steps back to back, an event every BLOCK steps: (mean ms, per-block ms)."""
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True)]
+        evs[0].record(stream)
+        done = 0
+        while done < K:
+            n = min(BLOCK, K - done)
+            for _ in range(n):
+                f()
+            done += n
+            evs.append(torch.cuda.Event(enable_timing=True))
+            evs[-1].record(stream)
+        torch.cuda.synchronize()
+        sizes = [BLOCK] * (K // BLOCK) + ([K % BLOCK] if K % BLOCK else [])
+        per = [evs[i].elapsed_time(evs[i + 1]) / sizes[i] for i in range(len(sizes))]
+        return evs[0].elapsed_time(evs[-1]) / K, per
+
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(K):  # the timed region: K whole steps back to back, nothing in between
-        rotate(); fwd(); bwd_prep(); bwd_grads()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / K
-    print(f"# timed {K} steps in {wall:.3f} s wall", file=sys.stderr, flush=True)
+    ms_step, blocks = timed(step)
+    print(f"# timed {K} steps in {time.perf_counter() - t0:.3f} s wall", file=sys.stderr,
+          flush=True)
+    ms_plain, blocks_plain = timed(plain_step)
+
+    flushed = None
+    if args.flush:
+        junk = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        per = []
+        for i in range(args.warmup + K):
+            junk.fill_(i & 0xff)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i >= args.warmup:
+                per.append(a.elapsed_time(b))
+        del junk
+        flushed = {"ms_per_step_median": round(pct(per, 50), 5),
+                   "ms_per_step_p10": round(pct(per, 10), 5),
+                   "ms_per_step_p90": round(pct(per, 90), 5),
+                   "tflops_median": None, "flush_bytes": FLUSH_BYTES, "steps": K}
 
     # per-kernel durations: R more whole steps with a HIP event on the kernels' stream
     # before and after every kernel, in five rounds; each interval is one kernel's share
@@ -171,20 +241,25 @@ def main():
             per[n].append(np.mean([row[i].elapsed_time(row[i + 1]) for row in evs]))
     per = {n: np.array(v) for n, v in per.items()}
     # leave every output as one full step writes it (for the parity check below)
-    rotate(); fwd(); bwd_prep(); bwd_grads()
+    step()
     torch.cuda.synchronize()
 
     fl = causal_flops(B, H, T, D)
+    ex = executed_mfma_flops(B, H, T, D)
     total = fl["fwd"] + fl["bwd"]
     value = total / (ms_step * 1e-3) / 1e12
+    tf = lambda ms: round(total / (ms * 1e-3) / 1e12, 2)
+    if flushed:
+        flushed["tflops_median"] = tf(flushed["ms_per_step_median"])
     kernels = {}
     for n, arr in per.items():
         ms = float(np.mean(arr))
         kernels[n] = {"avg_us": round(ms * 1e3, 2), "min_us": round(float(arr.min()) * 1e3, 2),
                       "max_us": round(float(arr.max()) * 1e3, 2),
-                      "tflops": round(fl[n] / (ms * 1e-3) / 1e12, 1)}
-    # the memory-bound passes: rotation reads q, k (bf16) and writes q', k' (fp16); the
-    # backward pre-pass reads o, dO (bf16) and lse and writes two fp32 per row
+                      "tflops": round(fl[n] / (ms * 1e-3) / 1e12, 1),
+                      "executed_tflops": round(ex[n] / (ms * 1e-3) / 1e12, 1)}
+    # the memory-bound passes: the rotation reads q, k (16-bit) and writes q', k' (fp16);
+    # the pre-pass reads o, dO (16-bit) and lse and writes two fp32 per row
     rot_bytes = 2 * (2 + 2) * B * H * T * D
     prep_bytes = 2 * 2 * B * H * T * D + 4 * B * H * T + 8 * B * H * T
     for n, nb in (("rotate_kernel", rot_bytes), ("bwd_prep_kernel", prep_bytes)):
@@ -194,7 +269,11 @@ def main():
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(dom, name)}
+                "traffic": measured_traffic(dom, name),
+                "algorithmic_gflop": round(fl[dom] / 1e9, 3),
+                "executed_gflop": round(ex[dom] / 1e9, 3),
+                "executed_frac": round(ex[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+                                       / PEAK_BF16_TFLOPS, 4)}
 
     cpu = None
     parity = None
@@ -213,14 +292,22 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_p10": round(pct(blocks, 10), 5),
+        "ms_per_step_median": round(pct(blocks, 50), 5),
+        "ms_per_step_p90": round(pct(blocks, 90), 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": name, "B": B, "H": H, "T": T, "D": D, "causal": True,
-                   "rope_base": w.base, "gflop_per_step": round(total / 1e9, 3)},
+                   "rope_base": w.base, "gflop_per_step": round(total / 1e9, 3),
+                   "step": "attn_fwd_save (rotate + fwd) + attn_bwd_saved (prep + grads)"},
         "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "plain_pair": {"step": "attn_fwd + attn_bwd", "ms_per_step": round(ms_plain, 5),
+                       "ms_per_step_median": round(pct(blocks_plain, 50), 5),
+                       "tflops": tf(ms_plain)},
+        "flushed": flushed,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -268,18 +355,18 @@ def bench_packed(args, dev):
     def permuted():
         for i, t in enumerate((q, k, v)):
             t.copy_(qkv[:, :, i].permute(0, 2, 1, 3))
-        attn.attn_fwd(q, k, v, cs, sn, o, lse, saved, nsv, B, H, T, D, dt, sh)
+        attn.attn_fwd_save(q, k, v, cs, sn, o, lse, saved, nsv, B, H, T, D, dt, sh)
         o_t2.copy_(o.permute(0, 2, 1, 3))
         do.copy_(do_t.permute(0, 2, 1, 3))
-        attn.attn_bwd(q, k, v, o, do, lse, cs, sn, saved, nsv, dq, dk, dv, ws, nws, B, H, T, D,
-                      dt, sh)
+        attn.attn_bwd_saved(q, k, v, o, do, lse, cs, sn, saved, nsv, dq, dk, dv, ws, nws, B, H,
+                            T, D, dt, sh)
         for i, t in enumerate((dq, dk, dv)):
             dqkv2[:, :, i].copy_(t.permute(0, 2, 1, 3))
 
     def plain():
-        attn.attn_fwd(q, k, v, cs, sn, o, lse, saved, nsv, B, H, T, D, dt, sh)
-        attn.attn_bwd(q, k, v, o, do, lse, cs, sn, saved, nsv, dq, dk, dv, ws, nws, B, H, T, D,
-                      dt, sh)
+        attn.attn_fwd_save(q, k, v, cs, sn, o, lse, saved, nsv, B, H, T, D, dt, sh)
+        attn.attn_bwd_saved(q, k, v, o, do, lse, cs, sn, saved, nsv, dq, dk, dv, ws, nws, B, H,
+                            T, D, dt, sh)
 
     def timed(f):
         for _ in range(args.warmup):
@@ -463,10 +550,10 @@ def bench_layer(args, dev):
 
 # kernel -> the sources that define it; a traffic figure is valid only for these exact sources
 KERNEL_SOURCES = {
+    "rotate_kernel": ["rope_tables.hip", "device_common.h"],
     "fwd_kernel": ["fwd_16bit.hip", "device_common.h"],
     "bwd_grads_kernel": ["bwd_16bit.hip", "device_common.h"],
     "bwd_prep_kernel": ["bwd_prep.hip", "device_common.h"],
-    "rotate_kernel": ["rope_tables.hip", "device_common.h"],
 }
 
 
@@ -508,10 +595,12 @@ def cpu_baseline(w, x, gpu_out, heads, min_seconds):
 
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                            if i.get("user_api") == "blas"] or [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas_threads = max([i.get("num_threads", 1) for i in blas] or [1])
+        blas_name = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}"
+                                      for i in blas})) or None
     except Exception:  # pragma: no cover - informational only
-        blas_threads = None
+        blas_threads, blas_name = None, None
     B, H, T, D = w.shape
     heads = max(1, min(heads, B * H))
     sel = [(i // H, i % H) for i in range(heads)]
@@ -535,6 +624,7 @@ def cpu_baseline(w, x, gpu_out, heads, min_seconds):
     secs = t_fwd + t_bwd
     cpu = {"value": round(passes * (fl["fwd"] + fl["bwd"]) / secs / 1e12, 6), "unit": "TFLOP/s",
            "cores": blas_threads, "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+           "blas": blas_name,
            "sample": f"{heads} of {B * H} heads (all T={T} rows), {passes} passes of fwd + bwd "
                      f"({t_fwd:.2f} s + {t_bwd:.2f} s), numpy float64 full T x T matrices, "
                      f"causal FLOP count"}

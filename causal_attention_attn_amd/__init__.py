@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     AttnError,
     attn_bwd,
+    attn_bwd_saved,
     attn_bwd_grads,
     attn_bwd_packed,
     attn_bwd_prep,
@@ -21,6 +22,7 @@ from ._lib import (  # noqa: F401
     attn_decode_workspace_bytes,
     attn_fwd,
     attn_fwd_packed,
+    attn_fwd_save,
     attn_fwd_rotated,
     attn_kv_append,
     attn_kv_cache_bytes,

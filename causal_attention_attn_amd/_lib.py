@@ -30,11 +30,14 @@ _SIGS = {
     "attn_rope_tables": (_I, [_P, _P, _I, _I, ctypes.c_double, _P]),
     "attn_saved_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "attn_rotate_qk": (_I, [_P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
-    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
+    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "attn_fwd_save": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
     "attn_fwd_rotated": (_I, [_P, _Z, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "attn_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
-    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _P, _Z,
+    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                       _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_saved": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _P, _Z,
+                            _I, _I, _I, _I, _I, _P]),
     "attn_bwd_prep": (_I, [_P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
     "attn_bwd_grads": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _P, _Z,
                             _I, _I, _I, _I, _I, _P]),
@@ -125,9 +128,14 @@ def attn_rotate_qk(q, k, cos_tab, sin_tab, saved, saved_bytes, B, H, T, D, dtype
           int(saved_bytes), B, H, T, D, dtype, _stream(stream))
 
 
-def attn_fwd(q, k, v, cos_tab, sin_tab, o, lse, saved, saved_bytes, B, H, T, D, dtype,
-             stream=None):
+def attn_fwd(q, k, v, cos_tab, sin_tab, o, lse, B, H, T, D, dtype, stream=None):
     _call("attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(cos_tab), _ptr(sin_tab), _ptr(o),
+          _ptr(lse), B, H, T, D, dtype, _stream(stream))
+
+
+def attn_fwd_save(q, k, v, cos_tab, sin_tab, o, lse, saved, saved_bytes, B, H, T, D, dtype,
+                  stream=None):
+    _call("attn_fwd_save", _ptr(q), _ptr(k), _ptr(v), _ptr(cos_tab), _ptr(sin_tab), _ptr(o),
           _ptr(lse), _ptr(saved), int(saved_bytes), B, H, T, D, dtype, _stream(stream))
 
 
@@ -140,11 +148,18 @@ def attn_bwd_workspace_bytes(B, H, T, D, dtype):
     return int(load().attn_bwd_workspace_bytes(B, H, T, D, dtype))
 
 
-def attn_bwd(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, dk, dv,
-             workspace, workspace_bytes, B, H, T, D, dtype, stream=None):
+def attn_bwd(q, k, v, o, dO, lse, cos_tab, sin_tab, dq, dk, dv, workspace, workspace_bytes,
+             B, H, T, D, dtype, stream=None):
     _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(cos_tab),
-          _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dq), _ptr(dk), _ptr(dv),
-          _ptr(workspace), int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
+          _ptr(sin_tab), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), int(workspace_bytes),
+          B, H, T, D, dtype, _stream(stream))
+
+
+def attn_bwd_saved(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, dk, dv,
+                   workspace, workspace_bytes, B, H, T, D, dtype, stream=None):
+    _call("attn_bwd_saved", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+          _ptr(cos_tab), _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dq), _ptr(dk),
+          _ptr(dv), _ptr(workspace), int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
 
 
 def attn_bwd_prep(o, dO, lse, workspace, workspace_bytes, B, H, T, D, dtype, stream=None):

@@ -31,6 +31,27 @@ def _shape(*ts):
     return tuple(x.shape)
 
 
+def _check_lse(lse, B, H, T, device):
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32
+            or tuple(lse.shape) != (B, H, T) or lse.device != device or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 [B, H, T] = {(B, H, T)} tensor on "
+                         f"{device}")
+
+
+def _saved_arg(saved, nsaved, device):
+    """(pointer source, byte size) of a saved buffer after checking it; None when
+    the dtype needs none."""
+    if nsaved == 0:
+        return None, 0
+    if (not isinstance(saved, torch.Tensor) or saved.device != device
+            or not saved.is_contiguous()):
+        raise ValueError(f"saved must be the contiguous tensor forward() returned, on {device}")
+    nbytes = saved.numel() * saved.element_size()
+    if nbytes < nsaved:
+        raise ValueError(f"saved holds {nbytes} bytes; these inputs need {nsaved}")
+    return saved, nbytes
+
+
 def rope_tables(T, D, base=10000.0, device=None):
     """fp32 cos/sin tables [T, D/2] built by the library's table kernel; cached
     per (device, T, D, base)."""
@@ -46,33 +67,43 @@ def rope_tables(T, D, base=10000.0, device=None):
     return _tables[key]
 
 
-def forward(q, k, v, base=10000.0):
-    """Causal RoPE attention forward; returns (o, lse, saved). `saved` holds the
-    rotated q and k (bf16 inputs; an empty tensor for fp32) and must be passed
-    to backward()."""
+def forward(q, k, v, base=10000.0, save=True):
+    """Causal RoPE attention forward; returns (o, lse, saved). With save=True (and
+    a 16-bit dtype) `saved` is a uint8 tensor holding the rotated q and k the
+    forward formed (attn_fwd_save), for backward(); otherwise it is None and the
+    forward is attn_fwd."""
     B, H, T, D = _shape(q, k, v)
     dt = _dtype_code(q)
     cs, sn = rope_tables(T, D, base, q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
-    saved = torch.empty(max(nsaved, 1), dtype=torch.uint8, device=q.device)
-    _lib.attn_fwd(q, k, v, cs, sn, o, lse, saved if nsaved else None, nsaved, B, H, T, D, dt)
+    if not save or nsaved == 0:
+        _lib.attn_fwd(q, k, v, cs, sn, o, lse, B, H, T, D, dt)
+        return o, lse, None
+    saved = torch.empty(nsaved, dtype=torch.uint8, device=q.device)
+    _lib.attn_fwd_save(q, k, v, cs, sn, o, lse, saved, nsaved, B, H, T, D, dt)
     return o, lse, saved
 
 
-def backward(q, k, v, o, do, lse, saved, base=10000.0):
+def backward(q, k, v, o, do, lse, saved=None, base=10000.0):
     """Gradients of sum(o * do) w.r.t. the pre-RoPE q, k and v; returns (dq, dk, dv).
-    `saved` is the third value forward() returned for these inputs."""
+    `saved`: the third value forward() returned for these q and k (attn_bwd_saved),
+    or None (attn_bwd, which rotates q and k again)."""
     B, H, T, D = _shape(q, k, v, o, do)
     dt = _dtype_code(q)
+    _check_lse(lse, B, H, T, q.device)
     cs, sn = rope_tables(T, D, base, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
     nbytes = _lib.attn_bwd_workspace_bytes(B, H, T, D, dt)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    _lib.attn_bwd(q, k, v, o, do, lse, cs, sn, saved if nsaved else None, nsaved, dq, dk, dv,
-                  ws, nbytes, B, H, T, D, dt)
+    nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
+    if saved is None or nsaved == 0:
+        _lib.attn_bwd(q, k, v, o, do, lse, cs, sn, dq, dk, dv, ws, nbytes, B, H, T, D, dt)
+    else:
+        sv, nsv = _saved_arg(saved, nsaved, q.device)
+        _lib.attn_bwd_saved(q, k, v, o, do, lse, cs, sn, sv, nsv, dq, dk, dv, ws, nbytes,
+                            B, H, T, D, dt)
     return dq, dk, dv
 
 
@@ -85,36 +116,40 @@ def _packed_shape(qkv):
     return B, H, T, D
 
 
-def forward_packed(qkv, base=10000.0):
+def forward_packed(qkv, base=10000.0, save=True):
     """Forward from the QKV projection's packed [B, T, 3, H, D] output; returns
     (o, lse, saved) with o as [B, T, H, D] (= [B, T, H*D], the out-projection's
-    input). 16-bit dtypes only."""
+    input) and saved as in forward(). 16-bit dtypes only."""
     B, H, T, D = _packed_shape(qkv)
     dt = _dtype_code(qkv)
     cs, sn = rope_tables(T, D, base, qkv.device)
     o = torch.empty((B, T, H, D), dtype=qkv.dtype, device=qkv.device)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=qkv.device)
     nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
-    saved = torch.empty(max(nsaved, 1), dtype=torch.uint8, device=qkv.device)
-    _lib.attn_fwd_packed(qkv, cs, sn, o, lse, saved, nsaved, B, H, T, D, dt)
+    saved = torch.empty(nsaved, dtype=torch.uint8, device=qkv.device) if save else None
+    _lib.attn_fwd_packed(qkv, cs, sn, o, lse, saved, nsaved if save else 0, B, H, T, D, dt)
     return o, lse, saved
 
 
-def backward_packed(qkv, o, do, lse, saved, base=10000.0):
+def backward_packed(qkv, o, do, lse, saved=None, base=10000.0):
     """Gradients of sum(o * do) w.r.t. the pre-RoPE q, k and v of a packed
-    [B, T, 3, H, D] tensor, returned in that layout (o and do are [B, T, H, D])."""
+    [B, T, 3, H, D] tensor, returned in that layout (o and do are [B, T, H, D]);
+    `saved` as in backward()."""
     B, H, T, D = _packed_shape(qkv)
     for t in (o, do):
-        if tuple(t.shape) != (B, T, H, D) or t.dtype != qkv.dtype or not t.is_contiguous():
-            raise ValueError("o and do must be contiguous [B, T, H, D] of the packed dtype")
+        if (tuple(t.shape) != (B, T, H, D) or t.dtype != qkv.dtype or not t.is_contiguous()
+                or t.device != qkv.device):
+            raise ValueError("o and do must be contiguous [B, T, H, D] of the packed dtype and "
+                             "device")
     dt = _dtype_code(qkv)
+    _check_lse(lse, B, H, T, qkv.device)
     cs, sn = rope_tables(T, D, base, qkv.device)
     dqkv = torch.empty_like(qkv)
     nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
+    sv, nsv = (None, 0) if saved is None else _saved_arg(saved, nsaved, qkv.device)
     nbytes = _lib.attn_bwd_workspace_bytes(B, H, T, D, dt)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=qkv.device)
-    _lib.attn_bwd_packed(qkv, o, do, lse, cs, sn, saved, nsaved, dqkv, ws, nbytes, B, H, T, D,
-                         dt)
+    _lib.attn_bwd_packed(qkv, o, do, lse, cs, sn, sv, nsv, dqkv, ws, nbytes, B, H, T, D, dt)
     return dqkv
 
 
@@ -127,7 +162,10 @@ class KVCache:
         self.B, self.H, self.Tmax, self.D, self.base = B, H, Tmax, D, base
         self.dtype = dtype
         self.code = _DTYPES[dtype]
-        self.device = torch.device(device if device is not None else "cuda")
+        dev = torch.device(device if device is not None else "cuda")
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
         self.nbytes = _lib.attn_kv_cache_bytes(B, H, Tmax, D, self.code)
         if self.nbytes == 0:
             raise ValueError("unsupported cache shape or dtype")
@@ -136,6 +174,11 @@ class KVCache:
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.cs, self.sn = rope_tables(Tmax, D, base, self.device)
 
+    def _on_device(self, *ts):
+        for t in ts:
+            if t.device != self.device:
+                raise ValueError(f"tensor on {t.device}; the cache lives on {self.device}")
+
     def append(self, k, v, pos0):
         """k, v: [B, H, n, D] pre-RoPE keys and values of positions pos0 .. pos0+n-1."""
         B, H, n, D = k.shape
@@ -143,6 +186,7 @@ class KVCache:
             raise ValueError("k and v must be [B, H, n, D] of the cache's B, H and D")
         if k.dtype != self.dtype or v.dtype != self.dtype:
             raise ValueError("k and v must have the cache's dtype")
+        self._on_device(k, v)
         _lib.attn_kv_append(k.contiguous(), v.contiguous(), self.cs, self.sn, self.buf,
                             self.nbytes, pos0, n, B, H, self.Tmax, D, self.code)
 
@@ -150,6 +194,7 @@ class KVCache:
         """q: [B, H, D] pre-RoPE query at position pos; returns (o [B, H, D], lse [B, H])."""
         if tuple(q.shape) != (self.B, self.H, self.D) or q.dtype != self.dtype:
             raise ValueError("q must be [B, H, D] of the cache's dtype")
+        self._on_device(q)
         o = torch.empty_like(q)
         lse = torch.empty((self.B, self.H), dtype=torch.float32, device=q.device)
         _lib.attn_decode(q.contiguous(), self.buf, self.nbytes, self.cs, self.sn, o, lse,
@@ -163,6 +208,7 @@ class KVCache:
         for t in (q, k_new, v_new):
             if tuple(t.shape) != (self.B, self.H, self.D) or t.dtype != self.dtype:
                 raise ValueError("q, k_new and v_new must be [B, H, D] of the cache's dtype")
+        self._on_device(q, k_new, v_new)
         o = torch.empty_like(q)
         lse = torch.empty((self.B, self.H), dtype=torch.float32, device=q.device)
         _lib.attn_decode_step(q.contiguous(), k_new.contiguous(), v_new.contiguous(), self.buf,

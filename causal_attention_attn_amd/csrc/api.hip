@@ -33,15 +33,26 @@ int check_ptrs(std::initializer_list<const void*> ps) {
     return ATTN_OK;
 }
 
-bool any_alias(std::initializer_list<const void*> outs, std::initializer_list<const void*> ins) {
-    for (const void* a : outs) {
-        for (const void* b : ins)
-            if (a == b) return true;
-    }
-    for (const void* a : outs) {
-        int n = 0;
-        for (const void* b : outs) n += (a == b);
-        if (n > 1) return true;
+// The bytes [p, p + n) a call reads or writes through one pointer argument.
+struct Span {
+    const void* p;
+    size_t n;
+};
+
+bool overlap(const Span& a, const Span& b) {
+    if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// True when an output's bytes overlap an input's or another output's (null
+// pointers and empty spans are skipped).
+bool any_alias(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+    for (const Span& a : outs) {
+        for (const Span& b : ins)
+            if (overlap(a, b)) return true;
+        for (const Span& b : outs)
+            if (&a != &b && overlap(a, b)) return true;
     }
     return false;
 }
@@ -54,15 +65,34 @@ int hip_status(hipError_t e) {
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+size_t elem_bytes(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+// Byte sizes of the attention tensors of one call.
+struct Sizes {
+    size_t x;    // one [B, H, T, D] tensor of the dtype
+    size_t row;  // one [B, H, T] fp32 tensor (lse)
+    size_t tab;  // one [T, D/2] fp32 table
+    Sizes(int B, int H, int T, int D, int dtype)
+        : x((size_t)B * H * T * D * elem_bytes(dtype)),
+          row((size_t)4 * B * H * T),
+          tab((size_t)T * (D / 2) * 4) {}
+};
+
 size_t saved_need(int B, int H, int T, int D, int dtype) {
     return dtype != ATTN_F32 ? round256((size_t)4 * B * H * T * D) : 0;
 }
 
-size_t workspace_need(int B, int H, int T, int dtype) {
+// per-row entries of the pre-pass: -lse*log2(e) and -delta (16-bit), delta (fp32)
+size_t rows_need(int B, int H, int T, int dtype) {
     return round256((size_t)(dtype != ATTN_F32 ? 8 : 4) * B * H * T);
 }
 
-// the rotated q/k buffer an entry point reads: required for bf16 and fp16, unused for fp32
+// attn_bwd: the per-row entries, then (16-bit path) room for the rotated q, k
+size_t workspace_need(int B, int H, int T, int D, int dtype) {
+    return rows_need(B, H, T, dtype) + saved_need(B, H, T, D, dtype);
+}
+
+// the rotated q/k buffer an entry point reads or writes: used by the 16-bit path only
 int check_saved(const void* saved, size_t saved_bytes, int B, int H, int T, int D, int dtype) {
     if (dtype == ATTN_F32) return ATTN_OK;
     if (saved == nullptr) return ATTN_ERR_NULL;
@@ -71,16 +101,8 @@ int check_saved(const void* saved, size_t saved_bytes, int B, int H, int T, int 
     return ATTN_OK;
 }
 
-int check_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-              const float* cs, const float* sn, const void* saved, size_t saved_bytes,
-              const void* ws, size_t ws_bytes, int B, int H, int T, int D, int dtype) {
-    int st = check_shape(B, H, T, D, dtype);
-    if (st) return st;
-    st = check_ptrs({q, k, v, dO, lse, cs, sn});
-    if (st) return st;
-    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
-    if (st) return st;
-    if (ws == nullptr || ws_bytes < workspace_need(B, H, T, dtype)) return ATTN_ERR_WORKSPACE;
+int check_workspace(const void* ws, size_t ws_bytes, size_t need) {
+    if (ws == nullptr || ws_bytes < need) return ATTN_ERR_WORKSPACE;
     if (misaligned(ws)) return ATTN_ERR_ALIGN;
     return ATTN_OK;
 }
@@ -94,6 +116,18 @@ attn::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* 
     a.lse = lse; a.cs = cs; a.sn = sn; a.rot = saved;
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.ws = static_cast<float*>(const_cast<void*>(ws));
+    a.lqkv = a.lo = attn::layout_bhtd(H, T, D);
+    a.B = B; a.H = H; a.T = T; a.D = D;
+    a.stream = static_cast<hipStream_t>(stream);
+    return a;
+}
+
+attn::FwdArgs fwd_args(const void* q, const void* k, const void* v, const float* cs,
+                       const float* sn, const void* rot, void* o, float* lse, int B, int H, int T,
+                       int D, void* stream) {
+    attn::FwdArgs a = {};
+    a.q = q; a.k = k; a.v = v; a.cs = cs; a.sn = sn; a.rot = rot;
+    a.o = o; a.lse = lse;
     a.lqkv = a.lo = attn::layout_bhtd(H, T, D);
     a.B = B; a.H = H; a.T = T; a.D = D;
     a.stream = static_cast<hipStream_t>(stream);
@@ -116,6 +150,52 @@ int check_packed(int B, int H, int T, int D, int dtype) {
 // the q, k and v slices of a packed [B, T, 3, H, D] tensor (16-bit elements)
 const void* packed_slot(const void* qkv, int slot, int H, int D) {
     return static_cast<const char*>(qkv) + (size_t)slot * H * D * 2;
+}
+
+// the part of an attn_bwd workspace that holds the rotated q, k (16-bit path)
+void* ws_rotated(void* ws, int B, int H, int T, int dtype) {
+    return static_cast<char*>(ws) + rows_need(B, H, T, dtype);
+}
+
+// The forward of the [B, H, T, D] entry points. 16-bit path: without `save`, one
+// launch of the RoPE-on-load kernel; with it, the rotation pass writes the
+// rotated q, k there and the forward reads them (the backward needs them too,
+// and one pass that feeds both is cheaper than the loader writing them out).
+// fp32: the fp32 kernel (save ignored).
+int run_fwd(const void* q, const void* k, const void* v, const float* cs, const float* sn,
+            void* o, float* lse, void* save, int B, int H, int T, int D, int dtype,
+            void* stream) {
+    if (dtype == ATTN_F32)
+        return hip_status(attn::launch_fwd_f32(
+            fwd_args(q, k, v, cs, sn, nullptr, o, lse, B, H, T, D, stream)));
+    if (save != nullptr) {
+        const int st = hip_status(attn::launch_rotate_qk(q, k, attn::layout_bhtd(H, T, D), cs, sn,
+                                                         save, B, H, T, D, dtype == ATTN_F16,
+                                                         static_cast<hipStream_t>(stream)));
+        if (st) return st;
+    }
+    return hip_status(attn::launch_fwd16(
+        fwd_args(q, k, v, cs, sn, save, o, lse, B, H, T, D, stream), dtype == ATTN_F16));
+}
+
+// The backward's two stages, from a buffer of rotated q, k (16-bit path; the
+// fp32 kernels rotate on load and ignore `rot`).
+int run_bwd_stages(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, const float* cs, const float* sn, const void* rot,
+                   void* dq, void* dk, void* dv, void* ws, int B, int H, int T, int D,
+                   int dtype, void* stream) {
+    const attn::BwdArgs a =
+        bwd_args(q, k, v, o, dO, lse, cs, sn, rot, dq, dk, dv, ws, B, H, T, D, stream);
+    if (dtype == ATTN_F32) {
+        int st = hip_status(attn::launch_bwd_prep_f32(a));
+        if (st) return st;
+        st = hip_status(attn::launch_bwd_dq_f32(a));
+        if (st) return st;
+        return hip_status(attn::launch_bwd_dkdv_f32(a));
+    }
+    const int st = hip_status(attn::launch_bwd_prep16(a, dtype == ATTN_F16));
+    if (st) return st;
+    return hip_status(attn::launch_bwd_grads16(a, dtype == ATTN_F16));
 }
 
 }  // namespace
@@ -143,7 +223,8 @@ int attn_rope_tables(float* cos_tab, float* sin_tab, int T, int D, double base, 
     if (T < 1 || D < 2 || D > 1024 || (D & 1)) return ATTN_ERR_SHAPE;
     if ((long long)T * (D / 2) >= (1ll << 31)) return ATTN_ERR_SHAPE;
     if (!(base > 1.0) || base != base) return ATTN_ERR_VALUE;
-    if (cos_tab == sin_tab) return ATTN_ERR_ALIAS;
+    const size_t tab = (size_t)T * (D / 2) * 4;
+    if (any_alias({{cos_tab, tab}, {sin_tab, tab}}, {})) return ATTN_ERR_ALIAS;
     return hip_status(attn::launch_rope_tables(cos_tab, sin_tab, T, D, base,
                                                static_cast<hipStream_t>(stream)));
 }
@@ -163,7 +244,10 @@ int attn_rotate_qk(const void* q, const void* k, const float* cos_tab, const flo
     if (st) return st;
     st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
     if (st) return st;
-    if (any_alias({saved}, {q, k, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
+    const Sizes z(B, H, T, D, dtype);
+    if (any_alias({{saved, saved_need(B, H, T, D, dtype)}},
+                  {{q, z.x}, {k, z.x}, {cos_tab, z.tab}, {sin_tab, z.tab}}))
+        return ATTN_ERR_ALIAS;
     return hip_status(attn::launch_rotate_qk(q, k, attn::layout_bhtd(H, T, D), cos_tab, sin_tab,
                                              saved, B, H, T, D, dtype == ATTN_F16,
                                              static_cast<hipStream_t>(stream)));
@@ -178,43 +262,48 @@ int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void*
     if (st) return st;
     st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
     if (st) return st;
-    if (any_alias({o, lse}, {v, saved})) return ATTN_ERR_ALIAS;
-    attn::FwdArgs a = {};
-    a.v = v; a.rot = saved; a.o = o; a.lse = lse;
-    a.lqkv = a.lo = attn::layout_bhtd(H, T, D);
-    a.B = B; a.H = H; a.T = T; a.D = D;
-    a.stream = static_cast<hipStream_t>(stream);
+    const Sizes z(B, H, T, D, dtype);
+    if (any_alias({{o, z.x}, {lse, z.row}}, {{v, z.x}, {saved, saved_need(B, H, T, D, dtype)}}))
+        return ATTN_ERR_ALIAS;
+    const attn::FwdArgs a =
+        fwd_args(nullptr, nullptr, v, nullptr, nullptr, saved, o, lse, B, H, T, D, stream);
     return hip_status(attn::launch_fwd16(a, dtype == ATTN_F16));
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, const float* cos_tab,
-             const float* sin_tab, void* o, float* lse, void* saved, size_t saved_bytes, int B,
-             int H, int T, int D, int dtype, void* stream) {
+             const float* sin_tab, void* o, float* lse, int B, int H, int T, int D, int dtype,
+             void* stream) {
+    int st = check_shape(B, H, T, D, dtype);
+    if (st) return st;
+    st = check_ptrs({q, k, v, cos_tab, sin_tab, o, lse});
+    if (st) return st;
+    const Sizes z(B, H, T, D, dtype);
+    if (any_alias({{o, z.x}, {lse, z.row}},
+                  {{q, z.x}, {k, z.x}, {v, z.x}, {cos_tab, z.tab}, {sin_tab, z.tab}}))
+        return ATTN_ERR_ALIAS;
+    return run_fwd(q, k, v, cos_tab, sin_tab, o, lse, nullptr, B, H, T, D, dtype, stream);
+}
+
+int attn_fwd_save(const void* q, const void* k, const void* v, const float* cos_tab,
+                  const float* sin_tab, void* o, float* lse, void* saved, size_t saved_bytes,
+                  int B, int H, int T, int D, int dtype, void* stream) {
     int st = check_shape(B, H, T, D, dtype);
     if (st) return st;
     st = check_ptrs({q, k, v, cos_tab, sin_tab, o, lse});
     if (st) return st;
     st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
     if (st) return st;
-    if (any_alias({o, lse}, {q, k, v, cos_tab, sin_tab, saved})) return ATTN_ERR_ALIAS;
-    if (dtype != ATTN_F32) {
-        if (any_alias({saved}, {q, k, v, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
-        st = attn_rotate_qk(q, k, cos_tab, sin_tab, saved, saved_bytes, B, H, T, D, dtype,
-                            stream);
-        if (st) return st;
-        return attn_fwd_rotated(saved, saved_bytes, v, o, lse, B, H, T, D, dtype, stream);
-    }
-    attn::FwdArgs a = {};
-    a.q = q; a.k = k; a.v = v; a.cs = cos_tab; a.sn = sin_tab; a.o = o; a.lse = lse;
-    a.lqkv = a.lo = attn::layout_bhtd(H, T, D);
-    a.B = B; a.H = H; a.T = T; a.D = D;
-    a.stream = static_cast<hipStream_t>(stream);
-    return hip_status(attn::launch_fwd_f32(a));
+    const Sizes z(B, H, T, D, dtype);
+    const Span sv = {dtype == ATTN_F32 ? nullptr : saved, saved_need(B, H, T, D, dtype)};
+    if (any_alias({{o, z.x}, {lse, z.row}, sv},
+                  {{q, z.x}, {k, z.x}, {v, z.x}, {cos_tab, z.tab}, {sin_tab, z.tab}}))
+        return ATTN_ERR_ALIAS;
+    return run_fwd(q, k, v, cos_tab, sin_tab, o, lse, saved, B, H, T, D, dtype, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype) {
     if (check_shape(B, H, T, D, dtype) != ATTN_OK) return 0;
-    return workspace_need(B, H, T, dtype);
+    return workspace_need(B, H, T, D, dtype);
 }
 
 int attn_bwd_prep(const void* o, const void* dO, const float* lse, void* workspace,
@@ -223,10 +312,11 @@ int attn_bwd_prep(const void* o, const void* dO, const float* lse, void* workspa
     if (st) return st;
     st = check_ptrs({o, dO, lse});
     if (st) return st;
-    if (workspace == nullptr || workspace_bytes < workspace_need(B, H, T, dtype))
-        return ATTN_ERR_WORKSPACE;
-    if (misaligned(workspace)) return ATTN_ERR_ALIGN;
-    if (any_alias({workspace}, {o, dO, lse})) return ATTN_ERR_ALIAS;
+    st = check_workspace(workspace, workspace_bytes, rows_need(B, H, T, dtype));
+    if (st) return st;
+    const Sizes z(B, H, T, D, dtype);
+    if (any_alias({{workspace, rows_need(B, H, T, dtype)}}, {{o, z.x}, {dO, z.x}, {lse, z.row}}))
+        return ATTN_ERR_ALIAS;
     const attn::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr,
                                      nullptr, nullptr, nullptr, nullptr, workspace, B, H, T, D,
                                      stream);
@@ -239,12 +329,21 @@ int attn_bwd_grads(const void* q, const void* k, const void* v, const void* dO,
                    const void* saved, size_t saved_bytes, void* dq, void* dk, void* dv,
                    const void* workspace, size_t workspace_bytes, int B, int H, int T, int D,
                    int dtype, void* stream) {
-    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, workspace,
-                       workspace_bytes, B, H, T, D, dtype);
+    int st = check_shape(B, H, T, D, dtype);
     if (st) return st;
-    st = check_ptrs({dq, dk, dv});
+    // the 16-bit kernels take the rotated q, k from `saved` and do not read q, k
+    st = dtype == ATTN_F32 ? check_ptrs({q, k, v, dO, lse, cos_tab, sin_tab, dq, dk, dv})
+                           : check_ptrs({v, dO, lse, cos_tab, sin_tab, dq, dk, dv});
     if (st) return st;
-    if (any_alias({dq, dk, dv}, {q, k, v, dO, lse, cos_tab, sin_tab, saved, workspace}))
+    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+    if (st) return st;
+    st = check_workspace(workspace, workspace_bytes, rows_need(B, H, T, dtype));
+    if (st) return st;
+    const Sizes z(B, H, T, D, dtype);
+    const Span sv = {dtype == ATTN_F32 ? nullptr : saved, saved_need(B, H, T, D, dtype)};
+    if (any_alias({{dq, z.x}, {dk, z.x}, {dv, z.x}},
+                  {{q, z.x}, {k, z.x}, {v, z.x}, {dO, z.x}, {lse, z.row}, {cos_tab, z.tab},
+                   {sin_tab, z.tab}, sv, {workspace, rows_need(B, H, T, dtype)}}))
         return ATTN_ERR_ALIAS;
     const attn::BwdArgs a = bwd_args(q, k, v, nullptr, dO, lse, cos_tab, sin_tab, saved, dq, dk,
                                      dv, workspace, B, H, T, D, stream);
@@ -255,20 +354,56 @@ int attn_bwd_grads(const void* q, const void* k, const void* v, const void* dO,
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-             const float* lse, const float* cos_tab, const float* sin_tab, const void* saved,
-             size_t saved_bytes, void* dq, void* dk, void* dv, void* workspace,
-             size_t workspace_bytes, int B, int H, int T, int D, int dtype, void* stream) {
-    int st = check_bwd(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, workspace,
-                       workspace_bytes, B, H, T, D, dtype);
+             const float* lse, const float* cos_tab, const float* sin_tab, void* dq, void* dk,
+             void* dv, void* workspace, size_t workspace_bytes, int B, int H, int T, int D,
+             int dtype, void* stream) {
+    int st = check_shape(B, H, T, D, dtype);
     if (st) return st;
-    st = check_ptrs({o, dq, dk, dv});
+    st = check_ptrs({q, k, v, o, dO, lse, cos_tab, sin_tab, dq, dk, dv});
     if (st) return st;
-    if (any_alias({dq, dk, dv, workspace}, {q, k, v, o, dO, lse, cos_tab, sin_tab, saved}))
+    const size_t need = workspace_need(B, H, T, D, dtype);
+    st = check_workspace(workspace, workspace_bytes, need);
+    if (st) return st;
+    const Sizes z(B, H, T, D, dtype);
+    if (any_alias({{dq, z.x}, {dk, z.x}, {dv, z.x}, {workspace, need}},
+                  {{q, z.x}, {k, z.x}, {v, z.x}, {o, z.x}, {dO, z.x}, {lse, z.row},
+                   {cos_tab, z.tab}, {sin_tab, z.tab}}))
         return ATTN_ERR_ALIAS;
-    st = attn_bwd_prep(o, dO, lse, workspace, workspace_bytes, B, H, T, D, dtype, stream);
+    void* rot = nullptr;
+    if (dtype != ATTN_F32) {  // rotate this call's q and k into the workspace
+        rot = ws_rotated(workspace, B, H, T, dtype);
+        st = hip_status(attn::launch_rotate_qk(q, k, attn::layout_bhtd(H, T, D), cos_tab,
+                                               sin_tab, rot, B, H, T, D, dtype == ATTN_F16,
+                                               static_cast<hipStream_t>(stream)));
+        if (st) return st;
+    }
+    return run_bwd_stages(q, k, v, o, dO, lse, cos_tab, sin_tab, rot, dq, dk, dv, workspace, B,
+                          H, T, D, dtype, stream);
+}
+
+int attn_bwd_saved(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, const float* cos_tab, const float* sin_tab,
+                   const void* saved, size_t saved_bytes, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, int B, int H, int T, int D,
+                   int dtype, void* stream) {
+    int st = check_shape(B, H, T, D, dtype);
     if (st) return st;
-    return attn_bwd_grads(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, dk, dv,
-                          workspace, workspace_bytes, B, H, T, D, dtype, stream);
+    st = dtype == ATTN_F32 ? check_ptrs({q, k, v, o, dO, lse, cos_tab, sin_tab, dq, dk, dv})
+                           : check_ptrs({v, o, dO, lse, cos_tab, sin_tab, dq, dk, dv});
+    if (st) return st;
+    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+    if (st) return st;
+    const size_t need = rows_need(B, H, T, dtype);
+    st = check_workspace(workspace, workspace_bytes, need);
+    if (st) return st;
+    const Sizes z(B, H, T, D, dtype);
+    const Span sv = {dtype == ATTN_F32 ? nullptr : saved, saved_need(B, H, T, D, dtype)};
+    if (any_alias({{dq, z.x}, {dk, z.x}, {dv, z.x}, {workspace, need}},
+                  {{q, z.x}, {k, z.x}, {v, z.x}, {o, z.x}, {dO, z.x}, {lse, z.row},
+                   {cos_tab, z.tab}, {sin_tab, z.tab}, sv}))
+        return ATTN_ERR_ALIAS;
+    return run_bwd_stages(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, dq, dk, dv, workspace, B,
+                          H, T, D, dtype, stream);
 }
 
 int attn_fwd_packed(const void* qkv, const float* cos_tab, const float* sin_tab, void* o,
@@ -278,21 +413,26 @@ int attn_fwd_packed(const void* qkv, const float* cos_tab, const float* sin_tab,
     if (st) return st;
     st = check_ptrs({qkv, cos_tab, sin_tab, o, lse});
     if (st) return st;
-    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
-    if (st) return st;
-    if (any_alias({o, lse, saved}, {qkv, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (saved != nullptr) {
+        st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+        if (st) return st;
+    }
+    const Sizes z(B, H, T, D, dtype);
+    if (any_alias({{o, z.x}, {lse, z.row}, {saved, saved_need(B, H, T, D, dtype)}},
+                  {{qkv, 3 * z.x}, {cos_tab, z.tab}, {sin_tab, z.tab}}))
+        return ATTN_ERR_ALIAS;
     const attn::Layout lqkv = attn::layout_bthd(H, T, D, 3);
-    st = hip_status(attn::launch_rotate_qk(packed_slot(qkv, 0, H, D), packed_slot(qkv, 1, H, D),
-                                           lqkv, cos_tab, sin_tab, saved, B, H, T, D,
-                                           dtype == ATTN_F16, s));
-    if (st) return st;
-    attn::FwdArgs a = {};
-    a.v = packed_slot(qkv, 2, H, D); a.rot = saved; a.o = o; a.lse = lse;
+    if (saved != nullptr) {  // the rotation pass, then the forward from its output
+        st = hip_status(attn::launch_rotate_qk(packed_slot(qkv, 0, H, D), packed_slot(qkv, 1, H, D),
+                                               lqkv, cos_tab, sin_tab, saved, B, H, T, D,
+                                               dtype == ATTN_F16, static_cast<hipStream_t>(stream)));
+        if (st) return st;
+    }
+    attn::FwdArgs a = fwd_args(packed_slot(qkv, 0, H, D), packed_slot(qkv, 1, H, D),
+                               packed_slot(qkv, 2, H, D), cos_tab, sin_tab, saved, o, lse, B, H, T,
+                               D, stream);
     a.lqkv = lqkv;
     a.lo = attn::layout_bthd(H, T, D, 1);
-    a.B = B; a.H = H; a.T = T; a.D = D;
-    a.stream = s;
     return hip_status(attn::launch_fwd16(a, dtype == ATTN_F16));
 }
 
@@ -304,16 +444,33 @@ int attn_bwd_packed(const void* qkv, const void* o, const void* dO, const float*
     if (st) return st;
     st = check_ptrs({qkv, o, dO, lse, cos_tab, sin_tab, dqkv});
     if (st) return st;
-    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+    if (saved != nullptr) {
+        st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+        if (st) return st;
+    }
+    // without a saved buffer the rotated q, k go into the workspace
+    const size_t need = saved != nullptr ? rows_need(B, H, T, dtype)
+                                         : workspace_need(B, H, T, D, dtype);
+    st = check_workspace(workspace, workspace_bytes, need);
     if (st) return st;
-    if (workspace == nullptr || workspace_bytes < workspace_need(B, H, T, dtype))
-        return ATTN_ERR_WORKSPACE;
-    if (misaligned(workspace)) return ATTN_ERR_ALIGN;
-    if (any_alias({dqkv, workspace}, {qkv, o, dO, lse, cos_tab, sin_tab, saved}))
+    const Sizes z(B, H, T, D, dtype);
+    if (any_alias({{dqkv, 3 * z.x}, {workspace, need}},
+                  {{qkv, 3 * z.x}, {o, z.x}, {dO, z.x}, {lse, z.row}, {cos_tab, z.tab},
+                   {sin_tab, z.tab}, {saved, saved_need(B, H, T, D, dtype)}}))
         return ATTN_ERR_ALIAS;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const void* rot = saved;
+    if (rot == nullptr) {
+        void* r = ws_rotated(workspace, B, H, T, dtype);
+        st = hip_status(attn::launch_rotate_qk(packed_slot(qkv, 0, H, D), packed_slot(qkv, 1, H, D),
+                                               attn::layout_bthd(H, T, D, 3), cos_tab, sin_tab, r,
+                                               B, H, T, D, dtype == ATTN_F16, s));
+        if (st) return st;
+        rot = r;
+    }
     char* g = static_cast<char*>(dqkv);
     attn::BwdArgs a = bwd_args(nullptr, nullptr, packed_slot(qkv, 2, H, D), o, dO, lse, cos_tab,
-                               sin_tab, saved, g, g + (size_t)H * D * 2, g + (size_t)2 * H * D * 2,
+                               sin_tab, rot, g, g + (size_t)H * D * 2, g + (size_t)2 * H * D * 2,
                                workspace, B, H, T, D, stream);
     a.lqkv = attn::layout_bthd(H, T, D, 3);
     a.lo = attn::layout_bthd(H, T, D, 1);
@@ -331,7 +488,7 @@ const char* attn_status_string(int status) {
         case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
         case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
         case ATTN_ERR_HIP: return "HIP launch failed";
-        case ATTN_ERR_ALIAS: return "output aliases an input";
+        case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
         case ATTN_ERR_VALUE: return "invalid scalar argument";
         case ATTN_ERR_SAVED: return "saved rotated q/k buffer too small";
         default: return "unknown status";
@@ -382,7 +539,10 @@ int attn_kv_append(const void* k, const void* v, const float* cos_tab, const flo
     st = check_ptrs({k, v, cos_tab, sin_tab, cache});
     if (st) return st;
     if (cache_bytes < cache_need(B, H, Tmax, D)) return ATTN_ERR_WORKSPACE;
-    if (any_alias({cache}, {k, v, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
+    const size_t kv = (size_t)B * H * n * D * 2, tab = (size_t)Tmax * (D / 2) * 4;
+    if (any_alias({{cache, cache_need(B, H, Tmax, D)}},
+                  {{k, kv}, {v, kv}, {cos_tab, tab}, {sin_tab, tab}}))
+        return ATTN_ERR_ALIAS;
     return hip_status(attn::launch_kv_append(k, v, cos_tab, sin_tab, cache, pos0, n, B, H, Tmax,
                                              D, dtype == ATTN_F16,
                                              static_cast<hipStream_t>(stream)));
@@ -401,7 +561,10 @@ int attn_decode(const void* q, const void* cache, size_t cache_bytes, const floa
     if (workspace == nullptr || workspace_bytes < decode_ws_need(B, H, Tmax, D))
         return ATTN_ERR_WORKSPACE;
     if (misaligned(workspace)) return ATTN_ERR_ALIGN;
-    if (any_alias({o, lse, workspace}, {q, cache, cos_tab, sin_tab})) return ATTN_ERR_ALIAS;
+    const size_t row = (size_t)B * H * D * 2, tab = (size_t)Tmax * (D / 2) * 4;
+    if (any_alias({{o, row}, {lse, (size_t)4 * B * H}, {workspace, decode_ws_need(B, H, Tmax, D)}},
+                  {{q, row}, {cache, cache_need(B, H, Tmax, D)}, {cos_tab, tab}, {sin_tab, tab}}))
+        return ATTN_ERR_ALIAS;
     return hip_status(attn::launch_decode(q, nullptr, nullptr, cache, cos_tab, sin_tab, o, lse,
                                           static_cast<float*>(workspace), pos, B, H, Tmax, D,
                                           dtype == ATTN_F16, static_cast<hipStream_t>(stream)));
@@ -420,8 +583,10 @@ int attn_decode_step(const void* q, const void* k_new, const void* v_new, void* 
     if (workspace == nullptr || workspace_bytes < decode_ws_need(B, H, Tmax, D))
         return ATTN_ERR_WORKSPACE;
     if (misaligned(workspace)) return ATTN_ERR_ALIGN;
-    if (any_alias({o, lse, workspace, cache}, {q, k_new, v_new, cos_tab, sin_tab}) ||
-        any_alias({o, lse, workspace}, {cache}))
+    const size_t row = (size_t)B * H * D * 2, tab = (size_t)Tmax * (D / 2) * 4;
+    if (any_alias({{o, row}, {lse, (size_t)4 * B * H}, {workspace, decode_ws_need(B, H, Tmax, D)},
+                   {cache, cache_need(B, H, Tmax, D)}},
+                  {{q, row}, {k_new, row}, {v_new, row}, {cos_tab, tab}, {sin_tab, tab}}))
         return ATTN_ERR_ALIAS;
     return hip_status(attn::launch_decode(q, k_new, v_new, cache, cos_tab, sin_tab, o, lse,
                                           static_cast<float*>(workspace), pos, B, H, Tmax, D,
@@ -469,9 +634,8 @@ int attn_rmsnorm_fwd(const void* x, const void* res, const void* g, float eps, v
     st = check_ptrs({x, g, y, rstd});
     if (st) return st;
     if ((res != nullptr && misaligned(res)) || (h != nullptr && misaligned(h))) return ATTN_ERR_ALIGN;
-    if (any_alias({y, rstd}, {x, g}) || (res != nullptr && any_alias({y, rstd}, {res})) ||
-        (h != nullptr && any_alias({h}, {x, g, y, rstd})) ||
-        (h != nullptr && res != nullptr && h == res))
+    const size_t nc = (size_t)N * C * 2;
+    if (any_alias({{y, nc}, {rstd, (size_t)4 * N}, {h, nc}}, {{x, nc}, {res, nc}, {g, (size_t)C * 2}}))
         return ATTN_ERR_ALIAS;
     return hip_status(attn::launch_rmsnorm_fwd(x, res, g, eps, h, y, rstd, N, C,
                                                dtype == ATTN_F16, static_cast<hipStream_t>(stream)));
@@ -492,8 +656,9 @@ int attn_rmsnorm_bwd(const void* h, const void* g, const float* rstd, const void
     if (dres != nullptr && misaligned(dres)) return ATTN_ERR_ALIGN;
     if (workspace == nullptr || workspace_bytes < norm_ws_need(N, C)) return ATTN_ERR_WORKSPACE;
     if (misaligned(workspace)) return ATTN_ERR_ALIGN;
-    if (any_alias({dh, dg, workspace}, {h, g, rstd, dy}) ||
-        (dres != nullptr && any_alias({dh, dg, workspace}, {dres})))
+    const size_t nc = (size_t)N * C * 2;
+    if (any_alias({{dh, nc}, {dg, (size_t)4 * C}, {workspace, norm_ws_need(N, C)}},
+                  {{h, nc}, {g, (size_t)C * 2}, {rstd, (size_t)4 * N}, {dy, nc}, {dres, nc}}))
         return ATTN_ERR_ALIAS;
     return hip_status(attn::launch_rmsnorm_bwd(h, g, rstd, dy, dres, dh, dg,
                                                static_cast<float*>(workspace), N, C,
@@ -505,7 +670,7 @@ int attn_swiglu_fwd(const void* u, void* out, int N, int F, int dtype, void* str
     if (st) return st;
     st = check_ptrs({u, out});
     if (st) return st;
-    if (any_alias({out}, {u})) return ATTN_ERR_ALIAS;
+    if (any_alias({{out, (size_t)N * F * 2}}, {{u, (size_t)2 * N * F * 2}})) return ATTN_ERR_ALIAS;
     return hip_status(attn::launch_swiglu(u, nullptr, out, N, F, false, dtype == ATTN_F16,
                                           static_cast<hipStream_t>(stream)));
 }
@@ -516,7 +681,8 @@ int attn_swiglu_bwd(const void* u, const void* dout, void* du, int N, int F, int
     if (st) return st;
     st = check_ptrs({u, dout, du});
     if (st) return st;
-    if (any_alias({du}, {u, dout})) return ATTN_ERR_ALIAS;
+    if (any_alias({{du, (size_t)2 * N * F * 2}}, {{u, (size_t)2 * N * F * 2}, {dout, (size_t)N * F * 2}}))
+        return ATTN_ERR_ALIAS;
     return hip_status(attn::launch_swiglu(u, dout, du, N, F, true, dtype == ATTN_F16,
                                           static_cast<hipStream_t>(stream)));
 }

@@ -48,14 +48,7 @@ constexpr int partial_stride() { return D + 4; }  // o[D], m, l, 2 pad: 16-byte 
 // R_u k for one 16-byte chunk (4 feature pairs) of a key row, rounded once to fp16.
 template <typename E>
 __device__ __forceinline__ u32x4 rotate_key_chunk(u32x4 wk, f32x4 cv, f32x4 sv) {
-    u32x4 rk;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const f32x2 kp = unpack2<E>(wk[p]);
-        const float k0 = kp[0], k1 = kp[1];
-        rk[p] = pack2<f16>(k0 * cv[p] - k1 * sv[p], k0 * sv[p] + k1 * cv[p]);
-    }
-    return rk;
+    return rope_chunk_f16<E>(wk, cv, sv, 1.f);
 }
 
 // Append n tokens to the cache: K' rows R_u k_u (u = pos0 + i) rounded once to
@@ -125,12 +118,12 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const u32x4 wq = *reinterpret_cast<const u32x4*>(q + (size_t)bh * D + 8 * cc);
     const f32x4 c4 = *reinterpret_cast<const f32x4*>(cs + (size_t)pos * (D / 2) + 4 * cc);
     const f32x4 s4 = *reinterpret_cast<const f32x4*>(sn + (size_t)pos * (D / 2) + 4 * cc);
+    const u32x4 rq = rope_chunk_f16<E>(wq, c4, s4, qs);
     f16x2 qh[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const f32x2 x = unpack2<E>(wq[p]);
-        qh[p] = __builtin_bit_cast(f16x2, pack2<f16>((x[0] * c4[p] - x[1] * s4[p]) * qs,
-                                                     (x[0] * s4[p] + x[1] * c4[p]) * qs));
+        const uint32_t w = rq[p];  // a plain value: bit_cast of a vector element reads element 0
+        qh[p] = __builtin_bit_cast(f16x2, w);
     }
     if constexpr (APPEND) {
         if (pos - u0 < kSlice) {  // uniform: this wave's slice holds the new row
@@ -277,12 +270,12 @@ __global__ __launch_bounds__(64 * kHeadWaves<D>()) void decode_head_kernel(
     const u32x4 wq = *reinterpret_cast<const u32x4*>(q + (size_t)bh * D + 8 * cc);
     const f32x4 c4 = *reinterpret_cast<const f32x4*>(cs + (size_t)pos * (D / 2) + 4 * cc);
     const f32x4 s4 = *reinterpret_cast<const f32x4*>(sn + (size_t)pos * (D / 2) + 4 * cc);
+    const u32x4 rq = rope_chunk_f16<E>(wq, c4, s4, qs);
     f16x2 qh[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const f32x2 x = unpack2<E>(wq[p]);
-        qh[p] = __builtin_bit_cast(f16x2, pack2<f16>((x[0] * c4[p] - x[1] * s4[p]) * qs,
-                                                     (x[0] * s4[p] + x[1] * c4[p]) * qs));
+        const uint32_t w = rq[p];  // a plain value: bit_cast of a vector element reads element 0
+        qh[p] = __builtin_bit_cast(f16x2, w);
     }
 
     float M = -INFINITY, l = 0.f;  // M: the wave's running maximum (uniform)

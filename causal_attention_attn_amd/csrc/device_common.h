@@ -115,6 +115,25 @@ __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
     }
 }
 
+// RoPE on one 16-byte chunk of a row: the four adjacent feature pairs
+// (x0, x1) of w (storage type E) become (x0 c - x1 s, x0 s + x1 c) for the
+// pair's cosine c and sine s, times `scale`, rounded once to fp16. The
+// arithmetic is spelled out (explicit fused multiply-adds) so that every kernel
+// that rotates a row - the forward's loaders, the rotation pass, the cache
+// append and the decode query - produces bitwise the same values.
+template <typename E>
+__device__ __forceinline__ u32x4 rope_chunk_f16(u32x4 w, f32x4 c, f32x4 s, float scale) {
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f32x2 x = unpack2<E>(w[p]);
+        const float y0 = __builtin_fmaf(x[0], c[p], -(x[1] * s[p]));
+        const float y1 = __builtin_fmaf(x[0], s[p], x[1] * c[p]);
+        r[p] = pack2<f16>(y0 * scale, y1 * scale);
+    }
+    return r;
+}
+
 template <typename V>
 __device__ __forceinline__ V as_vec8(u32x4 w) { return __builtin_bit_cast(V, w); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }

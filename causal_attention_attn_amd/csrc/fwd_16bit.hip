@@ -4,10 +4,16 @@
 // FlashAttention-style exact attention ("Show HN: NanoEuler", paragraph 2): the
 // score matrix is produced tile by tile in registers, a running row maximum and
 // row sum implement the softmax online, and only o and the per-row log-sum-exp
-// reach HBM. RoPE ("Tiny Hackable CUDA", section 3) has already been applied by
-// the rotation pass: q and k arrive rotated, in fp16. Causality (keys u <=
-// query t) is enforced by skipping every 32x32 block wholly above the diagonal
-// and masking only the diagonal blocks.
+// reach HBM. RoPE ("Tiny Hackable CUDA", section 3: on the query and key
+// projections) is applied on load, or has been applied by the rotation pass:
+//   * RoPE on load (ROPE): each lane rotates its own query once, in registers,
+//     and every 64-key tile goes global -> registers (raw keys and their cos/sin
+//     rows) -> rotation in fp32 -> fp16 -> LDS, one step ahead of its use;
+//   * rotated input: the rotation pass has written the rotated q, k (fp16), and
+//     key tiles stream straight from global memory into LDS.
+// Both form the same fp16 values (rope_chunk_f16), so both give the same o and
+// lse bitwise. Causality (keys u <= query t) is enforced by skipping every
+// 32x32 block wholly above the diagonal and masking only the diagonal blocks.
 //
 // Work decomposition (one workgroup = 4 waves = 128 queries of one head):
 //   * each wave owns 32 queries; its rotated queries live in registers as the
@@ -16,15 +22,15 @@
 //     score error small where the softmax is sharp (bf16 operands give ~3e-2
 //     error on O for logits of standard deviation ~9). P and V are of the
 //     storage type E (P is rounded to E before the PV product).
-//   * 64-key tiles of rotated K (fp16) and V (E) stream straight from
-//     global memory into an NS-stage LDS ring (buffer_load ... lds), issued
-//     NS-1 tiles ahead of use: no registers hold tiles in flight, and one
-//     barrier per tile both publishes a tile and frees the oldest stage;
+//   * 64-key tiles of V (E) - and of rotated K without ROPE - stream straight
+//     from global memory into a three-stage LDS ring (buffer_load ... lds),
+//     issued two tiles ahead of use; one barrier per tile both publishes a tile
+//     and frees the oldest stage;
 //   * S^T puts one query per lane column, so each lane owns one query's running
 //     max/sum; the running maximum enters as the MFMA's initial accumulator, so
 //     the per-element softmax work is exp2, rounding to E and a packed pair sum
 //     (the exact tile maximum is only taken when the probabilities would leave
-//     their bound, see fwd_tile);
+//     their bound, see fwd_softmax_pv);
 //   * the rounded probabilities of S^T are directly the B operand of
 //     O^T += V^T P^T; the V^T operand comes from the row-major V tile through
 //     the LDS transpose read (ds_read_b64_tr_b16);
@@ -208,41 +214,97 @@ __device__ __forceinline__ void fwd_softmax_pv(FwdState<D>& st, f32x16* x, const
     }
 }
 
+// Raw key rows of one 64-row tile and the RoPE table entries they need, held in
+// registers from their load until they are rotated into the LDS ring (RoPE on
+// load: the forward reads the caller's un-rotated k). Thread tid owns CPT = D/32
+// 16-byte chunks: chunk cc = tid % NC of tile rows tid / NC + i * RSTEP. Loads go
+// through buffer resources that end at row T, so rows past the sequence read as
+// zeros (cos = sin = 0 rotates them to zero).
+template <int D, typename E>
+struct KRot {
+    static constexpr int NC = D / 8;          // 16-byte chunks per row
+    static constexpr int CPT = D / 32;        // chunks per thread
+    static constexpr int RSTEP = 256 / NC;    // rows between a thread's chunks
+    u32x4 raw[CPT];
+    f32x4 c[CPT], s[CPT];
+
+    // rows r0 .. r0+63 of a head whose rows are `pitch` elements apart
+    __device__ __forceinline__ void load(const E* head, int pitch, const float* cs,
+                                         const float* sn, int T, int r0, int tid) {
+        const int rows = T > r0 ? T - r0 : 0;
+        const rsrc_t kb = make_rsrc(head + (size_t)r0 * pitch,
+                                    rows > 0 ? (uint32_t)((rows - 1) * pitch + D) * 2 : 0u);
+        const rsrc_t cb = make_rsrc(cs + (size_t)r0 * (D / 2), (uint32_t)rows * (D / 2) * 4);
+        const rsrc_t sb = make_rsrc(sn + (size_t)r0 * (D / 2), (uint32_t)rows * (D / 2) * 4);
+        const int cc = tid % NC, r = tid / NC;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int rr = r + i * RSTEP;
+            raw[i] = buf_load16(kb, (uint32_t)(rr * pitch + 8 * cc) * 2);
+            c[i] = __builtin_bit_cast(f32x4, buf_load16(cb, (uint32_t)(rr * (D / 2) + 4 * cc) * 4));
+            s[i] = __builtin_bit_cast(f32x4, buf_load16(sb, (uint32_t)(rr * (D / 2) + 4 * cc) * 4));
+        }
+    }
+
+    // Rotate, round to fp16 and put the chunks at their swizzled LDS positions in
+    // `tile`.
+    __device__ __forceinline__ void store(char* tile, int tid) const {
+        const int cc = tid % NC, r = tid / NC;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int rr = r + i * RSTEP;
+            *reinterpret_cast<u32x4*>(tile + rr * (2 * D) + 16 * swz<D>(rr, cc)) =
+                rope_chunk_f16<E>(raw[i], c[i], s[i], 1.f);
+        }
+    }
+};
+
 // Shared state of one workgroup's pass over its key tiles.
 template <int D, typename E>
 struct FwdCtx {
-    const f16* kr;
+    const f16* kr;      // pre-rotated keys (ROPE = false)
+    const E* k;         // un-rotated keys (ROPE = true)
     const E* v;
-    int vst;  // elements between consecutive rows of v
-    int T, wq0, lane, wave;
+    const float *cs, *sn;
+    int kst;            // elements between consecutive rows of k (ROPE)
+    int vst;            // elements between consecutive rows of v
+    int T, wq0, lane, wave, tid;
     int ntiles;  // key tiles of the block (no tile past the last one is loaded)
 };
 
 // Step n of the tile loop; tile n sits in ring stage STG = n % NS and its K
-// operands are already in kr. Scores of tile n first; then wait for tile n+1,
-// publish it with the barrier (which also frees the stage of tile n-1, whose
-// last reads were made before it) and refill that stage with tile n+NS-1;
+// operands are already in kr. Scores of tile n first; then (ROPE) rotate the raw
+// rows of tile n+1, loaded one step earlier, into their stage; wait for tile
+// n+1's V, publish both with the barrier (which also frees the stage of tile
+// n-1, whose last reads were made before it) and start loading tile n+2 (V
+// straight into LDS, K into registers; without ROPE both straight into LDS);
 // finish tile n (its V operands are read before the softmax, which hides their
 // latency) and read tile n+1's K operands while the PV products run.
-template <int D, typename E, int STG, bool DIAG, bool STRIDED>
+template <int D, typename E, int STG, bool DIAG, bool STRIDED, bool ROPE>
 __device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, KOps<D>& kr,
-                                         const Ring& rg, const TileLoads<D, 64, 4>& ld,
+                                         KRot<D, E>& kq, const Ring& rg,
+                                         const TileLoads<D, 64, 4>& ld,
                                          const OperandOffs<D>& of, const FwdCtx<D, E>& x, int n) {
     using C = FwdTile<D>;
     constexpr int NS = C::NS;
+    static_assert(NS == 3, "the loaders assume a three-stage ring");
     constexpr int NXT = (STG + 1) % NS;
     constexpr int FREE = (STG + NS - 1) % NS;
     const int k0 = n * C::BN;
     const bool live = !(DIAG && k0 > x.wq0);  // false: tile wholly above this wave's diagonal
     f32x16 s[C::NSB];
     if (live) fwd_scores<D, DIAG>(s, st, qf, kr, k0, x.wq0, x.lane);
-    wait_vmcnt<C::LPT * (NS - 3)>();
+    if constexpr (ROPE) {
+        if (!DIAG || n + 1 < x.ntiles) kq.store(rg.k[NXT], x.tid);
+    }
+    wait_vmcnt<0>();
     ring_barrier();
     const int nx = n + NS - 1;
     // full steps load unchecked: their tile nx lies past the block's last one
     // only for a ragged T, and is then read within the head or as zeros
     if (!DIAG || nx < x.ntiles) {
-        ld.issue(x.kr, x.T, nx * C::BN, rg.k[FREE], x.wave);
+        if constexpr (ROPE) kq.load(x.k, x.kst, x.cs, x.sn, x.T, nx * C::BN, x.tid);
+        else ld.issue(x.kr, x.T, nx * C::BN, rg.k[FREE], x.wave);
         if constexpr (STRIDED) ld.issue_strided(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave, x.vst);
         else ld.issue(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave);
     }
@@ -250,11 +312,16 @@ __device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, KOps<
     read_k(kr, rg.k[NXT], of);
 }
 
-template <int D, typename E, bool STRIDED>
+// The forward kernel. ROPE: q and k are the caller's un-rotated tensors (layout
+// lqk) and are rotated on load - each lane's query once, in registers, and every
+// key tile on its way into LDS. Without ROPE, qr and kr hold the rotated values
+// already (the rotation pass).
+template <int D, typename E, bool STRIDED, bool ROPE>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
-    const f16* __restrict__ qr, const f16* __restrict__ kr, const E* __restrict__ v,
-    E* __restrict__ o, float* __restrict__ lse, Layout lv, Layout lo, int H, int BH, int T,
-    int nqb, int ncu) {
+    const f16* __restrict__ qr, const f16* __restrict__ kr, const E* __restrict__ q,
+    const E* __restrict__ k, const float* __restrict__ cs, const float* __restrict__ sn,
+    const E* __restrict__ v, E* __restrict__ o, float* __restrict__ lse, Layout lqk, Layout lv,
+    Layout lo, int H, int BH, int T, int nqb, int ncu) {
     using C = FwdTile<D>;
     constexpr int NS = C::NS;
     // one __shared__ object per ring stage (see Ring); stages >= NS are stubs
@@ -279,30 +346,56 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
     const int kend = min(T, q0 + C::BM);
     const int ntiles = (kend + C::BN - 1) / C::BN;
     const int nfull = min(ntiles, q0 / C::BN);  // tiles wholly below every query of the block
-    // v and o: [B, H, T, D] unless STRIDED (then where their layouts put them)
-    const FwdCtx<D, E> x = {kr + hoff, v + (STRIDED ? lv.head(bh, H) : (long long)hoff),
-                            STRIDED ? lv.st : D, T, wq0, lane, wave, ntiles};
+    // q, k and v: [B, H, T, D] unless STRIDED (then where their layouts put them)
+    const long long qkhead = STRIDED ? lqk.head(bh, H) : (long long)hoff;
+    const int qkst = STRIDED ? lqk.st : D;
+    const FwdCtx<D, E> x = {kr + hoff, k + qkhead, v + (STRIDED ? lv.head(bh, H) : (long long)hoff),
+                            cs, sn, qkst, STRIDED ? lv.st : D, T, wq0, lane, wave, tid, ntiles};
     const TileLoads<D, 64, 4> ld(wave, lane);
     const OperandOffs<D> of(lane);
+    KRot<D, E> kq;
 
-    // prologue: tile 0, this lane's query, then tiles 1 .. NS-2 (rows past T read
-    // as zeros); the first step waits for tile 0 and the query only
-    ld.issue(x.kr, T, 0, rg.k[0], wave);
+    // prologue: tile 0, this lane's query, then tile 1 (rows past T read as
+    // zeros); the first step waits for tile 0 and the query only
+    if constexpr (ROPE) kq.load(x.k, qkst, cs, sn, T, 0, tid);
+    else ld.issue(x.kr, T, 0, rg.k[0], wave);
     if constexpr (STRIDED) ld.issue_strided(x.v, T, 0, rg.v[0], wave, x.vst);
     else ld.issue(x.v, T, 0, rg.v[0], wave);
 
-    const rsrc_t qh = make_rsrc(qr + hoff, (uint32_t)T * D * 2);
     f16x8 qf[C::DK];
+    if constexpr (ROPE) {
+        // this lane's query, features 16c + 8hf .. +7 for c < DK, rotated by R_tq
+        // and scaled by log2(e)/sqrt(D) in fp32, rounded once to fp16
+        const float qs = kLog2e / sqrtf((float)D);
+        const rsrc_t qh = make_rsrc(q + qkhead, (uint32_t)((T - 1) * qkst + D) * 2);
+        const rsrc_t ch = make_rsrc(cs, (uint32_t)T * (D / 2) * 4);
+        const rsrc_t sh = make_rsrc(sn, (uint32_t)T * (D / 2) * 4);
+        u32x4 wq[C::DK];
+        f32x4 cq[C::DK], sq[C::DK];
 #pragma unroll
-    for (int c = 0; c < C::DK; ++c)
-        qf[c] = __builtin_bit_cast(f16x8, buf_load16(qh, (uint32_t)(tq * D + 16 * c + 8 * hf) * 2));
+        for (int c = 0; c < C::DK; ++c) {
+            const int col = 16 * c + 8 * hf;
+            wq[c] = buf_load16(qh, (uint32_t)(tq * qkst + col) * 2);
+            cq[c] = __builtin_bit_cast(f32x4, buf_load16(ch, (uint32_t)(tq * (D / 2) + col / 2) * 4));
+            sq[c] = __builtin_bit_cast(f32x4, buf_load16(sh, (uint32_t)(tq * (D / 2) + col / 2) * 4));
+        }
+#pragma unroll
+        for (int c = 0; c < C::DK; ++c)
+            qf[c] = __builtin_bit_cast(f16x8, rope_chunk_f16<E>(wq[c], cq[c], sq[c], qs));
+        // tile 0's keys into stage 0
+        kq.store(rg.k[0], tid);
+    } else {
+        const rsrc_t qh = make_rsrc(qr + hoff, (uint32_t)T * D * 2);
+#pragma unroll
+        for (int c = 0; c < C::DK; ++c)
+            qf[c] = __builtin_bit_cast(f16x8, buf_load16(qh, (uint32_t)(tq * D + 16 * c + 8 * hf) * 2));
+    }
 
-#pragma unroll
-    for (int s = 1; s < NS - 1; ++s) {
-        if (s >= ntiles) break;
-        ld.issue(x.kr, T, s * C::BN, rg.k[s], wave);
-        if constexpr (STRIDED) ld.issue_strided(x.v, T, s * C::BN, rg.v[s], wave, x.vst);
-        else ld.issue(x.v, T, s * C::BN, rg.v[s], wave);
+    if (1 < ntiles) {
+        if constexpr (ROPE) kq.load(x.k, qkst, cs, sn, T, C::BN, tid);
+        else ld.issue(x.kr, T, C::BN, rg.k[1], wave);
+        if constexpr (STRIDED) ld.issue_strided(x.v, T, C::BN, rg.v[1], wave, x.vst);
+        else ld.issue(x.v, T, C::BN, rg.v[1], wave);
     }
 
     FwdState<D> st;
@@ -312,8 +405,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
     st.m = 0.f;
     st.l = 0.f;
 
-    // tile 0 published; its K operands in registers
-    wait_vmcnt<C::LPT * (NS - 2)>();
+    // tile 0 published; its K operands in registers (tile 1's V, and with ROPE
+    // its raw keys, may still be in flight)
+    if (1 < ntiles) {
+        if constexpr (ROPE) wait_vmcnt<C::LPT / 2 + 3 * KRot<D, E>::CPT>();
+        else wait_vmcnt<C::LPT>();
+    } else {
+        wait_vmcnt<0>();
+    }
     ring_barrier();
     KOps<D> kops;
     read_k(kops, rg.k[0], of);
@@ -322,13 +421,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
     // full tiles: branch-free bodies, ring stages as compile-time constants
     for (; n + NS <= nfull; n += NS)
         static_for<NS>([&](auto S) {
-            fwd_step<D, E, S, false, STRIDED>(st, qf, kops, rg, ld, of, x, n + S);
+            fwd_step<D, E, S, false, STRIDED, ROPE>(st, qf, kops, kq, rg, ld, of, x, n + S);
         });
     // the rest (at most NS-1 full tiles, then the diagonal tiles)
     for (; n < ntiles; ++n) {
         const int stg = n % NS;
         static_for<NS>([&](auto S) {
-            if (stg == S) fwd_step<D, E, S, true, STRIDED>(st, qf, kops, rg, ld, of, x, n);
+            if (stg == S) fwd_step<D, E, S, true, STRIDED, ROPE>(st, qf, kops, kq, rg, ld, of, x, n);
         });
     }
     wait_vmcnt<0>();  // no LDS writes may land after this workgroup's LDS is released
@@ -353,33 +452,45 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
 
 // Explicit instantiations: the host pass does not always emit the launch stub of
 // a kernel template with a 16-bit element-type argument on its own.
-#define ATTN_FWD_INST(D_, E_, S_)                                                            \
-    template __global__ void fwd16_kernel<D_, E_, S_>(const f16*, const f16*, const E_*, E_*, \
-                                                      float*, Layout, Layout, int, int, int,  \
-                                                      int, int);
-ATTN_FWD_INST(64, bf16, false) ATTN_FWD_INST(128, bf16, false)
-ATTN_FWD_INST(64, f16, false) ATTN_FWD_INST(128, f16, false)
-ATTN_FWD_INST(64, bf16, true) ATTN_FWD_INST(128, bf16, true)
-ATTN_FWD_INST(64, f16, true) ATTN_FWD_INST(128, f16, true)
+#define ATTN_FWD_INST(D_, E_, S_, R_)                                                            \
+    template __global__ void fwd16_kernel<D_, E_, S_, R_>(                                       \
+        const f16*, const f16*, const E_*, const E_*, const float*, const float*, const E_*, E_*, \
+        float*, Layout, Layout, Layout, int, int, int, int, int);
+#define ATTN_FWD_INST2(D_, E_, S_) ATTN_FWD_INST(D_, E_, S_, false) ATTN_FWD_INST(D_, E_, S_, true)
+ATTN_FWD_INST2(64, bf16, false) ATTN_FWD_INST2(128, bf16, false)
+ATTN_FWD_INST2(64, f16, false) ATTN_FWD_INST2(128, f16, false)
+ATTN_FWD_INST2(64, bf16, true) ATTN_FWD_INST2(128, bf16, true)
+ATTN_FWD_INST2(64, f16, true) ATTN_FWD_INST2(128, f16, true)
+#undef ATTN_FWD_INST2
 #undef ATTN_FWD_INST
+
+template <int D, typename E, bool STRIDED, bool ROPE>
+static void launch_fwd_t(const FwdArgs& a, int nqb, int BH) {
+    using C = FwdTile<D>;
+    const size_t n = (size_t)a.B * a.H * a.T * a.D;
+    const f16* rot = static_cast<const f16*>(a.rot);
+    hipLaunchKernelGGL((fwd16_kernel<D, E, STRIDED, ROPE>), dim3(nqb * BH), dim3(C::NT), 0,
+                       a.stream, rot, rot ? rot + n : nullptr, (const E*)a.q, (const E*)a.k,
+                       a.cs, a.sn, (const E*)a.v, (E*)a.o, a.lse, a.lqkv, a.lqkv, a.lo, a.H, BH,
+                       a.T, nqb, device_cu_count());
+}
+
+// rot non-null: the rotated q, k are there (the rotation pass ran); otherwise
+// the RoPE-on-load instance rotates the caller's q, k
+template <int D, typename E, bool STRIDED>
+static void launch_fwd_s(const FwdArgs& a, int nqb, int BH) {
+    if (a.rot != nullptr) launch_fwd_t<D, E, STRIDED, false>(a, nqb, BH);
+    else launch_fwd_t<D, E, STRIDED, true>(a, nqb, BH);
+}
 
 template <int D, typename E>
 static hipError_t launch_fwd(const FwdArgs& a) {
     using C = FwdTile<D>;
     const int BH = a.B * a.H;
     const int nqb = (a.T + C::BM - 1) / C::BM;
-    const size_t n = (size_t)a.B * a.H * a.T * a.D;
-    const f16* rot = static_cast<const f16*>(a.rot);
     // row pitch D for both means plain [B, H, T, D] (see Layout)
-    const bool strided = a.lqkv.st != a.D || a.lo.st != a.D;
-    if (strided)
-        hipLaunchKernelGGL((fwd16_kernel<D, E, true>), dim3(nqb * BH), dim3(C::NT), 0, a.stream,
-                           rot, rot + n, (const E*)a.v, (E*)a.o, a.lse, a.lqkv, a.lo, a.H, BH,
-                           a.T, nqb, device_cu_count());
-    else
-        hipLaunchKernelGGL((fwd16_kernel<D, E, false>), dim3(nqb * BH), dim3(C::NT), 0, a.stream,
-                           rot, rot + n, (const E*)a.v, (E*)a.o, a.lse, a.lqkv, a.lo, a.H, BH,
-                           a.T, nqb, device_cu_count());
+    if (a.lqkv.st != a.D || a.lo.st != a.D) launch_fwd_s<D, E, true>(a, nqb, BH);
+    else launch_fwd_s<D, E, false>(a, nqb, BH);
     return hipGetLastError();
 }
 

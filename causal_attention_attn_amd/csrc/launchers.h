@@ -34,7 +34,8 @@ inline Layout layout_bthd(int H, int T, int D, int slots) {
 struct FwdArgs {
     const void *q, *k, *v;
     const float *cs, *sn;
-    const void* rot;  // 16-bit path: rotated q * log2(e)/sqrt(D), then rotated k, [B, H, T, D] fp16 each
+    const void* rot;  // 16-bit path, optional: rotated q * log2(e)/sqrt(D), then rotated k,
+                      // [B, H, T, D] fp16 each (null: the forward rotates q and k on load)
     void* o;
     float* lse;
     Layout lqkv;  // q, k, v (the 16-bit path; fp32 takes [B, H, T, D] only)

@@ -69,14 +69,8 @@ __global__ __launch_bounds__(256) void rotate_qk_kernel(const E* __restrict__ q,
     const u32x4 wk = *reinterpret_cast<const u32x4*>(k + src);
     const f32x4 cv = *reinterpret_cast<const f32x4*>(cs + t * (D / 2) + 4 * c);
     const f32x4 sv = *reinterpret_cast<const f32x4*>(sn + t * (D / 2) + 4 * c);
-    u32x4 rq, rk;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const f32x2 qp = unpack2<E>(wq[p]), kp = unpack2<E>(wk[p]);
-        const float q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
-        rq[p] = pack2<f16>((q0 * cv[p] - q1 * sv[p]) * qs, (q0 * sv[p] + q1 * cv[p]) * qs);
-        rk[p] = pack2<f16>(k0 * cv[p] - k1 * sv[p], k0 * sv[p] + k1 * cv[p]);
-    }
+    const u32x4 rq = rope_chunk_f16<E>(wq, cv, sv, qs);
+    const u32x4 rk = rope_chunk_f16<E>(wk, cv, sv, 1.f);
     *reinterpret_cast<u32x4*>(out + dst) = rq;
     *reinterpret_cast<u32x4*>(out + n + dst) = rk;
 }

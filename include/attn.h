@@ -37,7 +37,8 @@
  *   - The caller owns all memory. The library never allocates, frees or
  *     synchronises; work is enqueued on `stream` (a hipStream_t; NULL = the
  *     default stream) and the call returns before the GPU finishes.
- *   - Outputs must not alias inputs; outputs are overwritten, not accumulated.
+ *   - No output may overlap an input or another output (checked on the byte
+ *     ranges each call touches); outputs are overwritten, not accumulated.
  *   - Every failure is reported by the return value. Arguments are validated
  *     before anything is launched; nothing aborts and no exception crosses the
  *     ABI. ATTN_ERR_HIP means a launch failed; attn_last_hip_error() then gives
@@ -62,7 +63,7 @@ enum attn_status {
     ATTN_ERR_ALIGN = 4,      /* a tensor pointer is not 16-byte aligned            */
     ATTN_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required         */
     ATTN_ERR_HIP = 6,        /* a HIP launch failed (see attn_last_hip_error)      */
-    ATTN_ERR_ALIAS = 7,      /* an output pointer equals an input pointer          */
+    ATTN_ERR_ALIAS = 7,      /* an output's bytes overlap an input's or an output's */
     ATTN_ERR_VALUE = 8,      /* a scalar argument (e.g. the RoPE base) is invalid   */
     ATTN_ERR_SAVED = 9       /* the saved rotated q/k buffer is too small           */
 };
@@ -80,61 +81,59 @@ int attn_rope_tables(float* cos_tab, float* sin_tab, int T, int D, double base,
                      void* stream);
 
 /*
- * attn_saved_bytes - size of the "saved" buffer that attn_fwd fills and the
- * backward reads: for the 16-bit path the RoPE-rotated q (times log2(e)/sqrt(D)) and
- * the RoPE-rotated k, each [B,H,T,D] fp16 (4*B*H*T*D bytes, rounded up to 256);
+ * attn_fwd - forward pass. Reads the pre-RoPE q, k and v, and writes
+ * o = softmax(S) v and lse (natural log-sum-exp of each row's scaled, masked
+ * scores; kept for the backward). FlashAttention-style: the T x T score matrix
+ * is never stored ("Show HN: NanoEuler", paragraph 2). RoPE is applied on load
+ * ("Tiny Hackable CUDA", section 3: RoPE on the query and key projections): on
+ * the 16-bit path each query row is rotated (and multiplied by log2(e)/sqrt(D))
+ * in fp32 once, in registers, and every key tile is rotated in fp32 on its way
+ * into on-chip memory; both are rounded once to fp16 for the score products.
+ *   q, k, v   [B,H,T,D] dtype, inputs (q, k not rotated)
+ *   cos_tab, sin_tab  [T,D/2] fp32 from attn_rope_tables (or equal values)
+ *   o         [B,H,T,D] dtype, output
+ *   lse       [B,H,T] fp32, output
+ */
+int attn_fwd(const void* q, const void* k, const void* v,
+             const float* cos_tab, const float* sin_tab,
+             void* o, float* lse,
+             int B, int H, int T, int D, int dtype, void* stream);
+
+/*
+ * attn_saved_bytes - size of the "saved" buffer of attn_fwd_save and
+ * attn_bwd_saved: for the 16-bit path the rotated q times log2(e)/sqrt(D),
+ * then the rotated k, each [B,H,T,D] fp16 (4*B*H*T*D bytes, rounded up to 256);
  * 0 for ATTN_F32, whose kernels rotate on load. Returns 0 for arguments the
  * other calls would reject.
  */
 size_t attn_saved_bytes(int B, int H, int T, int D, int dtype);
 
 /*
- * attn_rotate_qk - apply RoPE once ("Tiny Hackable CUDA", section 3): writes
- * c * R_t q_t, c = log2(e)/sqrt(D), then R_t k_t into `saved` ([2][B,H,T,D]
- * fp16), each value rotated (and scaled) in fp32 and rounded once to fp16. The
- * factor c makes a score product come out as S*log2(e), ready for base-2
- * exponentials. The stored values are no longer bf16 values; fp16's 11-bit
- * significand keeps the score products accurate where the softmax is sharp,
- * and bounds |c R_t q_t| and |R_t k_t| by 65504.
- * For ATTN_F32 it does nothing and returns ATTN_OK.
+ * attn_fwd_save - attn_fwd that also hands the rotated q and k to the
+ * backward, for a training step: the rotation pass (attn_rotate_qk) writes
+ * c * R_t q_t (c = log2(e)/sqrt(D)) and R_t k_t, fp16, into `saved`
+ * ([2][B,H,T,D] fp16, at least attn_saved_bytes() bytes), and the forward
+ * (attn_fwd_rotated) reads them from there; o and lse are bitwise those of
+ * attn_fwd (both form the same rotated values and feed them to the same
+ * arithmetic). Pass the buffer to attn_bwd_saved with the same q and k, and
+ * the backward skips their rotation. The backward needs the rotated values
+ * anyway, so one pass that serves both is cheaper than the on-load rotation
+ * writing them out. ATTN_F32: `saved` is ignored and may be NULL.
  */
-int attn_rotate_qk(const void* q, const void* k, const float* cos_tab, const float* sin_tab,
-                   void* saved, size_t saved_bytes, int B, int H, int T, int D, int dtype,
-                   void* stream);
+int attn_fwd_save(const void* q, const void* k, const void* v,
+                  const float* cos_tab, const float* sin_tab,
+                  void* o, float* lse, void* saved, size_t saved_bytes,
+                  int B, int H, int T, int D, int dtype, void* stream);
 
 /*
- * attn_fwd - forward pass. Reads the pre-RoPE q, k and v, and writes
- * o = softmax(S) v and lse (natural log-sum-exp of each row's scaled, masked
- * scores; saved for the backward). FlashAttention-style: the T x T score
- * matrix is never stored ("Show HN: NanoEuler", paragraph 2).
- *   q, k, v   [B,H,T,D] dtype, inputs
- *   cos_tab, sin_tab  [T,D/2] fp32 from attn_rope_tables (or equal values)
- *   o         [B,H,T,D] dtype, output
- *   lse       [B,H,T] fp32, output
- *   saved     16-bit path: device buffer of attn_saved_bytes(); receives the
- *             rotated q and k (attn_rotate_qk) and must be handed to the
- *             backward. ATTN_F32: ignored, may be NULL.
- * The 16-bit path enqueues attn_rotate_qk then attn_fwd_rotated.
- */
-int attn_fwd(const void* q, const void* k, const void* v,
-             const float* cos_tab, const float* sin_tab,
-             void* o, float* lse, void* saved, size_t saved_bytes,
-             int B, int H, int T, int D, int dtype, void* stream);
-
-/*
- * attn_fwd_rotated - the forward kernel alone (16-bit path only; ATTN_F32 gets
- * ATTN_ERR_DTYPE): o and lse from the rotated q and k already in `saved`
- * (attn_rotate_qk) and from v.
- */
-int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void* o, float* lse,
-                     int B, int H, int T, int D, int dtype, void* stream);
-
-/*
- * attn_bwd_workspace_bytes - device workspace the backward needs: for
- * the 16-bit path -lse_t * log2 e of every row ([B,H,T] fp32) followed by -delta_t
- * of every row ([B,H,T] fp32), 8*B*H*T bytes; for ATTN_F32 delta_t alone
- * (4*B*H*T bytes); rounded up to 256, where delta_t = sum_d dO[t,d] o[t,d].
- * Returns 0 for arguments attn_bwd would reject.
+ * attn_bwd_workspace_bytes - device workspace of attn_bwd, rounded up to 256:
+ * the per-row entries of the pre-pass, that is -lse_t * log2 e then -delta_t
+ * for every row on the 16-bit path (8*B*H*T bytes, rounded up to 256), or
+ * delta_t alone for ATTN_F32 (4*B*H*T), where delta_t = sum_d dO[t,d] o[t,d];
+ * then, on the 16-bit path, room for the rotated q and k (attn_saved_bytes()).
+ * attn_bwd_saved, attn_bwd_prep and attn_bwd_grads use only the per-row part,
+ * and accept a workspace of that size. Returns 0 for arguments attn_bwd would
+ * reject.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype);
 
@@ -143,12 +142,11 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype);
  * respect to the pre-RoPE q, k and v ("Show HN: NanoEuler", paragraph 2: every
  * analytic gradient, RoPE's included, is checked against centred differences).
  * Recompute-based: P is rebuilt from q, k and lse; nothing of size T x T is
- * stored. Enqueues attn_bwd_prep then attn_bwd_grads on `stream`.
- *   q, k, v, o, dO  [B,H,T,D] dtype, inputs (o and lse from attn_fwd); the
- *                   16-bit kernels take the rotated q and k from `saved`
+ * stored. The 16-bit path first rotates this call's q and k into the workspace
+ * (the values attn_fwd_save would have saved), then runs attn_bwd_prep and
+ * attn_bwd_grads on `stream`.
+ *   q, k, v, o, dO  [B,H,T,D] dtype, inputs (o and lse from attn_fwd)
  *   lse             [B,H,T] fp32, input
- *   saved           16-bit path: the buffer attn_fwd filled for these q and k
- *                   (or attn_rotate_qk); ATTN_F32: ignored, may be NULL
  *   dq, dk, dv      [B,H,T,D] dtype, outputs (overwritten)
  *   workspace       device buffer of at least attn_bwd_workspace_bytes()
  * The 16-bit path rounds dS = P (dP - delta) to fp16 for the dq/dk products, so
@@ -157,29 +155,68 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype);
 int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const void* dO, const float* lse,
              const float* cos_tab, const float* sin_tab,
-             const void* saved, size_t saved_bytes,
              void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes,
              int B, int H, int T, int D, int dtype, void* stream);
 
 /*
- * attn_bwd_prep - first stage of attn_bwd, the per-row pre-pass of the
- * recompute-based backward: delta_t = sum_d dO[t,d] o[t,d] (equal to
- * sum_u P[t,u] dP[t,u], the softmax Jacobian term) and, for the 16-bit path,
- * lse_t * log2 e, written to the workspace in the layout of
- * attn_bwd_workspace_bytes. o, dO [B,H,T,D] dtype and lse [B,H,T] fp32 are
- * inputs; the workspace must not alias them.
+ * attn_bwd_saved - attn_bwd without the rotation pass: the 16-bit kernels take
+ * the rotated q and k from `saved`, which must be what attn_fwd_save (or
+ * attn_rotate_qk) wrote for these q and k - a buffer left over from other
+ * inputs gives wrong gradients. q and k are not read on the 16-bit path (they
+ * may be NULL there); ATTN_F32 reads q and k and ignores `saved`. The workspace
+ * needs only the per-row part of attn_bwd_workspace_bytes(). Otherwise as
+ * attn_bwd.
+ */
+int attn_bwd_saved(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse,
+                   const float* cos_tab, const float* sin_tab,
+                   const void* saved, size_t saved_bytes,
+                   void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int H, int T, int D, int dtype, void* stream);
+
+/*
+ * The stages, for callers that schedule them separately (and to time each):
+ *
+ * attn_rotate_qk - RoPE once ("Tiny Hackable CUDA", section 3): writes
+ * c * R_t q_t, c = log2(e)/sqrt(D), then R_t k_t into `saved` ([2][B,H,T,D]
+ * fp16), each value rotated (and scaled) in fp32 and rounded once to fp16 -
+ * bitwise the values the on-load rotation of attn_fwd forms. The factor c makes a score product
+ * come out as S*log2(e), ready for base-2 exponentials. fp16's 11-bit
+ * significand keeps the score products accurate where the softmax is sharp,
+ * and bounds |c R_t q_t| and |R_t k_t| by 65504. ATTN_F32: does nothing.
+ */
+int attn_rotate_qk(const void* q, const void* k, const float* cos_tab, const float* sin_tab,
+                   void* saved, size_t saved_bytes, int B, int H, int T, int D, int dtype,
+                   void* stream);
+
+/*
+ * attn_fwd_rotated - the forward from rotated q and k already in `saved`
+ * (attn_rotate_qk) and from v: the same o and lse as attn_fwd. 16-bit path
+ * only (ATTN_F32 gets ATTN_ERR_DTYPE).
+ */
+int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void* o, float* lse,
+                     int B, int H, int T, int D, int dtype, void* stream);
+
+/*
+ * attn_bwd_prep - the per-row pre-pass of the recompute-based backward:
+ * delta_t = sum_d dO[t,d] o[t,d] (equal to sum_u P[t,u] dP[t,u], the softmax
+ * Jacobian term) and, for the 16-bit path, lse_t * log2 e, written to the
+ * per-row part of the workspace (see attn_bwd_workspace_bytes). o, dO
+ * [B,H,T,D] dtype and lse [B,H,T] fp32 are inputs.
  */
 int attn_bwd_prep(const void* o, const void* dO, const float* lse,
                   void* workspace, size_t workspace_bytes,
                   int B, int H, int T, int D, int dtype, void* stream);
 
 /*
- * attn_bwd_grads - second stage of attn_bwd: writes dq, dk (w.r.t. the pre-RoPE
- * q and k) and dv. Reads the workspace entries of attn_bwd_prep, which must
- * have been enqueued before it on the same stream (or completed) for the same
- * o, dO and lse. Same arguments and rules as attn_bwd, minus o; on the 16-bit path
- * dq and dk/dv come from one launch.
+ * attn_bwd_grads - writes dq, dk (w.r.t. the pre-RoPE q and k) and dv. Reads
+ * the workspace entries of attn_bwd_prep, which must have been enqueued before
+ * it on the same stream (or completed) for the same o, dO and lse. As
+ * attn_bwd_saved, minus o: the 16-bit path takes the rotated q and k from
+ * `saved` only (q and k are not read and may be NULL), and runs dq and dk/dv
+ * in one launch.
  */
 int attn_bwd_grads(const void* q, const void* k, const void* v,
                    const void* dO, const float* lse,
@@ -216,8 +253,11 @@ int attn_bwd_grads(const void* q, const void* k, const void* v,
  *   cos_tab, sin_tab  [T, D/2] fp32 from attn_rope_tables
  *   o         [B, T, H, D] dtype (= [B, T, H*D]), output
  *   lse       [B, H, T] fp32, output
- *   saved     device buffer of attn_saved_bytes(); receives the rotated q and k
- * Enqueues the rotation pass and the forward kernel.
+ *   saved     NULL, or a device buffer of attn_saved_bytes() that receives the
+ *             rotated q and k (as attn_fwd_save)
+ * Without saved: one launch of the forward kernel with RoPE on load (as
+ * attn_fwd); with it: the rotation pass, then the forward from its output (as
+ * attn_fwd_save).
  */
 int attn_fwd_packed(const void* qkv, const float* cos_tab, const float* sin_tab,
                     void* o, float* lse, void* saved, size_t saved_bytes,
@@ -230,11 +270,13 @@ int attn_fwd_packed(const void* qkv, const float* cos_tab, const float* sin_tab,
  *   qkv       [B, T, 3, H, D] dtype, the forward's input (v is read from it)
  *   o, dO     [B, T, H, D] dtype, inputs (o and lse from attn_fwd_packed)
  *   lse       [B, H, T] fp32, input
- *   saved     the buffer attn_fwd_packed filled
+ *   saved     the buffer attn_fwd_packed filled for this qkv, or NULL: then
+ *             the rotated q and k are formed again, in the workspace
  *   dqkv      [B, T, 3, H, D] dtype, output (overwritten): dq, dk, dv slots
- *   workspace device buffer of at least attn_bwd_workspace_bytes()
- * Enqueues the pre-pass and the gradient kernel; the |dS| bound of attn_bwd
- * applies.
+ *   workspace device buffer of at least attn_bwd_workspace_bytes() (the
+ *             per-row part suffices when saved is given)
+ * Enqueues (without saved) the rotation pass, then the pre-pass and the
+ * gradient kernel; the |dS| bound of attn_bwd applies.
  */
 int attn_bwd_packed(const void* qkv, const void* o, const void* dO, const float* lse,
                     const float* cos_tab, const float* sin_tab,

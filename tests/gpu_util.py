@@ -14,14 +14,39 @@ TOL = {"bf16": dict(max_abs=2e-2, rel_l2=1e-2), "f16": dict(max_abs=2e-2, rel_l2
        "f32": dict(max_abs=1e-4, rel_l2=1e-5)}
 
 
-def gpu_run(x, base=10000.0):
-    """x: dict of CPU tensors q, k, v, do. Returns dict of CPU tensors o, lse, dq, dk, dv."""
+# the ways through the C ABI that the parity tests exercise:
+#   "saved"   attn_fwd_save + attn_bwd_saved (the training pair the benchmark times)
+#   "plain"   attn_fwd + attn_bwd (the backward rotates q and k itself)
+#   "rotated" attn_rotate_qk + attn_fwd_rotated, then attn_bwd_saved on that buffer
+PATHS = ("saved", "plain", "rotated")
+
+
+def gpu_run(x, base=10000.0, path="saved"):
+    """x: dict of CPU tensors q, k, v, do. Returns dict of CPU tensors o, lse, dq,
+    dk, dv (and `saved`, the rotated q, k buffer, for the saved and rotated paths
+    of a 16-bit dtype)."""
     dev = torch.device("cuda", 0)
     g = {n: t.to(dev) for n, t in x.items()}
-    o, lse, saved = attn.forward(g["q"], g["k"], g["v"], base=base)
-    dq, dk, dv = attn.backward(g["q"], g["k"], g["v"], o, g["do"], lse, saved, base=base)
+    q, k, v, do = g["q"], g["k"], g["v"], g["do"]
+    saved = None
+    if path == "rotated" and q.dtype != torch.float32:
+        B, H, T, D = q.shape
+        dt = attn.api._dtype_code(q)
+        cs, sn = attn.rope_tables(T, D, base, dev)
+        ns = attn.attn_saved_bytes(B, H, T, D, dt)
+        saved = torch.empty(ns, dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        attn.attn_rotate_qk(q, k, cs, sn, saved, ns, B, H, T, D, dt)
+        attn.attn_fwd_rotated(saved, ns, v, o, lse, B, H, T, D, dt)
+    else:
+        o, lse, saved = attn.forward(q, k, v, base=base, save=(path != "plain"))
+    dq, dk, dv = attn.backward(q, k, v, o, do, lse, saved, base=base)
     torch.cuda.synchronize()
-    return {n: t.cpu() for n, t in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv).items()}
+    out = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+    if saved is not None:
+        out["saved"] = saved
+    return {n: t.cpu() for n, t in out.items()}
 
 
 def oracle_run(x, base=10000.0, heads=None):
@@ -36,7 +61,7 @@ def oracle_run(x, base=10000.0, heads=None):
 
 def select_heads(out, heads):
     return {n: np.stack([workloads.as_float64(t)[b, h] for b, h in heads])[None]
-            for n, t in out.items()}
+            for n, t in out.items() if n != "saved"}
 
 
 def errors(got, ref):
@@ -77,12 +102,14 @@ def to_packed(x, dev):
     return qkv.to(dev), x["do"].permute(0, 2, 1, 3).contiguous().to(dev)
 
 
-def gpu_run_packed(x, base=10000.0):
-    """The packed entry points on the same values as gpu_run; outputs come back
-    in [B, H, T, D] (lse [B, H, T]) as CPU tensors."""
+def gpu_run_packed(x, base=10000.0, save=True):
+    """The packed entry points on the same values as gpu_run (save: the forward
+    writes the rotated q, k and the backward reads them; otherwise the backward
+    forms them again); outputs come back in [B, H, T, D] (lse [B, H, T]) as CPU
+    tensors."""
     dev = torch.device("cuda", 0)
     qkv, do = to_packed(x, dev)
-    o, lse, saved = attn.forward_packed(qkv, base=base)
+    o, lse, saved = attn.forward_packed(qkv, base=base, save=save)
     dqkv = attn.backward_packed(qkv, o, do, lse, saved, base=base)
     torch.cuda.synchronize()
     bhtd = lambda t: t.permute(0, 2, 1, 3).contiguous().cpu()

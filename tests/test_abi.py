@@ -13,11 +13,15 @@ from causal_attention_attn_amd import _lib
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                       "include", "attn.h")
 
-# a fake, 16-byte aligned, non-null address; every call below fails validation
-# before any launch, so it is never dereferenced
-FAKE = 0x100000
+# fake, 16-byte aligned, non-null addresses 1 MiB apart (far more than any
+# buffer below needs, so they overlap only where a test plants an overlap);
+# every call below fails validation before any launch, so none is dereferenced
+FAKE = 0x10000000
 MIS = FAKE + 4
 
+
+def A(i, off=0):
+    return FAKE + (i << 20) + off
 
 @pytest.fixture(scope="module")
 def lib():
@@ -35,7 +39,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_fwd_rotated", "attn_rotate_qk", "attn_saved_bytes", "attn_bwd",
+    for n in ("attn_fwd", "attn_fwd_save", "attn_fwd_rotated", "attn_rotate_qk",
+              "attn_saved_bytes", "attn_bwd", "attn_bwd_saved",
               "attn_bwd_prep", "attn_bwd_grads", "attn_rope_tables", "attn_bwd_workspace_bytes",
               "attn_fwd_packed", "attn_bwd_packed", "attn_kv_cache_bytes", "attn_kv_append",
               "attn_decode_workspace_bytes", "attn_decode", "attn_decode_step", "attn_rmsnorm_fwd",
@@ -59,9 +64,12 @@ def test_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    assert attn.attn_bwd_workspace_bytes(8, 12, 1024, 64, 0) == 8 * 8 * 12 * 1024
+    # per-row entries (two fp32 per row, rounded up to 256), then room for the
+    # rotated q and k on the 16-bit path
+    assert attn.attn_bwd_workspace_bytes(8, 12, 1024, 64, 0) == 8 * 8 * 12 * 1024 + 4 * 8 * 12 * 1024 * 64
     assert attn.attn_bwd_workspace_bytes(8, 12, 1024, 64, 1) == 4 * 8 * 12 * 1024
-    assert attn.attn_bwd_workspace_bytes(1, 1, 3, 64, 0) == 256
+    assert attn.attn_bwd_workspace_bytes(1, 1, 3, 64, 0) == 256 + 768
+    assert attn.attn_bwd_workspace_bytes(1, 1, 3, 64, 2) == 256 + 768
     assert attn.attn_saved_bytes(8, 12, 1024, 64, 0) == 4 * 8 * 12 * 1024 * 64
     assert attn.attn_saved_bytes(8, 12, 1024, 64, 1) == 0
     assert attn.attn_saved_bytes(1, 1, 3, 96, 0) == 0
@@ -76,9 +84,13 @@ def status_of(fn, *args):
     return e.value.status
 
 
+# B=1, H=1, T=8, D=64 bf16: 1 KiB per [B,H,T,D] tensor, 32 B of lse, 1 KiB per
+# table, a 2 KiB saved buffer, 256 B of per-row workspace entries
+X, ROW, TAB, SAVED, WROWS = 1024, 32, 1024, 2048, 256
+
+
 def fwd_args(**over):
-    a = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, cos_tab=FAKE + 48, sin_tab=FAKE + 64,
-             o=FAKE + 80, lse=FAKE + 96, saved=FAKE + 112, saved_bytes=4 * 8 * 64,
+    a = dict(q=A(0), k=A(1), v=A(2), cos_tab=A(3), sin_tab=A(4), o=A(5), lse=A(6),
              B=1, H=1, T=8, D=64, dtype=0, stream=0)
     a.update(over)
     return a
@@ -95,54 +107,90 @@ def test_fwd_rejects_bad_arguments(lib):
     assert f(B=1 << 16, H=1 << 10, T=1 << 10) == 2      # 2^42 elements
     assert f(dtype=3) == 3
     assert f(k=MIS) == 4
-    assert f(o=FAKE) == 7                                 # o aliases q
-    assert f(lse=FAKE + 32) == 7                          # lse aliases v
+    assert f(o=A(0)) == 7                                 # o is q
+    assert f(o=A(0, X - 16)) == 7                         # o's first row overlaps q's last bytes
+    assert f(lse=A(2, 512)) == 7                          # lse inside v
+    assert f(o=A(3, -X + 16)) == 7                        # o's tail runs into the cos table
+
+
+def test_adjacent_buffers_are_not_aliases(lib):
+    # o ends exactly where lse starts and q ends exactly where o starts: no byte is
+    # shared, so validation passes the alias check and fails on the next argument
+    f = lambda **o: status_of(lambda: attn.attn_fwd_save(**{**fwd_args(), **o}))
+    assert f(o=A(0, X), lse=A(0, 2 * X), saved=A(7), saved_bytes=SAVED - 256) == 9
+
+
+def test_fwd_save_rejects_bad_arguments(lib):
+    base = fwd_args(saved=A(7), saved_bytes=SAVED)
+    f = lambda **o: status_of(lambda: attn.attn_fwd_save(**{**base, **o}))
     assert f(saved=0) == 1                                # bf16 needs the saved buffer
     assert f(saved=MIS) == 4
-    assert f(saved_bytes=4 * 8 * 64 - 1) == 9
-    assert f(saved=FAKE + 16) == 7                        # saved aliases k
+    assert f(saved_bytes=SAVED - 1) == 9
+    assert f(saved=A(1, 256)) == 7                        # saved overlaps k
+    assert f(saved=A(6, -SAVED + 16)) == 7                # saved runs into lse
+    assert f(o=A(7, 1008)) == 7                           # o inside saved
+    assert f(v=0) == 1
 
 
 def test_fwd_rotated_and_rotate_reject_bad_arguments(lib):
     f = lambda **o: status_of(lambda: attn.attn_fwd_rotated(
-        **{**dict(saved=FAKE, saved_bytes=4 * 8 * 64, v=FAKE + 16, o=FAKE + 32, lse=FAKE + 48,
+        **{**dict(saved=A(0), saved_bytes=SAVED, v=A(1), o=A(2), lse=A(3),
                   B=1, H=1, T=8, D=64, dtype=0, stream=0), **o}))
     assert f(dtype=1) == 3                                # fp32 has no rotated path
     assert f(saved=0) == 1
     assert f(saved_bytes=100) == 9
-    assert f(o=FAKE) == 7
+    assert f(o=A(0, 1024)) == 7                           # o inside saved
     g = lambda **o: status_of(lambda: attn.attn_rotate_qk(
-        **{**dict(q=FAKE, k=FAKE + 16, cos_tab=FAKE + 32, sin_tab=FAKE + 48, saved=FAKE + 64,
-                  saved_bytes=4 * 8 * 64, B=1, H=1, T=8, D=64, dtype=0, stream=0), **o}))
+        **{**dict(q=A(0), k=A(1), cos_tab=A(2), sin_tab=A(3), saved=A(4),
+                  saved_bytes=SAVED, B=1, H=1, T=8, D=64, dtype=0, stream=0), **o}))
     assert g(q=0) == 1
     assert g(saved_bytes=0) == 9
-    assert g(saved=FAKE) == 7
+    assert g(saved=A(0, 16)) == 7                         # saved overlaps q
     assert g(D=48) == 2
 
 
+def bwd_base(**over):
+    a = dict(q=A(0), k=A(1), v=A(2), o=A(3), dO=A(4), lse=A(5), cos_tab=A(6), sin_tab=A(7),
+             dq=A(8), dk=A(9), dv=A(10), workspace=A(11), workspace_bytes=WROWS + SAVED,
+             B=1, H=1, T=8, D=64, dtype=0, stream=0)
+    a.update(over)
+    return a
+
+
 def test_bwd_rejects_bad_arguments(lib):
-    base = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, o=FAKE + 48, dO=FAKE + 64, lse=FAKE + 80,
-                cos_tab=FAKE + 96, sin_tab=FAKE + 112, saved=FAKE + 192, saved_bytes=4 * 8 * 64,
-                dq=FAKE + 128, dk=FAKE + 144, dv=FAKE + 160, workspace=FAKE + 176,
-                workspace_bytes=256, B=1, H=1, T=8, D=64, dtype=0, stream=0)
-    f = lambda **o: status_of(lambda: attn.attn_bwd(**{**base, **o}))
+    f = lambda **o: status_of(lambda: attn.attn_bwd(**bwd_base(**o)))
     assert f(dO=0) == 1
+    assert f(q=0) == 1                                    # attn_bwd reads q and k itself
     assert f(D=100) == 2
     assert f(dtype=-1) == 3
     assert f(dq=MIS) == 4
     assert f(workspace=0) == 5
-    assert f(workspace_bytes=255) == 5
-    assert f(dk=FAKE) == 7
-    assert f(dv=FAKE + 144) == 7                          # dv aliases dk
-    assert f(workspace=FAKE + 80) == 7                    # workspace aliases lse
+    assert f(workspace_bytes=WROWS + SAVED - 1) == 5      # room for the rotated q, k too
+    assert f(dk=A(0)) == 7
+    assert f(dv=A(9, 512)) == 7                           # dv overlaps dk
+    assert f(workspace=A(5, 16)) == 7                     # workspace overlaps lse
+    assert f(workspace=A(10, X - 256)) == 7               # workspace starts in dv's last row
+    assert f(dq=A(11, WROWS + 1024)) == 7                 # dq inside the workspace's q, k part
+
+
+def test_bwd_saved_rejects_bad_arguments(lib):
+    base = bwd_base(saved=A(12), saved_bytes=SAVED, workspace_bytes=WROWS)
+    f = lambda **o: status_of(lambda: attn.attn_bwd_saved(**{**base, **o}))
     assert f(saved=0) == 1
     assert f(saved_bytes=8) == 9
-    assert f(dq=FAKE + 192) == 7                          # dq aliases saved
+    assert f(workspace_bytes=WROWS - 1) == 5              # the per-row part suffices
+    assert f(dq=A(12, 64)) == 7                           # dq overlaps saved
+    assert f(workspace=A(12, SAVED - 16)) == 7            # workspace overlaps saved's end
+    assert f(v=0) == 1
+    # the 16-bit path takes the rotated q, k from saved: q and k may be NULL there,
+    # and are then required for fp32 (which rotates on load)
+    assert f(q=0, k=0, dq=A(8, 1)) == 4                   # got past q, k to dq's alignment
+    assert f(q=0, dtype=1, workspace_bytes=256) == 1
 
 
 def test_bwd_stages_reject_bad_arguments(lib):
     f = lambda **o: status_of(lambda: attn.attn_bwd_prep(
-        **{**dict(o=FAKE, dO=FAKE + 16, lse=FAKE + 32, workspace=FAKE + 48, workspace_bytes=256,
+        **{**dict(o=A(0), dO=A(1), lse=A(2), workspace=A(3), workspace_bytes=WROWS,
                   B=1, H=1, T=8, D=64, dtype=0, stream=0), **o}))
     assert f(o=0) == 1
     assert f(lse=0) == 1
@@ -150,42 +198,41 @@ def test_bwd_stages_reject_bad_arguments(lib):
     assert f(dtype=5) == 3
     assert f(dO=MIS) == 4
     assert f(workspace=0) == 5
-    assert f(workspace_bytes=255) == 5
+    assert f(workspace_bytes=WROWS - 1) == 5
     assert f(workspace=MIS) == 4
-    assert f(workspace=FAKE + 16) == 7                   # workspace aliases dO
-    base = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, dO=FAKE + 64, lse=FAKE + 80,
-                cos_tab=FAKE + 96, sin_tab=FAKE + 112, saved=FAKE + 192, saved_bytes=4 * 8 * 64,
-                dq=FAKE + 128, dk=FAKE + 144, dv=FAKE + 160, workspace=FAKE + 176,
-                workspace_bytes=256, B=1, H=1, T=8, D=64, dtype=0, stream=0)
+    assert f(workspace=A(1, 1008)) == 7                   # workspace overlaps dO's last row
+    base = dict(q=A(0), k=A(1), v=A(2), dO=A(4), lse=A(5), cos_tab=A(6), sin_tab=A(7),
+                saved=A(12), saved_bytes=SAVED, dq=A(8), dk=A(9), dv=A(10), workspace=A(11),
+                workspace_bytes=WROWS, B=1, H=1, T=8, D=64, dtype=0, stream=0)
     g = lambda **o: status_of(lambda: attn.attn_bwd_grads(**{**base, **o}))
     assert g(dq=0) == 1
     assert g(saved=0) == 1
     assert g(saved_bytes=8) == 9
     assert g(workspace=0) == 5
-    assert g(dv=FAKE + 32) == 7                           # dv aliases v
-    assert g(dk=FAKE + 128) == 7                          # dk aliases dq
-    assert g(dq=FAKE + 176) == 7                          # dq aliases the workspace
+    assert g(dv=A(2)) == 7                                # dv is v
+    assert g(dk=A(8, 512)) == 7                           # dk overlaps dq
+    assert g(dq=A(11, 128)) == 7                          # dq overlaps the workspace
 
 
 def test_packed_entry_points_reject_bad_arguments(lib):
-    fb = dict(qkv=FAKE, cos_tab=FAKE + 16, sin_tab=FAKE + 32, o=FAKE + 48, lse=FAKE + 64,
-              saved=FAKE + 80, saved_bytes=4 * 8 * 64, B=1, H=1, T=8, D=64, dtype=0, stream=0)
+    # the packed tensor is 3 KiB here
+    fb = dict(qkv=A(0), cos_tab=A(1), sin_tab=A(2), o=A(3), lse=A(4), saved=A(5),
+              saved_bytes=SAVED, B=1, H=1, T=8, D=64, dtype=0, stream=0)
     f = lambda **o: status_of(lambda: attn.attn_fwd_packed(**{**fb, **o}))
     assert f(qkv=0) == 1
-    assert f(saved=0) == 1
     assert f(D=96) == 2
     assert f(dtype=1) == 3                                # fp32 has no packed path
     assert f(dtype=7) == 3
     assert f(o=MIS) == 4
     assert f(saved_bytes=16) == 9
-    assert f(o=FAKE) == 7                                 # o aliases qkv
-    assert f(saved=FAKE + 32) == 7                        # saved aliases a table
+    assert f(o=A(0, 2048)) == 7                           # o inside qkv's third kilobyte
+    assert f(saved=A(1, 512)) == 7                        # saved overlaps a table
     # the packed tensor (3*B*H*T*D elements) must stay below 2^31 elements
     assert f(B=1, H=16, T=1 << 19, D=128, saved_bytes=1 << 40) == 2   # 3 * 2^30 elements
     assert f(B=1, H=1 << 16, T=1, D=64, saved_bytes=1 << 40) == 2     # a token row of 3 * 2^22
-    bb = dict(qkv=FAKE, o=FAKE + 16, dO=FAKE + 32, lse=FAKE + 48, cos_tab=FAKE + 64,
-              sin_tab=FAKE + 80, saved=FAKE + 96, saved_bytes=4 * 8 * 64, dqkv=FAKE + 112,
-              workspace=FAKE + 128, workspace_bytes=256, B=1, H=1, T=8, D=64, dtype=0, stream=0)
+    bb = dict(qkv=A(0), o=A(1), dO=A(2), lse=A(3), cos_tab=A(4), sin_tab=A(5), saved=A(6),
+              saved_bytes=SAVED, dqkv=A(7), workspace=A(8), workspace_bytes=WROWS, B=1, H=1,
+              T=8, D=64, dtype=0, stream=0)
     g = lambda **o: status_of(lambda: attn.attn_bwd_packed(**{**bb, **o}))
     assert g(dqkv=0) == 1
     assert g(dO=0) == 1
@@ -193,11 +240,12 @@ def test_packed_entry_points_reject_bad_arguments(lib):
     assert g(T=0) == 2
     assert g(dqkv=MIS) == 4
     assert g(workspace=0) == 5
-    assert g(workspace_bytes=255) == 5
+    assert g(workspace_bytes=WROWS - 1) == 5
+    assert g(saved=0) == 5                                # without saved: room for q, k needed
     assert g(saved_bytes=8) == 9
-    assert g(dqkv=FAKE) == 7                              # dqkv aliases qkv
-    assert g(workspace=FAKE + 112) == 7                   # workspace aliases dqkv
-    assert g(dqkv=FAKE + 96) == 7                         # dqkv aliases saved
+    assert g(dqkv=A(0, 1024)) == 7                        # dqkv overlaps qkv
+    assert g(workspace=A(7, 3008)) == 7                   # workspace overlaps dqkv's end
+    assert g(dqkv=A(6, 16)) == 7                          # dqkv overlaps saved
 
 
 def test_decode_sizes(lib):

@@ -28,12 +28,14 @@ HALF = {"bf16": workloads.HEADLINE, "f16": "gpt2s_f16_b8h12t1024d64"}
 SHAPES = [(1, 1, 1), (2, 1, 65), (1, 3, 127), (1, 2, 200), (2, 2, 333)]
 
 
+@pytest.mark.parametrize("save", [True, False])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("B,H,T", SHAPES)
-def test_packed_small_shapes(B, H, T, D, dtype):
+def test_packed_small_shapes(B, H, T, D, dtype, save):
+    """With a saved buffer, and without one (the backward rotates q, k itself)."""
     x = workloads.make(workloads.WORKLOADS[HALF[dtype]], seed=T + D + 1, shape=(B, H, T, D))
-    got = gpu_run_packed(x)
+    got = gpu_run_packed(x, save=save)
     assert_close(got, oracle_run(x), dtype, f"packed {dtype} B{B} H{H} T{T} D{D}")
     ref = gpu_run(x)
     for n in ("o", "lse", "dq", "dk", "dv"):

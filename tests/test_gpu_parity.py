@@ -10,7 +10,8 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from tests.gpu_util import assert_close, gpu_run, oracle_run, select_heads
+    import causal_attention_attn_amd as attn
+    from tests.gpu_util import assert_close, gpu_run, oracle_run
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -58,23 +59,55 @@ def test_peaky_logits_small():
     assert_close(gpu_run(x), oracle_run(x), "bf16", "peaky small")
 
 
-FULL = [
-    ("gpt2s_bf16_b8h12t1024d64", [(0, 0), (3, 7), (7, 11)]),
-    ("gpt2s_f16_b8h12t1024d64", [(0, 0), (7, 11)]),
-    ("longctx_bf16_b2h12t4096d64", [(0, 0), (1, 11)]),
-    ("peaky_bf16_b16h12t2048d64", [(0, 0), (15, 11)]),
-    ("wide_bf16_b1h6t8192d128", [(0, 5)]),
-]
+FULL = ["gpt2s_bf16_b8h12t1024d64", "gpt2s_f16_b8h12t1024d64", "longctx_bf16_b2h12t4096d64",
+        "peaky_bf16_b16h12t2048d64", "wide_bf16_b1h6t8192d128"]
 
 
-@pytest.mark.parametrize("name,heads", FULL)
-def test_full_size_workloads_on_sampled_heads(name, heads):
-    """Full-size launch (the benchmark's configuration); the oracle checks whole
-    heads, which are independent of each other."""
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workloads_all_heads(name):
+    """Full-size launch in the benchmark's configuration (the saved path), every
+    output element of every head against the oracle."""
     w = workloads.WORKLOADS[name]
     x = workloads.make(w)
     got = gpu_run(x)
-    assert_close(select_heads(got, heads), oracle_run(x, heads=heads), w.dtype, name)
+    print(f"{name}: GPU done, oracle on all {w.B * w.H} heads", flush=True)
+    assert_close(got, oracle_run(x), w.dtype, name)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 2, 63), (2, 1, 65), (1, 3, 127), (1, 2, 200),
+                                   (2, 2, 333)])
+def test_paths_agree_bitwise(B, H, T, D, dtype):
+    """attn_fwd + attn_bwd (q, k rotated by the backward itself), attn_fwd_save +
+    attn_bwd_saved, and the rotation pass + attn_fwd_rotated give bitwise the same
+    outputs; the forward's saved buffer is bitwise the rotation pass's output."""
+    x = workloads.make(workloads.WORKLOADS[HALF[dtype]], seed=T + D + 3, shape=(B, H, T, D))
+    runs = {p: gpu_run(x, path=p) for p in ("saved", "plain", "rotated")}
+    for p in ("plain", "rotated"):
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            assert torch.equal(runs[p][n], runs["saved"][n]), (p, n)
+    n = B * H * T * D * 2  # bytes of rotated q, then of rotated k
+    for part in (slice(0, n), slice(n, 2 * n)):
+        assert torch.equal(runs["rotated"]["saved"][part], runs["saved"]["saved"][part])
+
+
+def test_backward_reads_its_own_q_and_k():
+    """attn_bwd rotates the q, k it is given; attn_bwd_saved trusts its buffer:
+    handed the rotated values of other inputs, it gives other gradients."""
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    x = workloads.make(w, seed=21, shape=(1, 2, 150, 64))
+    y = workloads.make(w, seed=22, shape=(1, 2, 150, 64))
+    ref = oracle_run(x)
+    dev = torch.device("cuda", 0)
+    g = {n: t.to(dev) for n, t in x.items()}
+    o, lse, _ = attn.forward(g["q"], g["k"], g["v"], save=False)
+    _, _, stale = attn.forward(y["q"].to(dev), y["k"].to(dev), y["v"].to(dev))
+    dq, dk, dv = attn.backward(g["q"], g["k"], g["v"], o, g["do"], lse, None)
+    got = dict(o=o.cpu(), lse=lse.cpu(), dq=dq.cpu(), dk=dk.cpu(), dv=dv.cpu())
+    assert_close(got, ref, "bf16", "attn_bwd from its own q, k")
+    dq2, _, _ = attn.backward(g["q"], g["k"], g["v"], o, g["do"], lse, stale)
+    assert not torch.equal(dq2.cpu(), got["dq"])
 
 
 def test_row_zero_is_v_zero_bitwise():
@@ -137,7 +170,6 @@ def test_rope_table_kernel():
 
 
 def test_abi_errors_on_gpu():
-    import causal_attention_attn_amd as attn
     q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="cuda")
     cs, sn = attn.rope_tables(8, 64, 10000.0, "cuda:0")
     o = torch.empty_like(q)
@@ -145,11 +177,13 @@ def test_abi_errors_on_gpu():
     ns = attn.attn_saved_bytes(1, 1, 8, 64, attn.ATTN_BF16)
     saved = torch.empty(ns, dtype=torch.uint8, device="cuda")
     with pytest.raises(attn.AttnError):
-        attn.attn_fwd(q, q, q, cs, sn, o, lse, saved, ns, 1, 1, 8, 96, attn.ATTN_BF16)
+        attn.attn_fwd(q, q, q, cs, sn, o, lse, 1, 1, 8, 96, attn.ATTN_BF16)
     with pytest.raises(attn.AttnError):
-        attn.attn_fwd(q, q, q, cs, sn, q, lse, saved, ns, 1, 1, 8, 64, attn.ATTN_BF16)
+        attn.attn_fwd(q, q, q, cs, sn, q, lse, 1, 1, 8, 64, attn.ATTN_BF16)
     with pytest.raises(attn.AttnError):
-        attn.attn_fwd(q, q, q, cs, sn, o, lse, saved, ns - 256, 1, 1, 8, 64, attn.ATTN_BF16)
-    attn.attn_fwd(q, q, q, cs, sn, o, lse, saved, ns, 1, 1, 8, 64, attn.ATTN_BF16)
+        attn.attn_fwd_save(q, q, q, cs, sn, o, lse, saved, ns - 256, 1, 1, 8, 64, attn.ATTN_BF16)
+    with pytest.raises(ValueError):  # the binding checks lse before any launch
+        attn.backward(q, q, q, o, q, lse[:, :, :4], saved)
+    attn.attn_fwd(q, q, q, cs, sn, o, lse, 1, 1, 8, 64, attn.ATTN_BF16)
     torch.cuda.synchronize()
     assert torch.all(o == 0)

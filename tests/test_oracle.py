@@ -222,6 +222,32 @@ def test_brute_force(T, D):
         np.testing.assert_allclose(a[0, 0], b, rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("T,D", [(1, 2), (3, 4), (5, 8), (8, 8)])
+def test_probabilities_match_brute_force(T, D):
+    """The full probability matrix against the scalar implementation's P (its own
+    rotation, scale and key-by-key softmax), masked entries included."""
+    q, k = rand((2, 1, T, D), 110 + T), rand((2, 1, T, D), 111 + T)
+    P = oracle.attention_probabilities(q, k)
+    for b in range(2):
+        _, _, bP = brute_force.head_forward(q[b, 0].tolist(), k[b, 0].tolist(),
+                                            k[b, 0].tolist())
+        np.testing.assert_allclose(P[b, 0], np.array(bP), rtol=1e-12, atol=1e-15)
+
+
+def test_probabilities_times_values_is_the_forward():
+    """P V equals the forward's output (the forward does not go through
+    attention_probabilities), and exp(S - lse) rebuilds P from the forward's lse."""
+    q, k, v = (rand((1, 2, 11, 8), 120 + s) for s in range(3))
+    P = oracle.attention_probabilities(q, k)
+    o, lse = oracle.attention_forward(q, k, v)
+    np.testing.assert_allclose(P @ v, o, rtol=1e-12, atol=1e-13)
+    qr, kr = oracle.rope(q), oracle.rope(k)
+    S = (qr @ np.swapaxes(kr, -1, -2)) / np.sqrt(8.0)
+    mask = np.triu(np.ones((11, 11), bool), 1)
+    rebuilt = np.where(mask, 0.0, np.exp(S - lse[..., None]))
+    np.testing.assert_allclose(P, rebuilt, rtol=1e-12, atol=1e-15)
+
+
 def test_torch_sdpa_float64_cross_check():
     torch = pytest.importorskip("torch")
     B, H, T, D = 2, 3, 45, 16
