@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     AttnError,
     attn_bwd,
     attn_bwd_saved,
+    attn_bwd_saved_noalloc,
     attn_bwd_grads,
     attn_bwd_packed,
     attn_bwd_prep,
@@ -27,6 +28,7 @@ from ._lib import (  # noqa: F401
     attn_kv_append,
     attn_kv_cache_bytes,
     attn_last_hip_error,
+    attn_noalloc_scratch_bytes,
     attn_rmsnorm_bwd,
     attn_rmsnorm_bwd_workspace_bytes,
     attn_rmsnorm_fwd,

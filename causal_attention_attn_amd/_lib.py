@@ -20,7 +20,7 @@ ATTN_F16 = 2
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
     4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_ALIAS",
-    8: "ATTN_ERR_VALUE", 9: "ATTN_ERR_SAVED",
+    8: "ATTN_ERR_VALUE", 9: "ATTN_ERR_SAVED", 10: "ATTN_ERR_SCRATCH",
 }
 
 _P = ctypes.c_void_p
@@ -55,6 +55,9 @@ _SIGS = {
     "attn_rmsnorm_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _P]),
     "attn_swiglu_fwd": (_I, [_P, _P, _I, _I, _I, _P]),
     "attn_swiglu_bwd": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "attn_bwd_saved_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P,
+                                    _I, _I, _I, _I, _I, _P]),
+    "attn_noalloc_scratch_bytes": (_Z, []),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
 }
@@ -236,6 +239,17 @@ def attn_swiglu_fwd(u, out, N, F, dtype, stream=None):
 
 def attn_swiglu_bwd(u, dout, du, N, F, dtype, stream=None):
     _call("attn_swiglu_bwd", _ptr(u), _ptr(dout), _ptr(du), N, F, dtype, _stream(stream))
+
+
+def attn_bwd_saved_noalloc(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, dk,
+                           dv, B, H, T, D, dtype, stream=None):
+    _call("attn_bwd_saved_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+          _ptr(cos_tab), _ptr(sin_tab), _ptr(saved), int(saved_bytes), _ptr(dq), _ptr(dk),
+          _ptr(dv), B, H, T, D, dtype, _stream(stream))
+
+
+def attn_noalloc_scratch_bytes():
+    return int(load().attn_noalloc_scratch_bytes())
 
 
 def attn_status_string(status):

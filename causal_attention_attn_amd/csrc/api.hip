@@ -491,11 +491,94 @@ const char* attn_status_string(int status) {
         case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
         case ATTN_ERR_VALUE: return "invalid scalar argument";
         case ATTN_ERR_SAVED: return "saved rotated q/k buffer too small";
+        case ATTN_ERR_SCRATCH: return "too large for the library's static scratch";
         default: return "unknown status";
     }
 }
 
 int attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"
+
+// ---- the backward of a training step without a workspace argument ----
+//
+// attn_bwd_saved_noalloc is attn_bwd_saved for callers that cannot allocate (code
+// under graph capture, tight serving loops): the pre-pass's per-row entries go to
+// `scratch`, a file-scope device array the library owns, instead of a workspace
+// the caller passes. Each GPU the library runs on holds its own copy until the
+// process ends; every call on a GPU overwrites that GPU's copy, so calls that
+// overlap on one GPU (other streams, other threads) race.
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64] = {};
+
+// The device address of the current device's copy of `scratch`. In host code the
+// array's name stands for a host-side symbol, not device memory, so every use
+// takes this address; it is looked up once per device, with that device current.
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= 64) return ATTN_ERR_VALUE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (p == nullptr) return ATTN_ERR_HIP;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int attn_bwd_saved_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const void* dO, const float* lse, const float* cos_tab,
+                           const float* sin_tab, const void* saved, size_t saved_bytes,
+                           void* dq, void* dk, void* dv, int B, int H, int T, int D, int dtype,
+                           void* stream) {
+    int st = check_shape(B, H, T, D, dtype);
+    if (st) return st;
+    st = dtype == ATTN_F32 ? check_ptrs({q, k, v, o, dO, lse, cos_tab, sin_tab, dq, dk, dv})
+                           : check_ptrs({v, o, dO, lse, cos_tab, sin_tab, dq, dk, dv});
+    if (st) return st;
+    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+    if (st) return st;
+    if (rows_need(B, H, T, dtype) > kScratchBytes) return ATTN_ERR_SCRATCH;
+    const Sizes z(B, H, T, D, dtype);
+    const Span sv = {dtype == ATTN_F32 ? nullptr : saved, saved_need(B, H, T, D, dtype)};
+    if (any_alias({{dq, z.x}, {dk, z.x}, {dv, z.x}},
+                  {{q, z.x}, {k, z.x}, {v, z.x}, {o, z.x}, {dO, z.x}, {lse, z.row},
+                   {cos_tab, z.tab}, {sin_tab, z.tab}, sv}))
+        return ATTN_ERR_ALIAS;
+    // the kernels run on the stream's device and use that device's copy of the scratch
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    if (stream != nullptr) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd);
+        if (e != hipSuccess) return hip_status(e);
+        if (sd != cur) return ATTN_ERR_VALUE;
+    }
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st) return st;
+    return run_bwd_stages(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, dq, dk, dv, ws, B, H, T,
+                          D, dtype, stream);
+}
 
 }  // extern "C"
 

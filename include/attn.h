@@ -65,7 +65,8 @@ enum attn_status {
     ATTN_ERR_HIP = 6,        /* a HIP launch failed (see attn_last_hip_error)      */
     ATTN_ERR_ALIAS = 7,      /* an output's bytes overlap an input's or an output's */
     ATTN_ERR_VALUE = 8,      /* a scalar argument (e.g. the RoPE base) is invalid   */
-    ATTN_ERR_SAVED = 9       /* the saved rotated q/k buffer is too small           */
+    ATTN_ERR_SAVED = 9,      /* the saved rotated q/k buffer is too small           */
+    ATTN_ERR_SCRATCH = 10    /* too large for the static scratch of a no-alloc call */
 };
 
 /*
@@ -412,6 +413,28 @@ int attn_decode_step(const void* q, const void* k_new, const void* v_new, void* 
                      size_t cache_bytes, const float* cos_tab, const float* sin_tab,
                      void* o, float* lse, void* workspace, size_t workspace_bytes, int pos,
                      int B, int H, int Tmax, int D, int dtype, void* stream);
+
+/*
+ * attn_bwd_saved_noalloc - attn_bwd_saved for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and bitwise the same dq, dk, dv, with the
+ * pre-pass's per-row entries in a device array the library owns instead of a
+ * caller workspace. Nothing is allocated or freed here. The array holds
+ * attn_noalloc_scratch_bytes() (4 MiB) on each GPU, enough for B*H*T up to
+ * 524288 rows on the 16-bit path (1048576 for ATTN_F32); larger problems get
+ * ATTN_ERR_SCRATCH before any launch. Every call on a GPU uses that GPU's one
+ * copy, so calls that overlap on one GPU (other streams or threads) race.
+ * `stream` must belong to the current device (else ATTN_ERR_VALUE).
+ */
+int attn_bwd_saved_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const void* dO, const float* lse,
+                           const float* cos_tab, const float* sin_tab,
+                           const void* saved, size_t saved_bytes,
+                           void* dq, void* dk, void* dv,
+                           int B, int H, int T, int D, int dtype, void* stream);
+
+/* attn_noalloc_scratch_bytes - bytes of that array on each GPU (4 MiB). */
+size_t attn_noalloc_scratch_bytes(void);
 
 /* attn_status_string - static, human-readable name of a status code. */
 const char* attn_status_string(int status);

@@ -57,7 +57,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(10):
+    for code in range(11):
         assert attn.attn_status_string(code) != "unknown status"
     assert attn.attn_status_string(99) == "unknown status"
     assert attn.attn_last_hip_error() == 0
