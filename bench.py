@@ -16,9 +16,9 @@ Prints ONE JSON line. The headline value is the whole step's rate over K steps
 launched back to back (in blocks of steps between HIP events: mean over all K,
 and the p10 / median / p90 of the per-block step times). Besides it the line
 carries
-  plain_pair    the same step through attn_fwd + attn_bwd (the forward rotates
-                q, k on load; the backward forms the rotated q, k again with
-                the rotation pass), timed the same way;
+  plain_pair    the same step through attn_fwd + attn_bwd, the calls with the
+                contract's signatures: the forward rotates q and k on load, the
+                backward's pre-pass rotates them again; timed the same way;
   flushed       with --flush: each step timed alone after 512 MB have been
                 written (cold caches);
   kernels       each kernel's average duration inside a step, from further
@@ -157,7 +157,7 @@ def main():
         attn.attn_fwd_rotated(saved, nsv, v, o, lse, B, H, T, D, dt, sh)
 
     def bwd_prep():
-        attn.attn_bwd_prep(o, do, lse, ws, wsb, B, H, T, D, dt, sh)
+        attn.attn_bwd_prep(None, None, o, do, lse, cs, sn, ws, wsb, B, H, T, D, dt, sh)
 
     def bwd_grads():
         attn.attn_bwd_grads(None, None, v, do, lse, cs, sn, saved, nsv, dq, dk, dv, ws, wsb,
@@ -258,12 +258,14 @@ def main():
                       "max_us": round(float(arr.max()) * 1e3, 2),
                       "tflops": round(fl[n] / (ms * 1e-3) / 1e12, 1),
                       "executed_tflops": round(ex[n] / (ms * 1e-3) / 1e12, 1)}
-    # the memory-bound passes: the rotation reads q, k (16-bit) and writes q', k' (fp16);
-    # the pre-pass reads o, dO (16-bit) and lse and writes two fp32 per row
-    rot_bytes = 2 * (2 + 2) * B * H * T * D
+    # the memory-bound passes: the rotation reads q, k (16-bit) and the two tables and
+    # writes q', k' (fp16); the pre-pass reads o, dO (16-bit) and lse and writes two fp32
+    # per row
+    rot_bytes = 2 * (2 + 2) * B * H * T * D + 2 * T * (D // 2) * 4
     prep_bytes = 2 * 2 * B * H * T * D + 4 * B * H * T + 8 * B * H * T
     for n, nb in (("rotate_kernel", rot_bytes), ("bwd_prep_kernel", prep_bytes)):
         kernels[n]["gbs"] = round(nb / (kernels[n]["avg_us"] * 1e-6) / 1e9, 1)
+        kernels[n]["bytes"] = nb
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
     ach = fl[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),

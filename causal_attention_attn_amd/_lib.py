@@ -38,7 +38,7 @@ _SIGS = {
                       _I, _I, _I, _I, _I, _P]),
     "attn_bwd_saved": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _P, _Z,
                             _I, _I, _I, _I, _I, _P]),
-    "attn_bwd_prep": (_I, [_P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_prep": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
     "attn_bwd_grads": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _P, _Z,
                             _I, _I, _I, _I, _I, _P]),
     "attn_fwd_packed": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
@@ -165,9 +165,11 @@ def attn_bwd_saved(q, k, v, o, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq
           _ptr(dv), _ptr(workspace), int(workspace_bytes), B, H, T, D, dtype, _stream(stream))
 
 
-def attn_bwd_prep(o, dO, lse, workspace, workspace_bytes, B, H, T, D, dtype, stream=None):
-    _call("attn_bwd_prep", _ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace), int(workspace_bytes),
-          B, H, T, D, dtype, _stream(stream))
+def attn_bwd_prep(q, k, o, dO, lse, cos_tab, sin_tab, workspace, workspace_bytes, B, H, T, D,
+                  dtype, stream=None):
+    _call("attn_bwd_prep", _ptr(q), _ptr(k), _ptr(o), _ptr(dO), _ptr(lse), _ptr(cos_tab),
+          _ptr(sin_tab), _ptr(workspace), int(workspace_bytes), B, H, T, D, dtype,
+          _stream(stream))
 
 
 def attn_bwd_grads(q, k, v, dO, lse, cos_tab, sin_tab, saved, saved_bytes, dq, dk, dv,

@@ -306,22 +306,33 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype) {
     return workspace_need(B, H, T, D, dtype);
 }
 
-int attn_bwd_prep(const void* o, const void* dO, const float* lse, void* workspace,
+int attn_bwd_prep(const void* q, const void* k, const void* o, const void* dO, const float* lse,
+                  const float* cos_tab, const float* sin_tab, void* workspace,
                   size_t workspace_bytes, int B, int H, int T, int D, int dtype, void* stream) {
     int st = check_shape(B, H, T, D, dtype);
     if (st) return st;
     st = check_ptrs({o, dO, lse});
     if (st) return st;
-    st = check_workspace(workspace, workspace_bytes, rows_need(B, H, T, dtype));
+    // with q and k (16-bit path) the pass also writes their rotation to the workspace
+    const bool rotate = dtype != ATTN_F32 && (q != nullptr || k != nullptr);
+    if (rotate) {
+        st = check_ptrs({q, k, cos_tab, sin_tab});
+        if (st) return st;
+    }
+    const size_t need = rotate ? workspace_need(B, H, T, D, dtype) : rows_need(B, H, T, dtype);
+    st = check_workspace(workspace, workspace_bytes, need);
     if (st) return st;
     const Sizes z(B, H, T, D, dtype);
-    if (any_alias({{workspace, rows_need(B, H, T, dtype)}}, {{o, z.x}, {dO, z.x}, {lse, z.row}}))
+    if (any_alias({{workspace, need}},
+                  {{o, z.x}, {dO, z.x}, {lse, z.row}, {rotate ? q : nullptr, z.x},
+                   {rotate ? k : nullptr, z.x}, {rotate ? cos_tab : nullptr, z.tab},
+                   {rotate ? sin_tab : nullptr, z.tab}}))
         return ATTN_ERR_ALIAS;
-    const attn::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr,
-                                     nullptr, nullptr, nullptr, nullptr, workspace, B, H, T, D,
-                                     stream);
-    return hip_status(dtype == ATTN_F32 ? attn::launch_bwd_prep_f32(a)
-                                        : attn::launch_bwd_prep16(a, dtype == ATTN_F16));
+    const attn::BwdArgs a = bwd_args(q, k, nullptr, o, dO, lse, cos_tab, sin_tab, nullptr, nullptr,
+                                     nullptr, nullptr, workspace, B, H, T, D, stream);
+    if (dtype == ATTN_F32) return hip_status(attn::launch_bwd_prep_f32(a));
+    return hip_status(attn::launch_bwd_prep16(
+        a, dtype == ATTN_F16, rotate ? ws_rotated(workspace, B, H, T, dtype) : nullptr));
 }
 
 int attn_bwd_grads(const void* q, const void* k, const void* v, const void* dO,
@@ -331,21 +342,27 @@ int attn_bwd_grads(const void* q, const void* k, const void* v, const void* dO,
                    int dtype, void* stream) {
     int st = check_shape(B, H, T, D, dtype);
     if (st) return st;
-    // the 16-bit kernels take the rotated q, k from `saved` and do not read q, k
+    // the 16-bit kernels take the rotated q, k from `saved` (or, without it, from
+    // the workspace, where attn_bwd_prep wrote them) and do not read q, k
     st = dtype == ATTN_F32 ? check_ptrs({q, k, v, dO, lse, cos_tab, sin_tab, dq, dk, dv})
                            : check_ptrs({v, dO, lse, cos_tab, sin_tab, dq, dk, dv});
     if (st) return st;
-    st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
-    if (st) return st;
-    st = check_workspace(workspace, workspace_bytes, rows_need(B, H, T, dtype));
+    const bool in_ws = dtype != ATTN_F32 && saved == nullptr;
+    if (!in_ws) {
+        st = check_saved(saved, saved_bytes, B, H, T, D, dtype);
+        if (st) return st;
+    }
+    const size_t need = in_ws ? workspace_need(B, H, T, D, dtype) : rows_need(B, H, T, dtype);
+    st = check_workspace(workspace, workspace_bytes, need);
     if (st) return st;
     const Sizes z(B, H, T, D, dtype);
     const Span sv = {dtype == ATTN_F32 ? nullptr : saved, saved_need(B, H, T, D, dtype)};
     if (any_alias({{dq, z.x}, {dk, z.x}, {dv, z.x}},
                   {{q, z.x}, {k, z.x}, {v, z.x}, {dO, z.x}, {lse, z.row}, {cos_tab, z.tab},
-                   {sin_tab, z.tab}, sv, {workspace, rows_need(B, H, T, dtype)}}))
+                   {sin_tab, z.tab}, sv, {workspace, need}}))
         return ATTN_ERR_ALIAS;
-    const attn::BwdArgs a = bwd_args(q, k, v, nullptr, dO, lse, cos_tab, sin_tab, saved, dq, dk,
+    const void* rot = in_ws ? ws_rotated(const_cast<void*>(workspace), B, H, T, dtype) : saved;
+    const attn::BwdArgs a = bwd_args(q, k, v, nullptr, dO, lse, cos_tab, sin_tab, rot, dq, dk,
                                      dv, workspace, B, H, T, D, stream);
     if (dtype != ATTN_F32) return hip_status(attn::launch_bwd_grads16(a, dtype == ATTN_F16));
     st = hip_status(attn::launch_bwd_dq_f32(a));
@@ -369,16 +386,18 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
                   {{q, z.x}, {k, z.x}, {v, z.x}, {o, z.x}, {dO, z.x}, {lse, z.row},
                    {cos_tab, z.tab}, {sin_tab, z.tab}}))
         return ATTN_ERR_ALIAS;
-    void* rot = nullptr;
-    if (dtype != ATTN_F32) {  // rotate this call's q and k into the workspace
-        rot = ws_rotated(workspace, B, H, T, dtype);
-        st = hip_status(attn::launch_rotate_qk(q, k, attn::layout_bhtd(H, T, D), cos_tab,
-                                               sin_tab, rot, B, H, T, D, dtype == ATTN_F16,
-                                               static_cast<hipStream_t>(stream)));
-        if (st) return st;
-    }
-    return run_bwd_stages(q, k, v, o, dO, lse, cos_tab, sin_tab, rot, dq, dk, dv, workspace, B,
-                          H, T, D, dtype, stream);
+    if (dtype == ATTN_F32)
+        return run_bwd_stages(q, k, v, o, dO, lse, cos_tab, sin_tab, nullptr, dq, dk, dv,
+                              workspace, B, H, T, D, dtype, stream);
+    // the pre-pass also rotates this call's q and k into the workspace, then the
+    // gradient kernel reads them there
+    void* rot = ws_rotated(workspace, B, H, T, dtype);
+    const attn::BwdArgs a =
+        bwd_args(q, k, v, o, dO, lse, cos_tab, sin_tab, rot, dq, dk, dv, workspace, B, H, T, D,
+                 stream);
+    st = hip_status(attn::launch_bwd_prep16(a, dtype == ATTN_F16, rot));
+    if (st) return st;
+    return hip_status(attn::launch_bwd_grads16(a, dtype == ATTN_F16));
 }
 
 int attn_bwd_saved(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -458,23 +477,17 @@ int attn_bwd_packed(const void* qkv, const void* o, const void* dO, const float*
                   {{qkv, 3 * z.x}, {o, z.x}, {dO, z.x}, {lse, z.row}, {cos_tab, z.tab},
                    {sin_tab, z.tab}, {saved, saved_need(B, H, T, D, dtype)}}))
         return ATTN_ERR_ALIAS;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    const void* rot = saved;
-    if (rot == nullptr) {
-        void* r = ws_rotated(workspace, B, H, T, dtype);
-        st = hip_status(attn::launch_rotate_qk(packed_slot(qkv, 0, H, D), packed_slot(qkv, 1, H, D),
-                                               attn::layout_bthd(H, T, D, 3), cos_tab, sin_tab, r,
-                                               B, H, T, D, dtype == ATTN_F16, s));
-        if (st) return st;
-        rot = r;
-    }
+    // without a saved buffer the pre-pass also rotates q and k, into the workspace
+    void* fresh = saved == nullptr ? ws_rotated(workspace, B, H, T, dtype) : nullptr;
+    const void* rot = saved != nullptr ? saved : fresh;
     char* g = static_cast<char*>(dqkv);
-    attn::BwdArgs a = bwd_args(nullptr, nullptr, packed_slot(qkv, 2, H, D), o, dO, lse, cos_tab,
-                               sin_tab, rot, g, g + (size_t)H * D * 2, g + (size_t)2 * H * D * 2,
-                               workspace, B, H, T, D, stream);
+    attn::BwdArgs a = bwd_args(packed_slot(qkv, 0, H, D), packed_slot(qkv, 1, H, D),
+                               packed_slot(qkv, 2, H, D), o, dO, lse, cos_tab, sin_tab, rot, g,
+                               g + (size_t)H * D * 2, g + (size_t)2 * H * D * 2, workspace, B, H,
+                               T, D, stream);
     a.lqkv = attn::layout_bthd(H, T, D, 3);
     a.lo = attn::layout_bthd(H, T, D, 1);
-    st = hip_status(attn::launch_bwd_prep16(a, dtype == ATTN_F16));
+    st = hip_status(attn::launch_bwd_prep16(a, dtype == ATTN_F16, fresh));
     if (st) return st;
     return hip_status(attn::launch_bwd_grads16(a, dtype == ATTN_F16));
 }

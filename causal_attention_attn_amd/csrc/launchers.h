@@ -66,7 +66,8 @@ hipError_t launch_rotate_qk(const void* q, const void* k, Layout lqk, const floa
                             const float* sn, void* out, int B, int H, int T, int D,
                             bool f16_storage, hipStream_t s);
 hipError_t launch_fwd16(const FwdArgs& a, bool f16_storage);
-hipError_t launch_bwd_prep16(const BwdArgs& a, bool f16_storage);   // workspace entries
+// workspace entries; rot non-null: also the rotated q, k (from a.q, a.k) into rot
+hipError_t launch_bwd_prep16(const BwdArgs& a, bool f16_storage, void* rot = nullptr);
 hipError_t launch_bwd_grads16(const BwdArgs& a, bool f16_storage);  // dq, dk, dv in one launch
 
 // Decode over a key/value cache (16-bit path): the cache is [B, H, Tmax, D] fp16

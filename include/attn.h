@@ -143,9 +143,10 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int D, int dtype);
  * respect to the pre-RoPE q, k and v ("Show HN: NanoEuler", paragraph 2: every
  * analytic gradient, RoPE's included, is checked against centred differences).
  * Recompute-based: P is rebuilt from q, k and lse; nothing of size T x T is
- * stored. The 16-bit path first rotates this call's q and k into the workspace
- * (the values attn_fwd_save would have saved), then runs attn_bwd_prep and
- * attn_bwd_grads on `stream`.
+ * stored. Two launches on `stream`: the pre-pass (attn_bwd_prep), which on the
+ * 16-bit path also rotates this call's q and k into the workspace (bitwise the
+ * values attn_fwd's on-load rotation forms), then the gradient kernel
+ * (attn_bwd_grads) reading them there.
  *   q, k, v, o, dO  [B,H,T,D] dtype, inputs (o and lse from attn_fwd)
  *   lse             [B,H,T] fp32, input
  *   dq, dk, dv      [B,H,T,D] dtype, outputs (overwritten)
@@ -205,19 +206,25 @@ int attn_fwd_rotated(const void* saved, size_t saved_bytes, const void* v, void*
  * delta_t = sum_d dO[t,d] o[t,d] (equal to sum_u P[t,u] dP[t,u], the softmax
  * Jacobian term) and, for the 16-bit path, lse_t * log2 e, written to the
  * per-row part of the workspace (see attn_bwd_workspace_bytes). o, dO
- * [B,H,T,D] dtype and lse [B,H,T] fp32 are inputs.
+ * [B,H,T,D] dtype and lse [B,H,T] fp32 are inputs. With q and k (16-bit path;
+ * NULL for both skips it) the same pass also writes their rotation - the values
+ * attn_rotate_qk writes - into the rest of the workspace, which must then hold
+ * attn_bwd_workspace_bytes(); cos_tab and sin_tab are read only then.
  */
-int attn_bwd_prep(const void* o, const void* dO, const float* lse,
+int attn_bwd_prep(const void* q, const void* k, const void* o, const void* dO, const float* lse,
+                  const float* cos_tab, const float* sin_tab,
                   void* workspace, size_t workspace_bytes,
                   int B, int H, int T, int D, int dtype, void* stream);
 
 /*
  * attn_bwd_grads - writes dq, dk (w.r.t. the pre-RoPE q and k) and dv. Reads
  * the workspace entries of attn_bwd_prep, which must have been enqueued before
- * it on the same stream (or completed) for the same o, dO and lse. As
- * attn_bwd_saved, minus o: the 16-bit path takes the rotated q and k from
- * `saved` only (q and k are not read and may be NULL), and runs dq and dk/dv
- * in one launch.
+ * it on the same stream (or completed) for the same o, dO and lse. The 16-bit
+ * path takes the rotated q and k from `saved` (as attn_bwd_saved) or, when
+ * `saved` is NULL, from the workspace, where attn_bwd_prep wrote them (then the
+ * workspace holds attn_bwd_workspace_bytes()); q and k are not read there and
+ * may be NULL. ATTN_F32 reads q and k. dq and dk/dv come from one launch.
+ * attn_bwd is attn_bwd_prep with q, k followed by this call with saved NULL.
  */
 int attn_bwd_grads(const void* q, const void* k, const void* v,
                    const void* dO, const float* lse,
@@ -276,8 +283,8 @@ int attn_fwd_packed(const void* qkv, const float* cos_tab, const float* sin_tab,
  *   dqkv      [B, T, 3, H, D] dtype, output (overwritten): dq, dk, dv slots
  *   workspace device buffer of at least attn_bwd_workspace_bytes() (the
  *             per-row part suffices when saved is given)
- * Enqueues (without saved) the rotation pass, then the pre-pass and the
- * gradient kernel; the |dS| bound of attn_bwd applies.
+ * Enqueues the pre-pass (which, without saved, also rotates q and k into the
+ * workspace) and the gradient kernel; the |dS| bound of attn_bwd applies.
  */
 int attn_bwd_packed(const void* qkv, const void* o, const void* dO, const float* lse,
                     const float* cos_tab, const float* sin_tab,

@@ -190,8 +190,8 @@ def test_bwd_saved_rejects_bad_arguments(lib):
 
 def test_bwd_stages_reject_bad_arguments(lib):
     f = lambda **o: status_of(lambda: attn.attn_bwd_prep(
-        **{**dict(o=A(0), dO=A(1), lse=A(2), workspace=A(3), workspace_bytes=WROWS,
-                  B=1, H=1, T=8, D=64, dtype=0, stream=0), **o}))
+        **{**dict(q=0, k=0, o=A(0), dO=A(1), lse=A(2), cos_tab=0, sin_tab=0, workspace=A(3),
+                  workspace_bytes=WROWS, B=1, H=1, T=8, D=64, dtype=0, stream=0), **o}))
     assert f(o=0) == 1
     assert f(lse=0) == 1
     assert f(D=32) == 2
@@ -201,12 +201,19 @@ def test_bwd_stages_reject_bad_arguments(lib):
     assert f(workspace_bytes=WROWS - 1) == 5
     assert f(workspace=MIS) == 4
     assert f(workspace=A(1, 1008)) == 7                   # workspace overlaps dO's last row
+    # with q and k the pass also rotates them: the tables are needed, and room for q', k'
+    assert f(q=A(4), k=A(5)) == 1                         # no tables
+    assert f(q=A(4), k=A(5), cos_tab=A(6), sin_tab=A(7)) == 5
+    assert f(q=A(4), k=A(5), cos_tab=A(6), sin_tab=A(7), workspace_bytes=WROWS + SAVED,
+             workspace=A(4, 512)) == 7                    # the workspace overlaps q
+    assert f(q=A(4), k=0, cos_tab=A(6), sin_tab=A(7), workspace_bytes=WROWS + SAVED) == 1
     base = dict(q=A(0), k=A(1), v=A(2), dO=A(4), lse=A(5), cos_tab=A(6), sin_tab=A(7),
                 saved=A(12), saved_bytes=SAVED, dq=A(8), dk=A(9), dv=A(10), workspace=A(11),
                 workspace_bytes=WROWS, B=1, H=1, T=8, D=64, dtype=0, stream=0)
     g = lambda **o: status_of(lambda: attn.attn_bwd_grads(**{**base, **o}))
     assert g(dq=0) == 1
-    assert g(saved=0) == 1
+    assert g(saved=0) == 5                                # then q', k' come from the workspace
+    assert g(saved=0, workspace_bytes=WROWS + SAVED, dq=A(11, WROWS + 64)) == 7
     assert g(saved_bytes=8) == 9
     assert g(workspace=0) == 5
     assert g(dv=A(2)) == 7                                # dv is v
