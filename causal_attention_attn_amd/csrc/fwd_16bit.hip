@@ -292,6 +292,11 @@ __device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, KOps<
     constexpr int FREE = (STG + NS - 1) % NS;
     const int k0 = n * C::BN;
     const bool live = !(DIAG && k0 > x.wq0);  // false: tile wholly above this wave's diagonal
+    // RoPE on load at D = 128 holds 48 registers of raw key rows and tables per
+    // thread; there the K operands are read when the step starts instead of one
+    // step ahead (their 64 registers would push the kernel into heavy spills)
+    constexpr bool KPF = !(ROPE && D == 128);
+    if constexpr (!KPF) read_k(kr, rg.k[STG], of);
     f32x16 s[C::NSB];
     if (live) fwd_scores<D, DIAG>(s, st, qf, kr, k0, x.wq0, x.lane);
     if constexpr (ROPE) {
@@ -309,7 +314,7 @@ __device__ __forceinline__ void fwd_step(FwdState<D>& st, const f16x8* qf, KOps<
         else ld.issue(x.v, x.T, nx * C::BN, rg.v[FREE], x.wave);
     }
     if (live) fwd_softmax_pv<D, E, DIAG>(st, s, rg.v[STG], of, k0, x.wq0, n == 0);
-    read_k(kr, rg.k[NXT], of);
+    if constexpr (KPF) read_k(kr, rg.k[NXT], of);
 }
 
 // The forward kernel. ROPE: q and k are the caller's un-rotated tensors (layout
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(
     }
     ring_barrier();
     KOps<D> kops;
-    read_k(kops, rg.k[0], of);
+    if constexpr (!(ROPE && D == 128)) read_k(kops, rg.k[0], of);
 
     int n = 0;
     // full tiles: branch-free bodies, ring stages as compile-time constants
