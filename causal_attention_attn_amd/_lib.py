@@ -11,7 +11,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libattn.so")
+# ATTN_LIBRARY names another build of the same library (the host-sanitizer
+# build the CPU tests load); by default the in-tree one
+LIB_PATH = os.environ.get("ATTN_LIBRARY") or os.path.join(_PKG, "libattn.so")
 
 ATTN_BF16 = 0
 ATTN_F32 = 1
