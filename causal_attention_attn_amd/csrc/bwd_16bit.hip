@@ -73,7 +73,49 @@ struct RowTables {
                 s[b][g] = *reinterpret_cast<const f32x2*>(sn + row + d / 2);
             }
     }
+    // The same entries from the table rows stage_tables copied into LDS: row r
+    // (0 .. 63) of the 64-row blocks cb (cos) and sb (sin) that hold this lane's row.
+    __device__ __forceinline__ void load_lds(const char* cb, const char* sb, int r, int hf) {
+        static_assert(D == 64, "LDS table rows are 128 bytes");
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int off = r * 128 + 16 * ((4 * b + g) ^ (r & 7)) + 8 * hf;
+                c[b][g] = *reinterpret_cast<const f32x2*>(cb + off);
+                s[b][g] = *reinterpret_cast<const f32x2*>(sb + off);
+            }
+    }
 };
+
+// At D = 64 (three ring stages) an item's RoPE table rows - cos and sin of its
+// 128 rows, 16 KB each - are copied straight into LDS during its last tile
+// step, into the two stages that step leaves free (no tile follows it), so the
+// epilogue finds them there instead of waiting for a memory round trip after
+// the loop. Wave w copies one 8 KB block: w = 0, 1 the cos rows 0-63 and 64-127
+// (into ca, cb), w = 2, 3 the sin rows (into sa, sb). In LDS the 16-byte chunk
+// c of row r sits at position c ^ (r & 7), so that 32 lanes reading one chunk
+// of 32 consecutive rows spread over the banks. Rows past T read as zeros (their
+// results are not stored).
+template <int D>
+__device__ __forceinline__ void stage_tables(const float* cs, const float* sn, int r0, int T,
+                                             char* ca, char* cb, char* sa, char* sb, int wave,
+                                             int lane) {
+    static_assert(D == 64, "one table row is 128 bytes");
+    const int rows = T > r0 ? T - r0 : 0;
+    const rsrc_t src = make_rsrc((wave < 2 ? cs : sn) + (size_t)r0 * (D / 2),
+                                 (uint32_t)rows * (D / 2) * 4);
+    char* dst = wave == 0 ? ca : wave == 1 ? cb : wave == 2 ? sa : sb;
+    // instruction i fills LDS bytes [1024 i, +1024) of the block: rows 8i + rr.
+    // The whole offset goes in the per-lane register: an instruction's immediate
+    // offset would be added to the LDS address as well.
+    const int rr = lane >> 3, pos = lane & 7;
+    const uint32_t v0 = (uint32_t)((wave & 1) * 64 * 128 + rr * 128 + 16 * (pos ^ rr));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, LDS_PTR(dst + i * 1024), 16,
+                                                 v0 + (uint32_t)i * 1024, 0, 0, 0);
+}
 
 // Epilogue stores through LDS. A wave's 32 output rows (2D bytes each) are put
 // into a 32 x 2D-byte LDS buffer in the accumulator layout (lane (c, h) owns
@@ -105,6 +147,46 @@ struct RowStage {
         }
     }
 };
+
+// An item's output rows: this wave's 32 rows of R^T (scale * acc) (dq, dk) or of
+// acc itself (dv), rounded to E, staged through LDS and stored as whole rows.
+template <int D, typename E>
+__device__ __forceinline__ void rope_out(const f32x16* acc, float scale, const RowTables<D>& tb,
+                                         const RowStage<D>& sg, E* head, int row0, int T,
+                                         int pitch, int c32, int hf, int lane) {
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x2 c2 = tb.c[b][g], s2 = tb.s[b][g];
+            u32x2 w;
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const float x0 = acc[b][4 * g + 2 * pr] * scale;
+                const float x1 = acc[b][4 * g + 2 * pr + 1] * scale;
+                w[pr] = pack2<E>(x0 * c2[pr] + x1 * s2[pr], x1 * c2[pr] - x0 * s2[pr]);
+            }
+            sg.put(c32, hf, b, g, w);
+        }
+    }
+    sg.store(head, row0, T, pitch, lane);
+}
+template <int D, typename E>
+__device__ __forceinline__ void plain_out(const f32x16* acc, const RowStage<D>& sg, E* head,
+                                          int row0, int T, int pitch, int c32, int hf, int lane) {
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x2 w;
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr)
+                w[pr] = pack2<E>(acc[b][4 * g + 2 * pr], acc[b][4 * g + 2 * pr + 1]);
+            sg.put(c32, hf, b, g, w);
+        }
+    }
+    sg.store(head, row0, T, pitch, lane);
+}
 
 // This wave's staging buffer once the ring is idle: one of the ring's stage
 // buffers (64 x 2D bytes each: room for two outputs of 32 rows).
@@ -170,28 +252,45 @@ __device__ __forceinline__ void dq_tile(f32x16* acc, const f16x8* qf, const vec8
     }
 }
 
-// Step n of the dq kernel's key-tile loop on ring stage STG (= n % NS).
-template <int D, typename E, int STG, bool DIAG, bool STRIDED>
+// Where an item's RoPE table rows come from (see stage_tables): the tables and
+// the item's first row.
+struct TabSrc {
+    const float* cs;
+    const float* sn;
+    int r0;
+};
+
+// Step n of the dq kernel's key-tile loop on ring stage STG (= n % NS). LAST:
+// the item's last step (D = 64 only), which copies the item's RoPE table rows
+// into the two stages it leaves free.
+template <int D, typename E, int STG, bool DIAG, bool STRIDED, bool LAST = false>
 __device__ __forceinline__ void dq_step(f32x16* acc, const f16x8* qf, const vec8<E>* df,
                                         const Ring& rg,
                                         const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
                                         const f16* kr, const E* v, int vst, int T, int n,
                                         int ntiles,
                                         int wq0, int lane, int wave, const f32x16& nl,
-                                        const f32x16& nd) {
+                                        const f32x16& nd, const TabSrc& tab = {}) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int NXT = (STG + NS - 1) % NS;
     // tiles past the item's last one are never loaded, so the last step has no
     // younger tile in flight and waits for everything
-    if (n + 1 < ntiles) wait_vmcnt<C::LPT * (NS - 2)>();
+    if (!LAST && n + 1 < ntiles) wait_vmcnt<C::LPT * (NS - 2)>();
     else wait_vmcnt<0>();
     ring_barrier();
-    const int nx = n + NS - 1;
-    if (nx < ntiles) {
-        ld.issue(kr, T, nx * C::KN, rg.k[NXT], wave);
-        if constexpr (STRIDED) ld.issue_strided(v, T, nx * C::KN, rg.v[NXT], wave, vst);
-        else ld.issue(v, T, nx * C::KN, rg.v[NXT], wave);
+    if constexpr (LAST) {
+        static_assert(NS == 3, "the last step's free stages");
+        constexpr int A = (STG + 1) % NS, B = (STG + 2) % NS;
+        stage_tables<D>(tab.cs, tab.sn, tab.r0, T, rg.k[A], rg.v[A], rg.k[B], rg.v[B], wave,
+                        lane);
+    } else {
+        const int nx = n + NS - 1;
+        if (nx < ntiles) {
+            ld.issue(kr, T, nx * C::KN, rg.k[NXT], wave);
+            if constexpr (STRIDED) ld.issue_strided(v, T, nx * C::KN, rg.v[NXT], wave, vst);
+            else ld.issue(v, T, nx * C::KN, rg.v[NXT], wave);
+        }
     }
     dq_tile<D, E, DIAG>(acc, qf, df, rg.k[STG], rg.v[STG], of, n * C::KN, wq0, lane, nl, nd);
 }
@@ -285,7 +384,10 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
         if constexpr (NS > 2)
             dq_step<D, E, 2, false, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n + 2, ntiles, wq0, lane, wave, nl, nd);
     }
-    for (; n < ntiles; ++n) {
+    // the remaining steps reach the diagonal; with three stages the last one is
+    // peeled off (it copies the RoPE table rows for the epilogue into LDS)
+    constexpr bool TAB = NS == 3;
+    for (; n + (TAB ? 1 : 0) < ntiles; ++n) {
         const int stg = n % NS;
         if (stg == 0)
             dq_step<D, E, 0, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
@@ -294,28 +396,34 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
         else if constexpr (NS > 2)
             dq_step<D, E, 2, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
     }
-    RowTables<D> tb;
-    tb.load(cs, sn, tq, T, hf);
-    wait_vmcnt<0>();
-
-    __syncthreads();  // the ring is idle: its stage buffers hold the output rows
-    const RowStage<D> sg = {stage_buffer<D>(rg, wave)};
-#pragma unroll
-    for (int b = 0; b < C::DB; ++b) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x2 c2 = tb.c[b][g], s2 = tb.s[b][g];
-            u32x2 w;
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-                const float x0 = acc[b][4 * g + 2 * pr] * scale;
-                const float x1 = acc[b][4 * g + 2 * pr + 1] * scale;
-                w[pr] = pack2<E>(x0 * c2[pr] + x1 * s2[pr], x1 * c2[pr] - x0 * s2[pr]);
-            }
-            sg.put(c32, hf, b, g, w);
-        }
+    if constexpr (TAB) {
+        // the last step and the epilogue, with the last step's ring stage L a
+        // compile-time constant (the stage buffers are distinct LDS objects)
+        const TabSrc tab = {cs, sn, q0};
+        const int stg = n % NS;
+        static_for<NS>([&](auto S) {
+            constexpr int L = decltype(S)::value;
+            if (stg != L) return;
+            dq_step<D, E, L, true, STRIDED, true>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd, tab);
+            wait_vmcnt<0>();
+            __syncthreads();  // the table rows have landed and every wave is done with the ring
+            // the table rows sit in the two stages after L; stage L itself (16 KB)
+            // stages the output rows, 4 KB per wave
+            constexpr int A = (L + 1) % NS, B = (L + 2) % NS;
+            const bool h = wave >= 2;
+            RowTables<D> tb;
+            tb.load_lds(h ? rg.v[A] : rg.k[A], h ? rg.v[B] : rg.k[B], 32 * (wave & 1) + c32, hf);
+            const RowStage<D> sg = {(h ? rg.v[L] : rg.k[L]) + (wave & 1) * 32 * 2 * D};
+            rope_out<D, E>(acc, scale, tb, sg, dq + vhead, wq0, T, vst, c32, hf, lane);
+        });
+    } else {
+        RowTables<D> tb;
+        tb.load(cs, sn, tq, T, hf);
+        wait_vmcnt<0>();
+        __syncthreads();  // the ring is idle: its stage buffers hold the output rows
+        const RowStage<D> sg = {stage_buffer<D>(rg, wave)};
+        rope_out<D, E>(acc, scale, tb, sg, dq + vhead, wq0, T, vst, c32, hf, lane);
     }
-    sg.store(dq + vhead, wq0, T, vst, lane);
 }
 
 // One 64-query tile of the dk/dv kernel for one wave (32 keys). DIAG: the tile
@@ -414,20 +522,30 @@ struct DkdvCtx {
     }
 };
 
-// Step of the dk/dv kernel's query-tile loop on ring stage STG.
-template <int D, typename E, int STG, bool DIAG, bool STRIDED>
+// Step of the dk/dv kernel's query-tile loop on ring stage STG. LAST: the
+// item's last step (D = 64 only), which copies the item's RoPE table rows into
+// the two stages it leaves free.
+template <int D, typename E, int STG, bool DIAG, bool STRIDED, bool LAST = false>
 __device__ __forceinline__ void dkdv_step(f32x16* dva, f32x16* dka, const f16x8* kf,
                                           const vec8<E>* vf, const Ring& rg,
                                           const TileLoads<D, 64, 4>& ld, const OperandOffs<D>& of,
-                                          const DkdvCtx<D, E, STRIDED>& x, int qt, int nqt) {
+                                          const DkdvCtx<D, E, STRIDED>& x, int qt, int nqt,
+                                          const TabSrc& tab = {}) {
     using C = BwdTile<D>;
     constexpr int NS = C::NS;
     constexpr int NXT = (STG + NS - 1) % NS;
     // tiles past the last query tile are never loaded (see dq_step)
-    if (qt + 1 < nqt) wait_vmcnt<(C::LPT + 1) * (NS - 2)>();
+    if (!LAST && qt + 1 < nqt) wait_vmcnt<(C::LPT + 1) * (NS - 2)>();
     else wait_vmcnt<0>();
     ring_barrier();
-    if (qt + NS - 1 < nqt) x.issue(ld, qt + NS - 1, rg.k[NXT], rg.v[NXT], rg.x[NXT]);
+    if constexpr (LAST) {
+        static_assert(NS == 3, "the last step's free stages");
+        constexpr int A = (STG + 1) % NS, B = (STG + 2) % NS;
+        stage_tables<D>(tab.cs, tab.sn, tab.r0, x.T, rg.k[A], rg.v[A], rg.k[B], rg.v[B], x.wave,
+                        x.lane);
+    } else if (qt + NS - 1 < nqt) {
+        x.issue(ld, qt + NS - 1, rg.k[NXT], rg.v[NXT], rg.x[NXT]);
+    }
     dkdv_tile<D, E, DIAG>(dva, dka, kf, vf, rg.k[STG], rg.v[STG],
                        reinterpret_cast<const float*>(rg.x[STG]), of, qt * C::QN, x.wk0, x.lane);
 }
@@ -489,57 +607,68 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
 #pragma unroll
     for (int b = 0; b < C::DB; ++b) dva[b] = dka[b] = f32x16{};
 
-    // ring stage of query tile qt is (qt - qt0) % NS; the diagonal tiles come first
+    // ring stage of query tile qt is (qt - qt0) % NS; the diagonal tiles come
+    // first. With three stages the last step is peeled off (it copies the RoPE
+    // table rows for the epilogue into LDS), so the loops stop before it.
+    constexpr bool TAB = NS == 3;
+    const int qlast = TAB ? nqt - 1 : nqt;
     int qt = qt0;
-    for (; qt < min(qfull, nqt); ++qt) {
+    for (; qt < min(qfull, qlast); ++qt) {
         const int stg = (qt - qt0) % NS;
         if (stg == 0) dkdv_step<D, E, 0, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
         else if (stg == 1) dkdv_step<D, E, 1, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
         else if constexpr (NS > 2) dkdv_step<D, E, 2, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
     // the full tiles, rotated so that the unrolled body starts on stage 0
-    for (; qt < nqt && (qt - qt0) % NS != 0; ++qt) {
+    for (; qt < qlast && (qt - qt0) % NS != 0; ++qt) {
         const int stg = (qt - qt0) % NS;
         if (stg == 1) dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
         else if constexpr (NS > 2) dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
-    for (; qt + NS <= nqt; qt += NS) {
+    for (; qt + NS <= qlast; qt += NS) {
         dkdv_step<D, E, 0, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
         dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt + 1, nqt);
         if constexpr (NS > 2) dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt + 2, nqt);
     }
-    for (; qt < nqt; ++qt) {
+    for (; qt < qlast; ++qt) {
         const int stg = (qt - qt0) % NS;
         if (stg == 0) dkdv_step<D, E, 0, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
         else if (stg == 1) dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
         else if constexpr (NS > 2) dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
     }
-    RowTables<D> tb;
-    tb.load(cs, sn, tk, T, hf);
-    wait_vmcnt<0>();
-
-    __syncthreads();  // the ring is idle: its stage buffers hold the output rows
-    const RowStage<D> sk = {stage_buffer<D>(rg, wave)};
-    const RowStage<D> sv = {sk.buf + 32 * 2 * D};
-#pragma unroll
-    for (int b = 0; b < C::DB; ++b) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x2 c2 = tb.c[b][g], s2 = tb.s[b][g];
-            u32x2 wk, wv;
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-                const float x0 = dka[b][4 * g + 2 * pr] * scale;
-                const float x1 = dka[b][4 * g + 2 * pr + 1] * scale;
-                wk[pr] = pack2<E>(x0 * c2[pr] + x1 * s2[pr], x1 * c2[pr] - x0 * s2[pr]);
-                wv[pr] = pack2<E>(dva[b][4 * g + 2 * pr], dva[b][4 * g + 2 * pr + 1]);
-            }
-            sk.put(c32, hf, b, g, wk);
-            sv.put(c32, hf, b, g, wv);
-        }
+    if constexpr (TAB) {
+        // the last step (it may also be a diagonal one: the diagonal variant
+        // gives the same result on a full tile) and the epilogue, with the last
+        // step's ring stage L a compile-time constant
+        const TabSrc tab = {cs, sn, k0};
+        const int stg = (qt - qt0) % NS;
+        static_for<NS>([&](auto S) {
+            constexpr int L = decltype(S)::value;
+            if (stg != L) return;
+            dkdv_step<D, E, L, true, STRIDED, true>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt, tab);
+            wait_vmcnt<0>();
+            __syncthreads();  // the table rows have landed and every wave is done with the ring
+            // the table rows sit in the two stages after L; stage L itself (16 KB)
+            // stages the output rows, 4 KB per wave: dk, then dv in the same place
+            // (one wave's own LDS accesses stay in program order)
+            constexpr int A = (L + 1) % NS, B = (L + 2) % NS;
+            const bool h = wave >= 2;
+            RowTables<D> tb;
+            tb.load_lds(h ? rg.v[A] : rg.k[A], h ? rg.v[B] : rg.k[B], 32 * (wave & 1) + c32, hf);
+            const RowStage<D> sg = {(h ? rg.v[L] : rg.k[L]) + (wave & 1) * 32 * 2 * D};
+            rope_out<D, E>(dka, scale, tb, sg, dk + vhead, wk0, T, vst, c32, hf, lane);
+            plain_out<D, E>(dva, sg, dv + vhead, wk0, T, vst, c32, hf, lane);
+        });
+    } else {
+        RowTables<D> tb;
+        tb.load(cs, sn, tk, T, hf);
+        wait_vmcnt<0>();
+        __syncthreads();  // the ring is idle: its stage buffers hold the output rows
+        const RowStage<D> sk = {stage_buffer<D>(rg, wave)};
+        const RowStage<D> sv = {sk.buf + 32 * 2 * D};
+        rope_out<D, E>(dka, scale, tb, sk, dk + vhead, wk0, T, vst, c32, hf, lane);
+        plain_out<D, E>(dva, sv, dv + vhead, wk0, T, vst, c32, hf, lane);
     }
-    sk.store(dk + vhead, wk0, T, vst, lane);
-    sv.store(dv + vhead, wk0, T, vst, lane);
 }
 
 // The gradient kernel: one launch runs both kinds of item, so the light items
