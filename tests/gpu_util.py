@@ -18,7 +18,9 @@ TOL = {"bf16": dict(max_abs=2e-2, rel_l2=1e-2), "f16": dict(max_abs=2e-2, rel_l2
 #   "saved"   attn_fwd_save + attn_bwd_saved (the training pair the benchmark times)
 #   "plain"   attn_fwd + attn_bwd (the backward rotates q and k itself)
 #   "rotated" attn_rotate_qk + attn_fwd_rotated, then attn_bwd_saved on that buffer
-PATHS = ("saved", "plain", "rotated")
+#   "stages"  the four stages one by one: attn_rotate_qk, attn_fwd_rotated,
+#             attn_bwd_prep, attn_bwd_grads (what the benchmark launches)
+PATHS = ("saved", "plain", "rotated", "stages")
 
 
 def gpu_run(x, base=10000.0, path="saved"):
@@ -29,6 +31,25 @@ def gpu_run(x, base=10000.0, path="saved"):
     g = {n: t.to(dev) for n, t in x.items()}
     q, k, v, do = g["q"], g["k"], g["v"], g["do"]
     saved = None
+    if path == "stages" and q.dtype != torch.float32:
+        B, H, T, D = q.shape
+        dt = attn.api._dtype_code(q)
+        cs, sn = attn.rope_tables(T, D, base, dev)
+        ns = attn.attn_saved_bytes(B, H, T, D, dt)
+        saved = torch.empty(ns, dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        attn.attn_rotate_qk(q, k, cs, sn, saved, ns, B, H, T, D, dt)
+        attn.attn_fwd_rotated(saved, ns, v, o, lse, B, H, T, D, dt)
+        wsb = attn.attn_bwd_workspace_bytes(B, H, T, D, dt)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        attn.attn_bwd_prep(None, None, o, do, lse, cs, sn, ws, wsb, B, H, T, D, dt)
+        attn.attn_bwd_grads(None, None, v, do, lse, cs, sn, saved, ns, dq, dk, dv, ws, wsb,
+                            B, H, T, D, dt)
+        torch.cuda.synchronize()
+        out = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, saved=saved)
+        return {n: t.cpu() for n, t in out.items()}
     if path == "rotated" and q.dtype != torch.float32:
         B, H, T, D = q.shape
         dt = attn.api._dtype_code(q)

@@ -80,16 +80,18 @@ def test_full_size_workloads_all_heads(name):
                                    (2, 2, 333)])
 def test_paths_agree_bitwise(B, H, T, D, dtype):
     """attn_fwd + attn_bwd (q, k rotated by the backward itself), attn_fwd_save +
-    attn_bwd_saved, and the rotation pass + attn_fwd_rotated give bitwise the same
-    outputs; the forward's saved buffer is bitwise the rotation pass's output."""
+    attn_bwd_saved, the rotation pass + attn_fwd_rotated, and the four stages one
+    by one give bitwise the same outputs; the forward's saved buffer is bitwise the
+    rotation pass's output."""
     x = workloads.make(workloads.WORKLOADS[HALF[dtype]], seed=T + D + 3, shape=(B, H, T, D))
-    runs = {p: gpu_run(x, path=p) for p in ("saved", "plain", "rotated")}
-    for p in ("plain", "rotated"):
+    runs = {p: gpu_run(x, path=p) for p in ("saved", "plain", "rotated", "stages")}
+    for p in ("plain", "rotated", "stages"):
         for n in ("o", "lse", "dq", "dk", "dv"):
             assert torch.equal(runs[p][n], runs["saved"][n]), (p, n)
     n = B * H * T * D * 2  # bytes of rotated q, then of rotated k
-    for part in (slice(0, n), slice(n, 2 * n)):
-        assert torch.equal(runs["rotated"]["saved"][part], runs["saved"]["saved"][part])
+    for p in ("rotated", "stages"):
+        for part in (slice(0, n), slice(n, 2 * n)):
+            assert torch.equal(runs[p]["saved"][part], runs["saved"]["saved"][part]), p
 
 
 def test_backward_reads_its_own_q_and_k():
