@@ -715,7 +715,7 @@ int check_swiglu(int N, int F, int dtype) {
 }
 
 size_t norm_ws_need(int N, int C) {
-    return round256((size_t)attn::rmsnorm_bwd_parts(N) * C * sizeof(float));
+    return round256((size_t)attn::rmsnorm_bwd_parts(N, C) * C * sizeof(float));
 }
 
 }  // namespace

@@ -85,7 +85,7 @@ hipError_t launch_decode(const void* q, const void* knew, const void* vnew, cons
 
 // The per-layer kernels next to attention (16-bit path): residual add +
 // RMSNorm and SwiGLU.
-int rmsnorm_bwd_parts(int N);  // workgroups of the backward = rows of its fp32 partial sums
+int rmsnorm_bwd_parts(int N, int C);  // workgroups of the backward = rows of its fp32 partial sums
 hipError_t launch_rmsnorm_fwd(const void* x, const void* r, const void* g, float eps, void* h,
                               void* y, float* rstd, int N, int C, bool f16_storage,
                               hipStream_t s);

@@ -75,14 +75,21 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const E* __restrict__ 
     if (lane == 0) rstd[row] = rs;
 }
 
+// Waves per workgroup of the RMSNorm backward: sixteen while a row's registers
+// leave four waves per SIMD (rows of up to 768 features), else four. Fewer,
+// larger workgroups leave fewer partial column sums for the dg reduction.
+constexpr int norm_bwd_waves(int nch) { return nch <= 3 ? 16 : 4; }
+
 // One wave per row, rows grid-strided; each workgroup leaves its column sums of
 // dy * h^ in part[blockIdx.x][C] (fp32) for the dg reduction.
 template <typename E, int NCH>
-__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
+__global__ __launch_bounds__(64 * norm_bwd_waves(NCH)) void rmsnorm_bwd_kernel(
     const E* __restrict__ h, const E* __restrict__ g, const float* __restrict__ rstd,
     const E* __restrict__ dy, const E* __restrict__ dres, E* __restrict__ dh,
     float* __restrict__ part, int N, int C) {
-    __shared__ f32x4 red[4][64][4];  // per wave: its lanes' column sums, 4 chunks at a time
+    constexpr int NW = norm_bwd_waves(NCH);
+    constexpr int KPR = 16 / NW;  // chunks per LDS round (16 KB)
+    __shared__ f32x4 red[NW][64][KPR];  // per wave: its lanes' column sums, KPR chunks at a time
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -95,8 +102,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
     // RP rows per pass (two while they fit in registers), all of their loads
     // issued before any arithmetic
     constexpr int RP = NCH <= 8 ? 2 : 1;
-    const int stride = gridDim.x * 4;
-    for (int row0 = blockIdx.x * 4 + wave; row0 < N; row0 += RP * stride) {
+    const int stride = gridDim.x * NW;
+    for (int row0 = blockIdx.x * NW + wave; row0 < N; row0 += RP * stride) {
         f32x4 hv[RP][NCH], dv[RP][NCH], rv[RP][NCH];
         float rs[RP];
 #pragma unroll
@@ -134,18 +141,20 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
                 store4(dh + base + 256 * j, (gd[j] - hh[j] * mean) * rs[q] + rv[q][j]);
         }
     }
-    // the workgroup's column sums: four waves added through LDS, four chunks at a time
+    // the workgroup's column sums: its waves added through LDS in a fixed order,
+    // KPR chunks at a time
 #pragma unroll
-    for (int j0 = 0; j0 < NCH; j0 += 4) {
+    for (int j0 = 0; j0 < NCH; j0 += KPR) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) red[wave][lane][k] = j0 + k < NCH ? acc[j0 + k] : zero;
+        for (int k = 0; k < KPR; ++k) red[wave][lane][k] = j0 + k < NCH ? acc[j0 + k] : zero;
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < KPR; ++k) {
                 if (j0 + k < NCH) {
-                    const f32x4 s = red[0][lane][k] + red[1][lane][k] + red[2][lane][k] +
-                                    red[3][lane][k];
+                    f32x4 s = red[0][lane][k];
+#pragma unroll
+                    for (int w = 1; w < NW; ++w) s += red[w][lane][k];
                     *reinterpret_cast<f32x4*>(part + (size_t)blockIdx.x * C + 4 * lane +
                                               256 * (j0 + k)) = s;
                 }
@@ -263,9 +272,11 @@ static hipError_t with_chunks(int nch, F&& f) {
     }
 }
 
-int rmsnorm_bwd_parts(int N) {
-    const int wgs = (N + 3) / 4;
-    return wgs < 1024 ? wgs : 1024;
+// 4096 waves at most (all resident), one row per wave and pass
+int rmsnorm_bwd_parts(int N, int C) {
+    const int nw = norm_bwd_waves(C >> 8);
+    const int wgs = (N + nw - 1) / nw, cap = 4096 / nw;
+    return wgs < cap ? wgs : cap;
 }
 
 template <typename E>
@@ -290,10 +301,10 @@ template <typename E>
 static hipError_t rmsnorm_bwd_t(const void* h, const void* g, const float* rstd, const void* dy,
                                 const void* dres, void* dh, float* dg, float* part, int N,
                                 int C, hipStream_t st) {
-    const int parts = rmsnorm_bwd_parts(N);
+    const int parts = rmsnorm_bwd_parts(N, C);
     hipError_t e = with_chunks(C >> 8, [&](auto K) {
         hipLaunchKernelGGL((rmsnorm_bwd_kernel<E, decltype(K)::value>), dim3((unsigned)parts),
-                           dim3(256), 0, st, (const E*)h, (const E*)g, rstd, (const E*)dy,
+                           dim3(64 * norm_bwd_waves(decltype(K)::value)), 0, st, (const E*)h, (const E*)g, rstd, (const E*)dy,
                            (const E*)dres, (E*)dh, part, N, C);
         return hipGetLastError();
     });

@@ -378,7 +378,8 @@ int attn_decode(const void* q, const void* cache, size_t cache_bytes,
 int attn_rmsnorm_fwd(const void* x, const void* res, const void* g, float eps,
                      void* h, void* y, float* rstd, int N, int C, int dtype, void* stream);
 
-/* attn_rmsnorm_bwd_workspace_bytes - min(ceil(N/4), 1024) * C fp32, rounded up to 256. */
+/* attn_rmsnorm_bwd_workspace_bytes - P * C fp32, rounded up to 256, with P = min(ceil(N/w),
+ * 4096/w) partial column sums, w = 16 for C <= 768 and 4 above. 0 for invalid arguments. */
 size_t attn_rmsnorm_bwd_workspace_bytes(int N, int C, int dtype);
 
 /*

@@ -310,8 +310,10 @@ def test_decode_entry_points_reject_bad_arguments(lib):
 
 
 def test_layer_entry_points_reject_bad_arguments(lib):
-    assert attn.attn_rmsnorm_bwd_workspace_bytes(8192, 768, 0) == 1024 * 768 * 4
-    assert attn.attn_rmsnorm_bwd_workspace_bytes(5, 256, 2) == 2 * 256 * 4
+    assert attn.attn_rmsnorm_bwd_workspace_bytes(8192, 768, 0) == 256 * 768 * 4
+    assert attn.attn_rmsnorm_bwd_workspace_bytes(8192, 1024, 0) == 1024 * 1024 * 4
+    assert attn.attn_rmsnorm_bwd_workspace_bytes(5, 256, 2) == 1 * 256 * 4
+    assert attn.attn_rmsnorm_bwd_workspace_bytes(33, 512, 0) == 3 * 512 * 4
     assert attn.attn_rmsnorm_bwd_workspace_bytes(5, 300, 0) == 0
     fb = dict(x=FAKE, res=FAKE + 16, g=FAKE + 32, eps=1e-5, h=FAKE + 48, y=FAKE + 64,
               rstd=FAKE + 80, N=4, C=256, dtype=0, stream=0)

@@ -63,7 +63,7 @@ def run_norm(x, r, g, dy, dres, dtype, eps=1e-5):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("N,C", [(1, 256), (3, 768), (37, 512), (130, 1024), (9, 4096)])
+@pytest.mark.parametrize("N,C", [(1, 256), (3, 768), (37, 512), (130, 1024), (9, 4096), (20001, 512)])
 @pytest.mark.parametrize("residual", [True, False])
 def test_rmsnorm(N, C, dtype, residual):
     x = workloads.layer_inputs("rmsnorm", N, C, dtype, seed=N + C)
