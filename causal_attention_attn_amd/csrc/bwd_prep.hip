@@ -60,10 +60,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const E* __restrict__ o,
         e0 = row * D + part * EPL;
         qk0 = e0;
     }
-    float acc = 0.f;
+    float acc = 0.f, nl = 0.f;
     if (valid) {
+        // lse is loaded with the rows, and the scheduling barrier keeps the
+        // compiler from issuing it only once o has arrived: a thread waits for
+        // one memory round trip, not two
+        if constexpr (HALF_LAYOUT) nl = lse[row];
         const u32x4 a = *reinterpret_cast<const u32x4*>(o + e0);
         const u32x4 b = *reinterpret_cast<const u32x4*>(dO + e0);
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (ROT) {
             const u32x4 wq = *reinterpret_cast<const u32x4*>(q + qk0);
             const u32x4 wk = *reinterpret_cast<const u32x4*>(k + qk0);
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const E* __restrict__ o,
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (valid && part == 0) {
         if constexpr (HALF_LAYOUT) {
-            ws[row] = -lse[row] * kLog2e;
+            ws[row] = -nl * kLog2e;
             ws[rows + row] = -acc;
         } else {
             ws[row] = acc;
