@@ -46,8 +46,11 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// One wave per row; lane l holds features 4l + 256j, j < NCH = C/256.
-template <typename E, int NCH>
+// One wave per row; lane l holds features 4l + 256j, j < NCH = C/256. RES: a
+// residual r is added first (a template argument, not a null test: a runtime
+// test splits every chunk's loads into branches, each ending in a wait for
+// memory). Every load of a row is issued before the first is waited for.
+template <typename E, int NCH, bool RES>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const E* __restrict__ x,
                                                           const E* __restrict__ r,
                                                           const E* __restrict__ g, float eps,
@@ -57,20 +60,25 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const E* __restrict__ 
     const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= N) return;
     const size_t base = (size_t)row * C + 4 * lane;
-    f32x4 v[NCH];
+    f32x4 v[NCH], rv[NCH], gg[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        v[j] = load4(x + base + 256 * j);
+        if constexpr (RES) rv[j] = load4(r + base + 256 * j);
+        gg[j] = load4(g + 4 * lane + 256 * j);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all loads before any arithmetic
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-        f32x4 a = load4(x + base + 256 * j);
-        if (r != nullptr) a = round4<E>(a + load4(r + base + 256 * j));
-        v[j] = a;
-        ss += a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3];
+        if constexpr (RES) v[j] = round4<E>(v[j] + rv[j]);
+        ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
     }
     const float rs = 1.f / sqrtf(wave_sum(ss) / (float)C + eps);
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         if (h != nullptr) store4(h + base + 256 * j, v[j]);
-        store4(y + base + 256 * j, v[j] * rs * load4(g + 4 * lane + 256 * j));
+        store4(y + base + 256 * j, v[j] * rs * gg[j]);
     }
     if (lane == 0) rstd[row] = rs;
 }
@@ -81,8 +89,10 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const E* __restrict__ 
 constexpr int norm_bwd_waves(int nch) { return nch <= 3 ? 16 : 4; }
 
 // One wave per row, rows grid-strided; each workgroup leaves its column sums of
-// dy * h^ in part[blockIdx.x][C] (fp32) for the dg reduction.
-template <typename E, int NCH>
+// dy * h^ in part[blockIdx.x][C] (fp32) for the dg reduction. RES: the residual
+// stream's own gradient dres is added to dh (a template argument for the reason
+// given at the forward kernel).
+template <typename E, int NCH, bool RES>
 __global__ __launch_bounds__(64 * norm_bwd_waves(NCH)) void rmsnorm_bwd_kernel(
     const E* __restrict__ h, const E* __restrict__ g, const float* __restrict__ rstd,
     const E* __restrict__ dy, const E* __restrict__ dres, E* __restrict__ dh,
@@ -108,37 +118,52 @@ __global__ __launch_bounds__(64 * norm_bwd_waves(NCH)) void rmsnorm_bwd_kernel(
         float rs[RP];
 #pragma unroll
         for (int q = 0; q < RP; ++q) {
-            const int row = row0 + q * stride;
-            if (row < N) {  // uniform
-                const size_t base = (size_t)row * C + 4 * lane;
-                rs[q] = rstd[row];
+            // a row past N loads row N-1 instead (never used): the loads of all
+            // RP rows then issue without a branch, and so without a wait, between
+            const int row = min(row0 + q * stride, N - 1);
+            const size_t base = (size_t)row * C + 4 * lane;
+            rs[q] = rstd[row];
 #pragma unroll
-                for (int j = 0; j < NCH; ++j) {
-                    hv[q][j] = load4(h + base + 256 * j);
-                    dv[q][j] = load4(dy + base + 256 * j);
-                    rv[q][j] = dres != nullptr ? load4(dres + base + 256 * j) : zero;
-                }
+            for (int j = 0; j < NCH; ++j) {
+                hv[q][j] = load4(h + base + 256 * j);
+                dv[q][j] = load4(dy + base + 256 * j);
+                rv[q][j] = RES ? load4(dres + base + 256 * j) : zero;
             }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // all loads of the pass before any arithmetic
+        if constexpr (RES) {
+            // a row's dres feeds only its conditional store; this empty use keeps
+            // the compiler from sinking those loads behind the earlier rows' work
+#pragma unroll
+            for (int q = 0; q < RP; ++q)
+#pragma unroll
+                for (int j = 0; j < NCH; ++j) asm volatile("" ::"v"(rv[q][j]));
         }
 #pragma unroll
         for (int q = 0; q < RP; ++q) {
             const int row = row0 + q * stride;
-            if (row >= N) break;  // uniform
+            // a row past N (uniform) is computed with rstd 0, which keeps it out
+            // of the column sums, and not stored; no branch before the
+            // arithmetic, or the compiler sinks this row's loads behind it
+            const bool live = row < N;
+            const float rq = live ? rs[q] : 0.f;
             const size_t base = (size_t)row * C + 4 * lane;
             f32x4 hh[NCH], gd[NCH];
             float dot = 0.f;
 #pragma unroll
             for (int j = 0; j < NCH; ++j) {
-                hh[j] = hv[q][j] * rs[q];
+                hh[j] = hv[q][j] * rq;
                 gd[j] = gg[j] * dv[q][j];
                 acc[j] += dv[q][j] * hh[j];
                 const f32x4 p = hh[j] * gd[j];
                 dot += p[0] + p[1] + p[2] + p[3];
             }
             const float mean = wave_sum(dot) / (float)C;
+            if (live) {
 #pragma unroll
-            for (int j = 0; j < NCH; ++j)
-                store4(dh + base + 256 * j, (gd[j] - hh[j] * mean) * rs[q] + rv[q][j]);
+                for (int j = 0; j < NCH; ++j)
+                    store4(dh + base + 256 * j, (gd[j] - hh[j] * mean) * rq + rv[q][j]);
+            }
         }
     }
     // the workgroup's column sums: its waves added through LDS in a fixed order,
@@ -242,12 +267,13 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const E* __restrict__ u,
 
 // Explicit instantiations: the host pass does not always emit the launch stub of
 // a kernel template with a 16-bit element-type argument on its own.
-#define ATTN_NORM_INST(E_, K_)                                                                  \
-    template __global__ void rmsnorm_fwd_kernel<E_, K_>(const E_*, const E_*, const E_*, float, \
-                                                        E_*, E_*, float*, int, int);            \
-    template __global__ void rmsnorm_bwd_kernel<E_, K_>(const E_*, const E_*, const float*,     \
-                                                        const E_*, const E_*, E_*, float*, int, \
-                                                        int);
+#define ATTN_NORM_INST_R(E_, K_, R_)                                                            \
+    template __global__ void rmsnorm_fwd_kernel<E_, K_, R_>(const E_*, const E_*, const E_*,    \
+                                                            float, E_*, E_*, float*, int, int);  \
+    template __global__ void rmsnorm_bwd_kernel<E_, K_, R_>(const E_*, const E_*, const float*, \
+                                                            const E_*, const E_*, E_*, float*,   \
+                                                            int, int);
+#define ATTN_NORM_INST(E_, K_) ATTN_NORM_INST_R(E_, K_, false) ATTN_NORM_INST_R(E_, K_, true)
 #define ATTN_NORM_INST_ALL(E_)                                                                  \
     ATTN_NORM_INST(E_, 1) ATTN_NORM_INST(E_, 2) ATTN_NORM_INST(E_, 3) ATTN_NORM_INST(E_, 4)     \
     ATTN_NORM_INST(E_, 5) ATTN_NORM_INST(E_, 6) ATTN_NORM_INST(E_, 7) ATTN_NORM_INST(E_, 8)     \
@@ -256,6 +282,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const E* __restrict__ u,
 ATTN_NORM_INST_ALL(bf16) ATTN_NORM_INST_ALL(f16)
 #undef ATTN_NORM_INST_ALL
 #undef ATTN_NORM_INST
+#undef ATTN_NORM_INST_R
 template __global__ void swiglu_kernel<bf16, false>(const bf16*, const bf16*, bf16*, long long, int);
 template __global__ void swiglu_kernel<bf16, true>(const bf16*, const bf16*, bf16*, long long, int);
 template __global__ void swiglu_kernel<f16, false>(const f16*, const f16*, f16*, long long, int);
@@ -283,9 +310,16 @@ template <typename E>
 static hipError_t rmsnorm_fwd_t(const void* x, const void* r, const void* g, float eps, void* h,
                                 void* y, float* rstd, int N, int C, hipStream_t st) {
     return with_chunks(C >> 8, [&](auto K) {
-        hipLaunchKernelGGL((rmsnorm_fwd_kernel<E, decltype(K)::value>),
-                           dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, (const E*)x,
-                           (const E*)r, (const E*)g, eps, (E*)h, (E*)y, rstd, N, C);
+        constexpr int NCH = decltype(K)::value;
+        const dim3 grid((unsigned)((N + 3) / 4));
+        if (r != nullptr)
+            hipLaunchKernelGGL((rmsnorm_fwd_kernel<E, NCH, true>), grid, dim3(256), 0, st,
+                               (const E*)x, (const E*)r, (const E*)g, eps, (E*)h, (E*)y, rstd, N,
+                               C);
+        else
+            hipLaunchKernelGGL((rmsnorm_fwd_kernel<E, NCH, false>), grid, dim3(256), 0, st,
+                               (const E*)x, (const E*)r, (const E*)g, eps, (E*)h, (E*)y, rstd, N,
+                               C);
         return hipGetLastError();
     });
 }
@@ -303,9 +337,16 @@ static hipError_t rmsnorm_bwd_t(const void* h, const void* g, const float* rstd,
                                 int C, hipStream_t st) {
     const int parts = rmsnorm_bwd_parts(N, C);
     hipError_t e = with_chunks(C >> 8, [&](auto K) {
-        hipLaunchKernelGGL((rmsnorm_bwd_kernel<E, decltype(K)::value>), dim3((unsigned)parts),
-                           dim3(64 * norm_bwd_waves(decltype(K)::value)), 0, st, (const E*)h, (const E*)g, rstd, (const E*)dy,
-                           (const E*)dres, (E*)dh, part, N, C);
+        constexpr int NCH = decltype(K)::value;
+        const dim3 grid((unsigned)parts), block(64 * norm_bwd_waves(NCH));
+        if (dres != nullptr)
+            hipLaunchKernelGGL((rmsnorm_bwd_kernel<E, NCH, true>), grid, block, 0, st,
+                               (const E*)h, (const E*)g, rstd, (const E*)dy, (const E*)dres,
+                               (E*)dh, part, N, C);
+        else
+            hipLaunchKernelGGL((rmsnorm_bwd_kernel<E, NCH, false>), grid, block, 0, st,
+                               (const E*)h, (const E*)g, rstd, (const E*)dy, (const E*)dres,
+                               (E*)dh, part, N, C);
         return hipGetLastError();
     });
     if (e != hipSuccess) return e;
