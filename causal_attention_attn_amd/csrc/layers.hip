@@ -130,14 +130,19 @@ __global__ __launch_bounds__(64 * norm_bwd_waves(NCH)) void rmsnorm_bwd_kernel(
                 rv[q][j] = RES ? load4(dres + base + 256 * j) : zero;
             }
         }
-        __builtin_amdgcn_sched_barrier(0);  // all loads of the pass before any arithmetic
-        if constexpr (RES) {
-            // a row's dres feeds only its conditional store; this empty use keeps
-            // the compiler from sinking those loads behind the earlier rows' work
+        if constexpr (NCH <= 4) {
+            // all loads of the pass before any arithmetic (for wider rows holding
+            // them all at once costs more registers than it saves waiting)
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (RES) {
+                // a row's dres feeds only its conditional store; this empty use
+                // keeps the compiler from sinking those loads behind the earlier
+                // rows' work
 #pragma unroll
-            for (int q = 0; q < RP; ++q)
+                for (int q = 0; q < RP; ++q)
 #pragma unroll
-                for (int j = 0; j < NCH; ++j) asm volatile("" ::"v"(rv[q][j]));
+                    for (int j = 0; j < NCH; ++j) asm volatile("" ::"v"(rv[q][j]));
+            }
         }
 #pragma unroll
         for (int q = 0; q < RP; ++q) {
