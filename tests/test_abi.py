@@ -105,6 +105,7 @@ def test_fwd_rejects_bad_arguments(lib):
     assert f(T=0) == 2
     assert f(B=0) == 2
     assert f(B=1 << 16, H=1 << 10, T=1 << 10) == 2      # 2^42 elements
+    assert f(B=1, H=2048, T=8192, D=128) == 2           # exactly 2^31 elements per tensor
     assert f(dtype=3) == 3
     assert f(k=MIS) == 4
     assert f(o=A(0)) == 7                                 # o is q

@@ -112,6 +112,42 @@ def test_backward_reads_its_own_q_and_k():
     assert not torch.equal(dq2.cpu(), got["dq"])
 
 
+def test_maximum_size_sampled_heads():
+    """The largest [B, H, T, D] tensor the entry points accept (one head short of
+    2^31 elements: B1 H2047 T8192 D128, bf16, about 45 GB on the GPU with the
+    outputs, the saved buffer and the workspace) through the training pair. Three
+    heads (first, middle, last) are checked against the oracle element by element;
+    every head is checked for finite outputs and for o's first row being exactly v's
+    first row (the first query attends to key 0 alone). Inputs are drawn on the GPU
+    from a seeded generator, with the headline workload's distributions."""
+    B, H, T, D = 1, 2047, 8192, 128
+    assert B * H * T * D < 2 ** 31 <= B * (H + 1) * T * D
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(2047)
+    shape = (B, H, T, D)
+    q = torch.randn(shape, generator=g, device=dev, dtype=torch.bfloat16)
+    k = torch.randn(shape, generator=g, device=dev, dtype=torch.bfloat16)
+    v = torch.randn(shape, generator=g, device=dev, dtype=torch.bfloat16)
+    do = (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * 0.1).to(torch.bfloat16)
+    print("maximum size: inputs drawn", flush=True)
+    o, lse, saved = attn.forward(q, k, v, save=True)
+    dq, dk, dv = attn.backward(q, k, v, o, do, lse, saved)
+    torch.cuda.synchronize()
+    print("maximum size: GPU forward and backward done", flush=True)
+    for n, t in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv).items():
+        assert bool(torch.isfinite(t).all()), f"{n} has non-finite values"
+    assert torch.equal(o[:, :, 0], v[:, :, 0])
+    del saved
+    heads = [(0, 0), (0, H // 2), (0, H - 1)]
+    x = {n: torch.stack([t[b, h] for b, h in heads])[None].cpu() for n, t in
+         dict(q=q, k=k, v=v, do=do).items()}
+    got = {n: torch.stack([t[b, h] for b, h in heads])[None].cpu() for n, t in
+           dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv).items()}
+    print("maximum size: oracle on 3 heads", flush=True)
+    assert_close(got, oracle_run(x), "bf16", "maximum size B1 H2047 T8192 D128, heads 0, 1023, 2046")
+
+
 def test_row_zero_is_v_zero_bitwise():
     w = workloads.WORKLOADS[workloads.HEADLINE]
     for D in (64, 128):
