@@ -1,7 +1,8 @@
 """attn_bwd_saved_noalloc, the backward that allocates nothing (its per-row
 entries live in the library's static device array), against attn_bwd_saved with
 a caller workspace: bitwise the same gradients, on two calls in a row (the
-second on a smaller problem, over the array the first one left behind)."""
+second on a smaller problem, over the array the first one left behind); and the
+training pair built on it captured into a HIP graph and replayed."""
 
 import pytest
 
@@ -73,3 +74,62 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     with pytest.raises(attn.AttnError) as e:
         attn.attn_bwd_saved_noalloc(t, t, t, t, t, t, t, t, t, ns, t, t, t, B, H, T, D, 0)
     assert e.value.status == 10
+
+
+def test_noalloc_training_pair_in_a_hip_graph():
+    """The training pair with nothing allocated inside it (attn_fwd_save into caller
+    buffers, then attn_bwd_saved_noalloc) captured into a HIP graph, the use these
+    entry points serve. Every replay, with eager launches and synchronisations
+    between the replays, gives bitwise the eager outputs; after an input changes in
+    place, a replay gives bitwise the new eager outputs (the graph reads its inputs
+    when it runs). Only the library's kernel launches are captured."""
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    B, H, T, D = 2, 3, 700, 64
+    x = workloads.make(w, seed=11, shape=(B, H, T, D))
+    dev = torch.device("cuda", 0)
+    g = {n: t.to(dev) for n, t in x.items()}
+    q, k, v, do = g["q"], g["k"], g["v"], g["do"]
+    cs, sn = attn.rope_tables(T, D, 10000.0, dev)
+    ns = attn.attn_saved_bytes(B, H, T, D, 0)
+    saved = torch.empty(ns, dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    outs = (o, lse, dq, dk, dv)
+    names = ("o", "lse", "dq", "dk", "dv")
+
+    def step():
+        attn.attn_fwd_save(q, k, v, cs, sn, o, lse, saved, ns, B, H, T, D, 0)
+        attn.attn_bwd_saved_noalloc(q, k, v, o, do, lse, cs, sn, saved, ns, dq, dk, dv,
+                                    B, H, T, D, 0)
+
+    def spoil():
+        # eager work between replays: a fill kernel over every output
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+
+    step()  # eager warm-up: the scratch address and the CU count are looked up here
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        spoil()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b, n in zip(outs, ref, names):
+            assert torch.equal(a, b), (r, n)
+    v.mul_(0.5)
+    step()
+    torch.cuda.synchronize()
+    ref2 = [t.clone() for t in outs]
+    assert not torch.equal(ref2[0], ref[0])
+    for r in range(2):
+        spoil()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b, n in zip(outs, ref2, names):
+            assert torch.equal(a, b), ("after the input changed", r, n)
