@@ -211,6 +211,33 @@ def test_rope_table_kernel():
         np.testing.assert_allclose(sn.cpu().double().numpy(), np.sin(ang), rtol=0, atol=1e-7)
 
 
+def test_binding_rejects_before_any_launch():
+    """The Python helpers check what the C ABI cannot see (tensor devices, a saved
+    buffer's real size, lse's dtype and device) and raise ValueError before they
+    allocate outputs or launch anything."""
+    dev = torch.device("cuda", 0)
+    q = torch.randn((1, 2, 40, 64), device=dev).to(torch.bfloat16)
+    o, lse, saved = attn.forward(q, q, q)
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError):  # a saved buffer shorter than these inputs need
+        attn.backward(q, q, q, o, q, lse, saved[:-256])
+    with pytest.raises(ValueError):  # saved on the host
+        attn.backward(q, q, q, o, q, lse, saved.cpu())
+    with pytest.raises(ValueError):  # lse on the host
+        attn.backward(q, q, q, o, q, lse.cpu(), saved)
+    with pytest.raises(ValueError):  # lse of another dtype
+        attn.backward(q, q, q, o, q, lse.double(), saved)
+    cache = attn.KVCache(1, 2, 64, 64, dtype=torch.bfloat16, device=dev)
+    kv = torch.zeros((1, 2, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # host k, v
+        cache.append(kv, kv, 0)
+    with pytest.raises(ValueError):  # host q
+        cache.decode(torch.zeros((1, 2, 64), dtype=torch.bfloat16), 3)
+    with pytest.raises(ValueError):  # host q, k, v for a fused step
+        x = torch.zeros((1, 2, 64), dtype=torch.bfloat16)
+        cache.step(x, x, x, 3)
+
+
 def test_abi_errors_on_gpu():
     q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="cuda")
     cs, sn = attn.rope_tables(8, 64, 10000.0, "cuda:0")
