@@ -93,17 +93,19 @@ def backward(q, k, v, o, do, lse, saved=None, base=10000.0):
     B, H, T, D = _shape(q, k, v, o, do)
     dt = _dtype_code(q)
     _check_lse(lse, B, H, T, q.device)
+    nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
+    use_saved = saved is not None and nsaved != 0
+    sv, nsv = _saved_arg(saved, nsaved, q.device) if use_saved else (None, 0)
+    # every argument is checked; only now is anything allocated or launched
     cs, sn = rope_tables(T, D, base, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nbytes = _lib.attn_bwd_workspace_bytes(B, H, T, D, dt)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
-    if saved is None or nsaved == 0:
-        _lib.attn_bwd(q, k, v, o, do, lse, cs, sn, dq, dk, dv, ws, nbytes, B, H, T, D, dt)
-    else:
-        sv, nsv = _saved_arg(saved, nsaved, q.device)
+    if use_saved:
         _lib.attn_bwd_saved(q, k, v, o, do, lse, cs, sn, sv, nsv, dq, dk, dv, ws, nbytes,
                             B, H, T, D, dt)
+    else:
+        _lib.attn_bwd(q, k, v, o, do, lse, cs, sn, dq, dk, dv, ws, nbytes, B, H, T, D, dt)
     return dq, dk, dv
 
 
@@ -143,10 +145,11 @@ def backward_packed(qkv, o, do, lse, saved=None, base=10000.0):
                              "device")
     dt = _dtype_code(qkv)
     _check_lse(lse, B, H, T, qkv.device)
-    cs, sn = rope_tables(T, D, base, qkv.device)
-    dqkv = torch.empty_like(qkv)
     nsaved = _lib.attn_saved_bytes(B, H, T, D, dt)
     sv, nsv = (None, 0) if saved is None else _saved_arg(saved, nsaved, qkv.device)
+    # every argument is checked; only now is anything allocated or launched
+    cs, sn = rope_tables(T, D, base, qkv.device)
+    dqkv = torch.empty_like(qkv)
     nbytes = _lib.attn_bwd_workspace_bytes(B, H, T, D, dt)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=qkv.device)
     _lib.attn_bwd_packed(qkv, o, do, lse, cs, sn, sv, nsv, dqkv, ws, nbytes, B, H, T, D, dt)
