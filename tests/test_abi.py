@@ -373,3 +373,33 @@ def test_rope_tables_reject_bad_arguments(lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load(str(tmp_path / "libattn.so"))
+
+
+def _readme_blocks(lang):
+    readme = os.path.join(os.path.dirname(HEADER), os.pardir, "README.md")
+    return re.findall(r"```" + lang + r"\n(.*?)```", open(readme).read(), re.S)
+
+
+def test_readme_examples_compile(tmp_path):
+    """The usage examples stay in step with the header and the binding: the C one
+    compiles against include/attn.h with warnings as errors, and the Python one
+    parses and names only functions the binding has."""
+    import ast
+    import shutil
+    import subprocess
+    (c_src,) = _readme_blocks("c")
+    (py_src,) = _readme_blocks("python")
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "example.c"
+    src.write_text(c_src)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-c",
+                        "-I", os.path.dirname(HEADER), str(src), "-o", str(tmp_path / "e.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    tree = ast.parse(py_src)
+    used = {n.attr for n in ast.walk(tree)
+            if isinstance(n, ast.Attribute) and isinstance(n.value, ast.Name)
+            and n.value.id == "attn"}
+    assert used and all(hasattr(attn, a) for a in used), used
