@@ -265,6 +265,21 @@ __global__ __launch_bounds__(64 * kHeadWaves<D>()) void decode_head_kernel(
     const uint32_t bytes = (uint32_t)(APPEND ? pos : pos + 1) * D * 2;
     const rsrc_t kb = make_rsrc(kc + (size_t)bh * Tmax * D, bytes);
     const rsrc_t vb = make_rsrc(vc + (size_t)bh * Tmax * D, bytes);
+    // the K' and V rows of a slice: rows past the buffers' ends read as zeros
+    u32x4 kr[NI], vr[NI];
+    auto load_slice = [&](int u0) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t off = (uint32_t)((u0 + i * RPI + rl) * D + 8 * cc) * 2;
+            kr[i] = buf_load16(kb, off);
+            vr[i] = buf_load16(vb, off);
+        }
+    };
+    // the wave's first slice is requested before the query (a wave without
+    // slices reads zeros and never uses them), so the two loads share one
+    // memory round trip instead of taking two in turn
+    load_slice(wave * kSlice);
+    __builtin_amdgcn_sched_barrier(0);
 
     // this lane's chunk of the query: R_pos q scaled by log2(e)/sqrt(D), fp16
     const u32x4 wq = *reinterpret_cast<const u32x4*>(q + (size_t)bh * D + 8 * cc);
@@ -282,13 +297,7 @@ __global__ __launch_bounds__(64 * kHeadWaves<D>()) void decode_head_kernel(
     float oa[8] = {};
     for (int sl = wave; sl < nsplit; sl += nw) {
         const int u0 = sl * kSlice;
-        u32x4 kr[NI], vr[NI];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const uint32_t off = (uint32_t)((u0 + i * RPI + rl) * D + 8 * cc) * 2;
-            kr[i] = buf_load16(kb, off);
-            vr[i] = buf_load16(vb, off);
-        }
+        if (sl != wave) load_slice(u0);
         if constexpr (APPEND) {
             if (pos - u0 < kSlice) {  // uniform: this slice holds the new row
                 const int r = pos - u0;
