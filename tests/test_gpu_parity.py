@@ -112,12 +112,12 @@ def test_backward_reads_its_own_q_and_k():
     assert not torch.equal(dq2.cpu(), got["dq"])
 
 
-@pytest.mark.parametrize("H,D", [(4095, 64), (2047, 128)])
-def test_maximum_size_sampled_heads(H, D):
+@pytest.mark.parametrize("dtype,H,D", [("bf16", 4095, 64), ("bf16", 2047, 128), ("f16", 4095, 64)])
+def test_maximum_size_sampled_heads(dtype, H, D):
     """The largest [B, H, T, D] tensors the entry points accept (one head short of
-    2^31 elements at T = 8192: H4095 at D = 64, H2047 at D = 128; bf16, about 45 GB
-    on the GPU with the outputs, the saved buffer and the workspace) through the
-    training pair. Three heads (first, middle, last) are checked against the oracle
+    2^31 elements at T = 8192: H4095 at D = 64, H2047 at D = 128; bf16, and fp16
+    storage at D = 64; about 45 GB on the GPU with the outputs, the saved buffer
+    and the workspace) through the training pair. Three heads (first, middle, last) are checked against the oracle
     element by element; every head is checked for finite outputs and for o's first
     row being exactly v's first row (the first query attends to key 0 alone). Inputs
     are drawn on the GPU from a seeded generator, with the headline workload's
@@ -126,12 +126,13 @@ def test_maximum_size_sampled_heads(H, D):
     assert B * H * T * D < 2 ** 31 <= B * (H + 1) * T * D
     dev = torch.device("cuda", 0)
     g = torch.Generator(device=dev)
-    g.manual_seed(H)
+    g.manual_seed(H + (dtype == "f16"))
     shape = (B, H, T, D)
-    q = torch.randn(shape, generator=g, device=dev, dtype=torch.bfloat16)
-    k = torch.randn(shape, generator=g, device=dev, dtype=torch.bfloat16)
-    v = torch.randn(shape, generator=g, device=dev, dtype=torch.bfloat16)
-    do = (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * 0.1).to(torch.bfloat16)
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    q = torch.randn(shape, generator=g, device=dev, dtype=dt)
+    k = torch.randn(shape, generator=g, device=dev, dtype=dt)
+    v = torch.randn(shape, generator=g, device=dev, dtype=dt)
+    do = (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * 0.1).to(dt)
     print("maximum size: inputs drawn", flush=True)
     o, lse, saved = attn.forward(q, k, v, save=True)
     dq, dk, dv = attn.backward(q, k, v, o, do, lse, saved)
@@ -149,7 +150,7 @@ def test_maximum_size_sampled_heads(H, D):
     print("maximum size: oracle on 3 heads", flush=True)
     del q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()  # the 45 GB go back before the next test
-    assert_close(got, oracle_run(x), "bf16", f"maximum size B1 H{H} T8192 D{D}, heads {heads}")
+    assert_close(got, oracle_run(x), dtype, f"maximum size {dtype} B1 H{H} T8192 D{D}, heads {heads}")
 
 
 def test_row_zero_is_v_zero_bitwise():
