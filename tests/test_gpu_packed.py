@@ -84,3 +84,47 @@ def test_packed_writes_nothing_outside_its_outputs():
         assert torch.isfinite(buf[pad:pad + n].float()).all()
     ref = gpu_run(x)
     assert torch.equal(o.view(B, T, H, D).permute(0, 2, 1, 3).cpu(), ref["o"])
+
+
+@pytest.mark.parametrize("H,D", [(1365, 64), (682, 128)])
+def test_packed_maximum_size(H, D):
+    """The largest packed tensor the packed entry points accept: one head short of
+    2^31 elements in [B, T, 3, H, D] at T = 8192 (H1365 at D = 64, H682 at D = 128),
+    bf16. Every output is bitwise that of the [B, H, T, D] entry points on the same
+    values, three heads are checked against the oracle, and o's first row is v's.
+    Inputs are drawn on the GPU from a seeded generator."""
+    B, T = 1, 8192
+    assert 3 * B * H * T * D < 2 ** 31 <= 3 * B * (H + 1) * T * D
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(H + D)
+    qkv = torch.randn((B, T, 3, H, D), generator=g, device=dev, dtype=torch.bfloat16)
+    do = (torch.randn((B, T, H, D), generator=g, device=dev, dtype=torch.float32) * 0.1).to(
+        torch.bfloat16)
+    print(f"packed maximum size H{H} D{D}: inputs drawn", flush=True)
+    o, lse, saved = attn.forward_packed(qkv, save=True)
+    dqkv = attn.backward_packed(qkv, o, do, lse, saved)
+    torch.cuda.synchronize()
+    del saved
+    print("packed maximum size: packed forward and backward done", flush=True)
+    bhtd = lambda t: t.permute(0, 2, 1, 3).contiguous()
+    q, k, v, dob = bhtd(qkv[:, :, 0]), bhtd(qkv[:, :, 1]), bhtd(qkv[:, :, 2]), bhtd(do)
+    o2, lse2, saved2 = attn.forward(q, k, v, save=True)
+    dq2, dk2, dv2 = attn.backward(q, k, v, o2, dob, lse2, saved2)
+    torch.cuda.synchronize()
+    del saved2
+    print("packed maximum size: [B, H, T, D] forward and backward done", flush=True)
+    assert torch.equal(bhtd(o), o2) and torch.equal(lse, lse2)
+    for s, (n, ref) in enumerate(zip(("dq", "dk", "dv"), (dq2, dk2, dv2))):
+        assert torch.equal(bhtd(dqkv[:, :, s]), ref), n
+    for n, t in dict(o=o2, lse=lse2, dq=dq2, dk=dk2, dv=dv2).items():
+        assert bool(torch.isfinite(t).all()), f"{n} has non-finite values"
+    assert torch.equal(o2[:, :, 0], v[:, :, 0])
+    heads = [(0, 0), (0, H // 2), (0, H - 1)]
+    pick = lambda t: torch.stack([t[b, h] for b, h in heads])[None].cpu()
+    x = {n: pick(t) for n, t in dict(q=q, k=k, v=v, do=dob).items()}
+    got = {n: pick(t) for n, t in dict(o=o2, lse=lse2, dq=dq2, dk=dk2, dv=dv2).items()}
+    del qkv, do, o, lse, dqkv, q, k, v, dob, o2, lse2, dq2, dk2, dv2
+    torch.cuda.empty_cache()
+    print("packed maximum size: oracle on 3 heads", flush=True)
+    assert_close(got, oracle_run(x), "bf16", f"packed maximum size B1 H{H} T8192 D{D}, heads {heads}")
