@@ -232,3 +232,44 @@ def test_fused_step_many_heads(D, Tmax, dtype):
         prev = pos + 1
     torch.cuda.synchronize()
     assert torch.equal(a.buf, b.buf)
+
+
+def test_decode_maximum_size():
+    """The largest cache the decode calls accept: one head short of 2^31 elements
+    per [B, H, Tmax, D] half at Tmax = 8192 (B1 H4095 D64, bf16; 17 GB of cache).
+    All 8192 positions are appended in one call; decode at the last position is
+    checked against the oracle on three heads (first, middle, last), and the
+    fused step at that position (the first 8191 rows appended into a second
+    cache) gives bitwise the same o, lse and cache rows. Inputs are drawn on the
+    GPU from a seeded generator."""
+    B, H, Tmax, D = 1, 4095, 8192, 64
+    assert B * H * Tmax * D < 2 ** 31 <= B * (H + 1) * Tmax * D
+    pos = Tmax - 1
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4095)
+    k = torch.randn((B, H, Tmax, D), generator=g, device=DEV, dtype=torch.bfloat16)
+    v = torch.randn((B, H, Tmax, D), generator=g, device=DEV, dtype=torch.bfloat16)
+    q = torch.randn((B, H, D), generator=g, device=DEV, dtype=torch.bfloat16)
+    print("decode maximum size: inputs drawn", flush=True)
+    a = attn.KVCache(B, H, Tmax, D, torch.bfloat16, DEV)
+    a.append(k, v, 0)
+    oa, la = a.decode(q, pos)
+    torch.cuda.synchronize()
+    print("decode maximum size: append and decode done", flush=True)
+    b = attn.KVCache(B, H, Tmax, D, torch.bfloat16, DEV)
+    b.append(k[:, :, :pos].contiguous(), v[:, :, :pos].contiguous(), 0)
+    ob, lb = b.step(q, k[:, :, pos].contiguous(), v[:, :, pos].contiguous(), pos)
+    torch.cuda.synchronize()
+    print("decode maximum size: fused step done", flush=True)
+    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    assert torch.equal(a.buf, b.buf)
+    del b
+    assert bool(torch.isfinite(oa).all()) and bool(torch.isfinite(la).all())
+    heads = [0, H // 2, H - 1]
+    f = lambda t: workloads.as_float64(t[:, heads].cpu())
+    ro, rl = oracle.attention_decode(f(q), f(k), f(v), pos)
+    o3, l3 = f(oa), la[:, heads].cpu().numpy().astype(np.float64)
+    mx, rel = errors(o3, ro)
+    assert mx <= TOL["bf16"]["max_abs"] and rel <= TOL["bf16"]["rel_l2"], (mx, rel)
+    lmx, _ = errors(l3, rl)
+    assert lmx <= 1e-2 + 1e-3 * float(np.max(np.abs(rl))), lmx
