@@ -132,3 +132,60 @@ def test_swiglu_full_workload_and_extremes():
     out, du = run_swiglu(u, torch.ones((1, 8), dtype=torch.bfloat16), "bf16")
     close(out, oracle.swiglu_forward(f64(u)), "bf16", "swiglu extremes out")
     close(du, oracle.swiglu_backward(f64(u), np.ones((1, 8))), "bf16", "swiglu extremes du")
+
+
+def test_layers_maximum_size():
+    """The largest tensors the per-layer calls accept: N*C one row short of 2^31
+    elements for RMSNorm (N 524287, C 4096, with the residual) and 2*N*F for
+    SwiGLU (N 262143, F 4096), bf16. Rows are independent in both forwards, in
+    the RMSNorm dh and in SwiGLU's du, so the first, middle and last rows are
+    checked against the oracle; h must be the rounded x + r bitwise everywhere,
+    and every output finite. Inputs are drawn on the GPU from a seeded generator."""
+    dt, code = torch.bfloat16, CODE["bf16"]
+    g_ = torch.Generator(device=DEV)
+    g_.manual_seed(2 ** 31 - 1)
+    rnd = lambda *s: torch.randn(s, generator=g_, device=DEV, dtype=torch.float32)
+    N, C = 524287, 4096
+    assert N * C < 2 ** 31 <= (N + 1) * C
+    x, r = rnd(N, C).to(dt), rnd(N, C).to(dt)
+    dy, dres = (rnd(N, C) * 0.1).to(dt), (rnd(N, C) * 0.1).to(dt)
+    gain = (1.0 + 0.1 * rnd(C)).to(dt)
+    h, y, dh = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    rstd = torch.empty(N, dtype=torch.float32, device=DEV)
+    dg = torch.empty(C, dtype=torch.float32, device=DEV)
+    attn.attn_rmsnorm_fwd(x, r, gain, 1e-5, h, y, rstd, N, C, code)
+    nw = attn.attn_rmsnorm_bwd_workspace_bytes(N, C, code)
+    ws = torch.empty(nw, dtype=torch.uint8, device=DEV)
+    attn.attn_rmsnorm_bwd(h, gain, rstd, dy, dres, dh, dg, ws, nw, N, C, code)
+    torch.cuda.synchronize()
+    print("layers maximum size: RMSNorm done", flush=True)
+    assert torch.equal(h, (x.float() + r.float()).to(dt))
+    for n, t in dict(y=y, rstd=rstd, dh=dh, dg=dg).items():
+        assert bool(torch.isfinite(t).all()), f"rmsnorm {n} has non-finite values"
+    rows = [0, 1, N // 2, N - 2, N - 1]
+    pick = lambda t: t[rows].cpu()
+    hs, gs = f64(pick(h)), f64(gain.cpu())
+    _, ry, rr = oracle.rmsnorm_forward(hs, gs)
+    rdh, _ = oracle.rmsnorm_backward(hs, gs, f64(pick(dy)), dres=f64(pick(dres)))
+    close(pick(y), ry, "bf16", "rmsnorm maximum size y")
+    np.testing.assert_allclose(f64(pick(rstd)), rr, rtol=1e-5)
+    close(pick(dh), rdh, "bf16", "rmsnorm maximum size dh")
+    del x, r, dy, dres, h, y, dh, ws
+    torch.cuda.empty_cache()
+
+    N, F = 262143, 4096
+    assert 2 * N * F < 2 ** 31 <= 2 * (N + 1) * F
+    u = rnd(N, 2 * F).to(dt)
+    dout = (rnd(N, F) * 0.1).to(dt)
+    out, du = torch.empty((N, F), dtype=dt, device=DEV), torch.empty_like(u)
+    attn.attn_swiglu_fwd(u, out, N, F, code)
+    attn.attn_swiglu_bwd(u, dout, du, N, F, code)
+    torch.cuda.synchronize()
+    print("layers maximum size: SwiGLU done", flush=True)
+    for n, t in dict(out=out, du=du).items():
+        assert bool(torch.isfinite(t).all()), f"swiglu {n} has non-finite values"
+    rows = [0, 1, N // 2, N - 2, N - 1]
+    us = f64(u[rows].cpu())
+    close(out[rows].cpu(), oracle.swiglu_forward(us), "bf16", "swiglu maximum size out")
+    close(du[rows].cpu(), oracle.swiglu_backward(us, f64(dout[rows].cpu())), "bf16",
+          "swiglu maximum size du")
