@@ -387,14 +387,31 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
     // the remaining steps reach the diagonal; with three stages the last one is
     // peeled off (it copies the RoPE table rows for the epilogue into LDS)
     constexpr bool TAB = NS == 3;
-    for (; n + (TAB ? 1 : 0) < ntiles; ++n) {
-        const int stg = n % NS;
-        if (stg == 0)
+    if constexpr (TAB) {
+        // at most NS-1 full tiles and one of the two diagonal tiles precede the
+        // last step, on stages 0, 1, 2 in turn: straight-line steps with
+        // compile-time stages (a loop that picks the stage at run time makes the
+        // compiler copy the accumulators between its branches)
+        static_assert(C::QM / C::KN == 2, "two diagonal key tiles per q-block");
+        if (n + 1 < ntiles) {
             dq_step<D, E, 0, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
-        else if (stg == 1)
+            ++n;
+        }
+        if (n + 1 < ntiles) {
             dq_step<D, E, 1, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
-        else if constexpr (NS > 2)
+            ++n;
+        }
+        if (n + 1 < ntiles) {
             dq_step<D, E, 2, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
+            ++n;
+        }
+    } else {
+        for (; n < ntiles; ++n) {
+            if (n % NS == 0)
+                dq_step<D, E, 0, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
+            else
+                dq_step<D, E, 1, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
+        }
     }
     if constexpr (TAB) {
         // the last step and the epilogue, with the last step's ring stage L a
@@ -613,28 +630,54 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
     constexpr bool TAB = NS == 3;
     const int qlast = TAB ? nqt - 1 : nqt;
     int qt = qt0;
-    for (; qt < min(qfull, qlast); ++qt) {
-        const int stg = (qt - qt0) % NS;
-        if (stg == 0) dkdv_step<D, E, 0, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if (stg == 1) dkdv_step<D, E, 1, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if constexpr (NS > 2) dkdv_step<D, E, 2, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-    }
-    // the full tiles, rotated so that the unrolled body starts on stage 0
-    for (; qt < qlast && (qt - qt0) % NS != 0; ++qt) {
-        const int stg = (qt - qt0) % NS;
-        if (stg == 1) dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if constexpr (NS > 2) dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+    if constexpr (TAB) {
+        // straight-line steps with compile-time stages wherever the stage is
+        // known (see dq_item): the diagonal tiles (at most two, stages 0 and 1),
+        // then full tiles up to the next stage 0
+        static_assert(C::KM / C::QN == 2, "two diagonal query tiles per key block");
+        const int qd = min(qfull, qlast);
+        if (qt < qd) {
+            dkdv_step<D, E, 0, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+            ++qt;
+        }
+        if (qt < qd) {
+            dkdv_step<D, E, 1, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+            ++qt;
+        }
+        if (qt < qlast && qt - qt0 == 1) {
+            dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+            ++qt;
+        }
+        if (qt < qlast && qt - qt0 == 2) {
+            dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+            ++qt;
+        }
+    } else {
+        for (; qt < min(qfull, qlast); ++qt) {
+            if ((qt - qt0) % NS == 0) dkdv_step<D, E, 0, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+            else dkdv_step<D, E, 1, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        }
+        // the full tiles, rotated so that the unrolled body starts on stage 0
+        if (qt < qlast && (qt - qt0) % NS != 0) {
+            dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+            ++qt;
+        }
     }
     for (; qt + NS <= qlast; qt += NS) {
         dkdv_step<D, E, 0, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
         dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt + 1, nqt);
         if constexpr (NS > 2) dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt + 2, nqt);
     }
-    for (; qt < qlast; ++qt) {
-        const int stg = (qt - qt0) % NS;
-        if (stg == 0) dkdv_step<D, E, 0, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if (stg == 1) dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        else if constexpr (NS > 2) dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+    // at most NS-1 full tiles remain, from stage 0
+    if (qt < qlast) {
+        dkdv_step<D, E, 0, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+        ++qt;
+    }
+    if constexpr (NS > 2) {
+        if (qt < qlast) {
+            dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+            ++qt;
+        }
     }
     if constexpr (TAB) {
         // the last step (it may also be a diagonal one: the diagonal variant
