@@ -406,12 +406,14 @@ __device__ __forceinline__ void dq_item(const BwdPtrs<E>& pp, const Ring& rg, in
             ++n;
         }
     } else {
-        for (; n < ntiles; ++n) {
-            if (n % NS == 0)
-                dq_step<D, E, 0, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
-            else
-                dq_step<D, E, 1, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
-        }
+        // two stages, no peeled step: at most one full tile and the two diagonal
+        // tiles remain, on stages 0, 1, 0
+        static_for<3>([&](auto S) {
+            if (n < ntiles) {
+                dq_step<D, E, S % NS, true, STRIDED>(acc, qf, df, rg, ld, of, kh, vh, vst, T, n, ntiles, wq0, lane, wave, nl, nd);
+                ++n;
+            }
+        });
     }
     if constexpr (TAB) {
         // the last step and the epilogue, with the last step's ring stage L a
@@ -630,7 +632,7 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
     constexpr bool TAB = NS == 3;
     const int qlast = TAB ? nqt - 1 : nqt;
     int qt = qt0;
-    if constexpr (TAB) {
+    {
         // straight-line steps with compile-time stages wherever the stage is
         // known (see dq_item): the diagonal tiles (at most two, stages 0 and 1),
         // then full tiles up to the next stage 0
@@ -648,19 +650,11 @@ __device__ __forceinline__ void dkdv_item(const BwdPtrs<E>& pp, const Ring& rg, 
             dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
             ++qt;
         }
-        if (qt < qlast && qt - qt0 == 2) {
-            dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-            ++qt;
-        }
-    } else {
-        for (; qt < min(qfull, qlast); ++qt) {
-            if ((qt - qt0) % NS == 0) dkdv_step<D, E, 0, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-            else dkdv_step<D, E, 1, true, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-        }
-        // the full tiles, rotated so that the unrolled body starts on stage 0
-        if (qt < qlast && (qt - qt0) % NS != 0) {
-            dkdv_step<D, E, 1, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
-            ++qt;
+        if constexpr (NS > 2) {
+            if (qt < qlast && qt - qt0 == 2) {
+                dkdv_step<D, E, 2, false, STRIDED>(dva, dka, kf, vf, rg, ld, of, x, qt, nqt);
+                ++qt;
+            }
         }
     }
     for (; qt + NS <= qlast; qt += NS) {
