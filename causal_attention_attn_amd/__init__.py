@@ -42,6 +42,8 @@ from ._lib import (  # noqa: F401
 )
 from .api import (  # noqa: F401
     KVCache,
+    attention,
+    attention_packed,
     backward,
     backward_packed,
     forward,

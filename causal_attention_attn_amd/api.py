@@ -218,3 +218,52 @@ class KVCache:
                               self.nbytes, self.cs, self.sn, o, lse, self.ws, self.ws_bytes, pos,
                               self.B, self.H, self.Tmax, self.D, self.code)
         return o, lse
+
+
+class _Attention(torch.autograd.Function):
+    """forward() and backward() as one autograd node: the forward keeps o, lse and
+    the rotated q, k it formed, and the backward hands them to attn_bwd_saved."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, base):
+        o, lse, saved = forward(q, k, v, base=base, save=True)
+        ctx.base = base
+        ctx.has_saved = saved is not None
+        ctx.save_for_backward(q, k, v, o, lse, *([saved] if saved is not None else []))
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, *rest = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, o, do.contiguous(), lse, rest[0] if ctx.has_saved else None,
+                              base=ctx.base)
+        return dq, dk, dv, None
+
+
+def attention(q, k, v, base=10000.0):
+    """Causal RoPE attention of [B, H, T, D] q, k, v (bf16, fp16 or fp32, on the
+    GPU) as a differentiable torch op: o = forward(...)[0], and o.backward() (or
+    any autograd use) runs the library's backward."""
+    return _Attention.apply(q, k, v, base)
+
+
+class _AttentionPacked(torch.autograd.Function):
+    """forward_packed() and backward_packed() as one autograd node."""
+
+    @staticmethod
+    def forward(ctx, qkv, base):
+        o, lse, saved = forward_packed(qkv, base=base, save=True)
+        ctx.base = base
+        ctx.save_for_backward(qkv, o, lse, saved)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        qkv, o, lse, saved = ctx.saved_tensors
+        return backward_packed(qkv, o, do.contiguous(), lse, saved, base=ctx.base), None
+
+
+def attention_packed(qkv, base=10000.0):
+    """attention() on the QKV projection's packed [B, T, 3, H, D] output (16-bit
+    dtypes), returning o as [B, T, H, D]; differentiable with respect to qkv."""
+    return _AttentionPacked.apply(qkv, base)
