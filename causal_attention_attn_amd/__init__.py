@@ -48,5 +48,7 @@ from .api import (  # noqa: F401
     backward_packed,
     forward,
     forward_packed,
+    rmsnorm,
     rope_tables,
+    swiglu,
 )

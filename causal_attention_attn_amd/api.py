@@ -267,3 +267,85 @@ def attention_packed(qkv, base=10000.0):
     """attention() on the QKV projection's packed [B, T, 3, H, D] output (16-bit
     dtypes), returning o as [B, T, H, D]; differentiable with respect to qkv."""
     return _AttentionPacked.apply(qkv, base)
+
+
+def _rows(t, what):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous GPU tensor")
+    if t.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"{what}: bfloat16 or float16 expected")
+    return t.reshape(-1, t.shape[-1])
+
+
+class _RMSNorm(torch.autograd.Function):
+    """Residual add + RMSNorm (attn_rmsnorm_fwd / attn_rmsnorm_bwd) as one node:
+    outputs y and, with a residual, the stored sum h = x + res."""
+
+    @staticmethod
+    def forward(ctx, x, g, res, eps):
+        x2 = _rows(x, "x")
+        N, C = x2.shape
+        if tuple(g.shape) != (C,) or g.dtype != x.dtype or g.device != x.device:
+            raise ValueError("g must be [C] of x's dtype and device")
+        if res is not None and (res.shape != x.shape or res.dtype != x.dtype
+                                or res.device != x.device or not res.is_contiguous()):
+            raise ValueError("res must match x")
+        dt = _dtype_code(x)
+        y = torch.empty_like(x)
+        h = torch.empty_like(x) if res is not None else None
+        rstd = torch.empty(N, dtype=torch.float32, device=x.device)
+        _lib.attn_rmsnorm_fwd(x2, res, g, eps, h, y, rstd, N, C, dt)
+        ctx.save_for_backward(h if res is not None else x, g, rstd)
+        ctx.has_res = res is not None
+        if res is None:
+            return y
+        return y, h
+
+    @staticmethod
+    def backward(ctx, dy, dh_out=None):
+        h, g, rstd = ctx.saved_tensors
+        N, C = h.reshape(-1, h.shape[-1]).shape
+        dt = _dtype_code(h)
+        dy = dy.contiguous() if dy is not None else torch.zeros_like(h)
+        dres = dh_out.contiguous() if (ctx.has_res and dh_out is not None) else None
+        dh = torch.empty_like(h)
+        dg = torch.empty(C, dtype=torch.float32, device=h.device)
+        nw = _lib.attn_rmsnorm_bwd_workspace_bytes(N, C, dt)
+        ws = torch.empty(nw, dtype=torch.uint8, device=h.device)
+        _lib.attn_rmsnorm_bwd(h, g, rstd, dy, dres, dh, dg, ws, nw, N, C, dt)
+        return dh, dg.to(g.dtype), (dh if ctx.has_res else None), None
+
+
+def rmsnorm(x, g, res=None, eps=1e-5):
+    """y = RMSNorm(x [+ res]) * g over the last dimension (C a multiple of 256,
+    up to 4096; bf16 or fp16 on the GPU), differentiable. With res, returns
+    (y, h) where h = x + res is the stored residual stream. g's gradient is
+    reduced in fp32 and rounded to g's dtype."""
+    return _RMSNorm.apply(x, g, res, eps)
+
+
+class _SwiGLU(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, u):
+        u2 = _rows(u, "u")
+        N, F2 = u2.shape
+        if F2 % 16:
+            raise ValueError("the last dimension of u must be 2F with F a multiple of 8")
+        out = torch.empty((*u.shape[:-1], F2 // 2), dtype=u.dtype, device=u.device)
+        _lib.attn_swiglu_fwd(u2, out, N, F2 // 2, _dtype_code(u))
+        ctx.save_for_backward(u)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        (u,) = ctx.saved_tensors
+        N, F2 = u.reshape(-1, u.shape[-1]).shape
+        du = torch.empty_like(u)
+        _lib.attn_swiglu_bwd(u, dout.contiguous(), du, N, F2 // 2, _dtype_code(u))
+        return du
+
+
+def swiglu(u):
+    """silu(a) * b for u = [a | b] along the last dimension (the fused gate/up
+    projection; bf16 or fp16 on the GPU), differentiable."""
+    return _SwiGLU.apply(u)

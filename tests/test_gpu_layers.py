@@ -189,3 +189,41 @@ def test_layers_maximum_size():
     close(out[rows].cpu(), oracle.swiglu_forward(us), "bf16", "swiglu maximum size out")
     close(du[rows].cpu(), oracle.swiglu_backward(us, f64(dout[rows].cpu())), "bf16",
           "swiglu maximum size du")
+
+
+@pytest.mark.parametrize("residual", [True, False])
+def test_rmsnorm_autograd(residual):
+    """attn.rmsnorm as a differentiable op: y (and h), and the gradients of x, res
+    and g for L = sum(y * dy) + sum(h * dres), bitwise those of the direct calls
+    (g's gradient rounded from the fp32 dg)."""
+    N, C = 300, 768
+    x = workloads.layer_inputs("rmsnorm", N, C, "bf16", seed=77)
+    d = {n: t.to(DEV) for n, t in x.items()}
+    xg = d["x"].clone().requires_grad_()
+    gg = d["g"].clone().requires_grad_()
+    if residual:
+        rg = d["r"].clone().requires_grad_()
+        y, h = attn.rmsnorm(xg, gg, rg)
+        ((y.float() * d["dy"].float()).sum() + (h.float() * d["dres"].float()).sum()).backward()
+    else:
+        y = attn.rmsnorm(xg, gg)
+        (y.float() * d["dy"].float()).sum().backward()
+    rh, ry, _, rdh, rdg = run_norm(x["x"], x["r"] if residual else None, x["g"], x["dy"],
+                                   x["dres"] if residual else None, "bf16")
+    assert torch.equal(y.detach().cpu(), ry)
+    if residual:
+        assert torch.equal(h.detach().cpu(), rh)
+        assert torch.equal(rg.grad.cpu(), rdh)
+    assert torch.equal(xg.grad.cpu(), rdh)
+    assert torch.equal(gg.grad.cpu(), rdg.to(torch.bfloat16))
+
+
+def test_swiglu_autograd():
+    N, F = 64, 1000
+    x = workloads.layer_inputs("swiglu", N, F, "bf16", seed=78)
+    u = x["u"].to(DEV).requires_grad_()
+    out = attn.swiglu(u)
+    out.backward(x["dout"].to(DEV))
+    rout, rdu = run_swiglu(x["u"], x["dout"], "bf16")
+    assert torch.equal(out.detach().cpu(), rout)
+    assert torch.equal(u.grad.cpu(), rdu)
